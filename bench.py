@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark: one grouped Muon step over a synthetic parameter set on one MI355X.
+
+A "step" is one muon_step call: momentum + norm, the Newton-Schulz schedule
+(Gram, polynomial and update per iteration) and scale / weight decay / apply,
+over every matrix of the workload, with inputs already resident in HBM.
+
+Default workload: the d=2048, 24-layer transformer parameter set in bf16
+(per layer Q, K, V, O 2048x2048, MLP up 8192x2048 and down 2048x8192:
+144 matrices), hybrid schedule of 8 fast + 2 stable iterations, Moonlight
+scale, lr 3e-4, weight decay 0.01, beta 0.95.
+
+Prints ONE JSON line.  `value` is matrices per second of whole steps.  The
+Newton-Schulz FLOP count is algorithmic, 3 m^2 n + m^3 per iteration with
+m = min(rows, cols), n = max(rows, cols) (half Gram, half polynomial, full
+update).  `roofline` is for the dominant kernel (the update, 2 m^2 n per
+matrix per launch), timed with HIP events recorded on the launch stream over
+the timed region.  `cpu_baseline` times the fp64 oracle on a bounded sample
+of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+F32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix
+HBM_PEAK_GBS = 8000.0
+
+
+def ns_flops(shapes, steps):
+    tot = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        tot += (3 * m * m * n + m ** 3) * steps
+    return tot
+
+
+def update_flops_per_launch(shapes):
+    return sum(2 * min(r, c) ** 2 * max(r, c) for r, c in shapes)
+
+
+def cpu_baseline(wl, budget_s=20.0):
+    """Time the fp64 oracle on a bounded sample of the workload's matrices."""
+    import numpy as np
+    import oracle as orc
+    import workloads as wk
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    # keep the workload's shape mix: walk distinct shapes round-robin
+    by_shape = {}
+    for i, s in enumerate(wl.shapes):
+        by_shape.setdefault(s, []).append(i)
+    counts = {s: len(v) for s, v in by_shape.items()}
+    order = []
+    total = sum(counts.values())
+    # proportional sample: for c3 this is 4 square : 1 up : 1 down
+    g = min(counts.values())
+    for s, v in by_shape.items():
+        order.extend(v[: max(1, counts[s] // g)])
+    hp = wl.hp
+    done, t_used, names = 0, 0.0, []
+    for i in order:
+        h = wk.host_matrix(wl, i)
+        t0 = time.perf_counter()
+        orc.muon_step(h["W"], h["G"], h["M"], lr=hp["lr"], beta=hp["beta"], weight_decay=hp["weight_decay"],
+                      schedule=hp["schedule"], scale_rule=hp["scale_rule"], eps=hp["eps"], dtype=wl.dtype)
+        t_used += time.perf_counter() - t0
+        done += 1
+        names.append("x".join(map(str, wl.shapes[i])))
+        if t_used > budget_s:
+            break
+    return {
+        "value": done / t_used,
+        "unit": "matrices/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {total} matrices ({', '.join(names)}), fp64 numpy, {t_used:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=3, help="workload id (1-5)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU sharding of the "
+              "step is described in the design notes and not built here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import matrix_aware_optimizer_amd as mao
+    import workloads as wk
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    mao.load()
+    wl = wk.WORKLOADS[args.workload]
+    hp = wl.hp
+
+    print(f"# generating {wl.n} matrices on the device ({wl.name})", file=sys.stderr, flush=True)
+    W, G, M = [], [], []
+    for i in range(wl.n):
+        d = wk.device_matrix(wl, i, dev)
+        W.append(d["W"]); G.append(d["G"]); M.append(d["M"])
+    torch.cuda.synchronize()
+    kw = dict(lr=hp["lr"], beta=hp["beta"], weight_decay=hp["weight_decay"], schedule=hp["schedule"],
+              scale_rule=hp["scale_rule"], eps=hp["eps"])
+    need = mao.muon_workspace_bytes(W, G, M, **kw)
+    ws = mao.allocate_workspace(need, dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        mao.muon_step(W, G, M, workspace=ws, stream=stream, **kw)
+    torch.cuda.synchronize()
+    print(f"# warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    mao.muon_profile_enable(True)
+    mao.muon_profile_read()          # reset counters
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        mao.muon_step(W, G, M, workspace=ws, stream=stream, **kw)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = mao.muon_profile_read()
+    mao.muon_profile_enable(False)
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    steps_ns = len(hp["schedule"])
+    flops_ns = ns_flops(wl.shapes, steps_ns)
+    ns_ms = (prof["gram"]["ms"] + prof["poly"]["ms"] + prof["update"]["ms"]) / args.steps
+    upd = prof["update"]
+    upd_ms = upd["ms"] / max(1, upd["launches"])
+    upd_tflops = update_flops_per_launch(wl.shapes) / (upd_ms * 1e-3) / 1e12
+    bf16 = wl.dtype == "bf16"
+    peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
+
+    elem = sum(r * c for r, c in wl.shapes)
+    es = 2 if bf16 else 4
+    k1_ms = prof["momentum_norm"]["ms"] / max(1, prof["momentum_norm"]["launches"])
+    k5_ms = prof["apply"]["ms"] / max(1, prof["apply"]["launches"])
+
+    out = {
+        "metric": "Muon step matrices/s and NS TFLOP/s as % of MI355X bf16 MFMA peak",
+        "value": round(wl.n / (ms_per_step * 1e-3), 3),
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "matrices": wl.n,
+            "ns_steps": steps_ns,
+            "schedule": "8 fast + 2 stable" if args.workload == 3 else f"{steps_ns} fast",
+            "scale_rule": hp["scale_rule"],
+        },
+        "ns_tflops_algorithmic": round(flops_ns / (ns_ms * 1e-3) / 1e12, 2),
+        "ns_frac_of_peak": round(flops_ns / (ns_ms * 1e-3) / 1e12 / peak, 4),
+        "ns_ms_per_step": round(ns_ms, 4),
+        "step_tflops_algorithmic": round(flops_ns / (ms_per_step * 1e-3) / 1e12, 2),
+        "kernel_ms_per_step": {k: round(v["ms"] / args.steps, 4) for k, v in prof.items()},
+        "elementwise_gbs": {
+            "momentum_norm": round(3 * es * elem / (k1_ms * 1e-3) / 1e9, 1),
+            "apply": round((2 * es + 4) * elem / (k5_ms * 1e-3) / 1e9, 1),
+        },
+        "roofline": {
+            "kernel": "update (X <- aX + BX)",
+            "bound": "mfma",
+            "achieved": round(upd_tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(upd_tflops / peak, 4),
+            "traffic": None,
+            "avg_launch_ms": round(upd_ms, 4),
+            "flops_per_launch": update_flops_per_launch(wl.shapes),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("# timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

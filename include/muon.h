@@ -1,0 +1,154 @@
+/*
+ * muon.h -- C ABI of the MI355X (gfx950) Muon optimizer step.
+ *
+ * One call runs the whole Muon step over a list of 2-D weight matrices:
+ *   M' = beta*M + G                        (momentum, no dampening)
+ *   U  = M'   (or beta*M' + G with MUON_FLAG_NESTEROV)
+ *   X0 = U / (||U||_F + eps)               (Frobenius normalization)
+ *   X  <- a_k X + (b_k A + c_k A A) X,  A = X X^T,  k = 1..ns_steps
+ *         (on the smaller side: matrices with rows > cols are transposed)
+ *   W' = (1 - lr*wd) W - lr * s_rule(rows, cols) * X
+ * Sources, cited by page title and section:
+ *   [Muon优化器] linsight.cn/f25d614e.html -- the industrial Muon class
+ *     (momentum, Nesterov, decay and apply), zeropower_via_newtonschulz
+ *     (normalization, transposition, the quintic iteration) and section
+ *     "缩放因子：从初始化到更新尺度" (the four scale rules);
+ *   [DeepSeek V4 summary] prism.simon-ai.net/article/8795, section
+ *     "Muon的训练效率与DeepSeek V4的混合优化策略" -- per-step coefficients
+ *     (8 fast iterations, then 2 stable ones);
+ *   [Adam vs Muon essay] guanweilu.cn/article/354.html -- the step as
+ *     muon_step(weight, grad, momentum, lr, beta).
+ *
+ * Conventions for every entry point:
+ *  - Matrices are dense, row-major, contiguous, rows = d_out, cols = d_in
+ *    (the PyTorch Linear layout), in device memory of the current HIP
+ *    device.  All matrices of one call share one dtype (hp->dtype).
+ *  - The caller owns every device buffer, including the workspace; the
+ *    library never allocates device memory in these calls and keeps no
+ *    pointer once the enqueued work has finished.  Host arrays (mats,
+ *    hp->schedule) are read during the call only.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default
+ *    stream.  Work is enqueued asynchronously; device buffers must stay
+ *    alive until the stream reaches that point.
+ *  - Argument validation is synchronous and happens before anything is
+ *    enqueued; on any error nothing is modified.  Faults during kernel
+ *    execution surface at the caller's next synchronization.
+ *  - NaN/Inf in G or M are not checked; they stay inside their own matrix.
+ *  - Not re-entrant on one workspace: concurrent calls need separate
+ *    workspaces (and, if they must overlap, separate streams).
+ */
+#ifndef MUON_MI355X_H
+#define MUON_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MUON_OK = 0,
+    MUON_ERR_INVALID_ARG = -1,  /* bad pointer, shape, enum, non-finite scalar, overlap */
+    MUON_ERR_UNSUPPORTED = -2,  /* device is not gfx950, or a size beyond the limits below */
+    MUON_ERR_WORKSPACE = -3,    /* workspace NULL, too small or not 256-byte aligned */
+    MUON_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed */
+} muon_status;
+
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
+
+/* [Muon优化器] section "缩放因子：从初始化到更新尺度" (d_out = rows, d_in = cols):
+ *   NAIVE         1
+ *   KELLER_JORDAN sqrt(max(1, d_out/d_in))
+ *   MUP           sqrt(d_out/d_in)
+ *   MOONLIGHT     0.2 * sqrt(max(d_out, d_in))                               */
+typedef enum {
+    MUON_SCALE_NAIVE = 0,
+    MUON_SCALE_KELLER_JORDAN = 1,
+    MUON_SCALE_MUP = 2,
+    MUON_SCALE_MOONLIGHT = 3
+} muon_scale_rule;
+
+/* One Newton-Schulz step's coefficients: X <- a X + (b A + c A A) X. */
+typedef struct { float a, b, c; } muon_ns_coeffs;
+
+/* Nesterov form: the iteration runs on beta*M' + G instead of M'
+ * ([Muon优化器], industrial Muon class, nesterov branch). */
+#define MUON_FLAG_NESTEROV 1u
+
+/* Upper limits of this build. */
+#define MUON_MAX_NS_STEPS 64
+#define MUON_MAX_MATRICES 65536
+#define MUON_MAX_DIM      (1 << 20)
+
+typedef struct {
+    void*       weight;    /* in/out, rows x cols */
+    const void* grad;      /* in; NULL => the matrix is skipped entirely (state untouched) */
+    void*       momentum;  /* in/out optimizer state, same dtype and shape */
+    int64_t     rows, cols;
+} muon_matrix;
+
+typedef struct {
+    float lr;                         /* finite */
+    float beta;                       /* finite */
+    float weight_decay;               /* finite */
+    float eps;                        /* finite, >= 0; added to the Frobenius norm */
+    int32_t scale_rule;               /* muon_scale_rule */
+    int32_t ns_steps;                 /* 0..MUON_MAX_NS_STEPS; 0 => X = X0 */
+    const muon_ns_coeffs* schedule;   /* host array of ns_steps triples (finite) */
+    int32_t dtype;                    /* muon_dtype of weight, grad and momentum */
+    uint32_t flags;                   /* MUON_FLAG_NESTEROV or 0 */
+} muon_hparams;
+
+/* Bytes of device workspace muon_step needs for this list (0 on invalid
+ * arguments; the reason is in muon_last_error_message()).  Host-only. */
+size_t muon_workspace_bytes(const muon_matrix* mats, int32_t n, const muon_hparams* hp);
+
+/* One Muon step over `n` matrices, grouped: one launch per phase covers all
+ * of them.  `workspace` is device memory of at least muon_workspace_bytes()
+ * bytes, 256-byte aligned; its contents need not be initialized.
+ * Writes weight and momentum of every matrix whose grad is non-NULL. */
+muon_status muon_step(const muon_matrix* mats, int32_t n, const muon_hparams* hp,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Orthogonalization only (the zeropower_via_newtonschulz contract of
+ * [Muon优化器]): out = NS(in / (||in||_F + eps)) with hp's schedule.
+ * `in` has hp->dtype; `out` is fp32, same shape, row-major; in and out must
+ * not overlap.  hp's lr, beta, weight_decay, scale_rule and flags are ignored. */
+typedef struct {
+    const void* in;
+    float*      out;
+    int64_t     rows, cols;
+} muon_ns_matrix;
+
+size_t muon_ns_workspace_bytes(const muon_ns_matrix* mats, int32_t n, const muon_hparams* hp);
+muon_status muon_ns(const muon_ns_matrix* mats, int32_t n, const muon_hparams* hp,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+const char* muon_status_string(int32_t status);
+/* Detail of the calling thread's last failure ("" if none). */
+const char* muon_last_error_message(void);
+
+/* Optional per-kernel timing with HIP events recorded on the launch stream.
+ * While enabled, every launch of muon_step / muon_ns is bracketed by two
+ * events; muon_profile_read synchronizes them and returns, per kernel class,
+ * the summed duration in milliseconds and the number of launches, then
+ * resets the counters.  Classes: 0 momentum+norm, 1 norm finalize, 2 Gram,
+ * 3 polynomial, 4 update, 5 apply.  Host-side bookkeeping only. */
+#define MUON_KCLASS_COUNT 6
+typedef struct {
+    double  ms[MUON_KCLASS_COUNT];
+    int64_t launches[MUON_KCLASS_COUNT];
+} muon_profile;
+
+muon_status muon_profile_enable(int32_t on);
+muon_status muon_profile_read(muon_profile* out);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t muon_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MUON_MI355X_H */

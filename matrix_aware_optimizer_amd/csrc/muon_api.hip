@@ -1,0 +1,591 @@
+// Host side of the C ABI in include/muon.h: argument validation, the
+// grouped-batch plan (orientation, padding, tile prefix sums, workspace
+// layout), descriptor upload and the launch sequence
+//     momentum+norm -> norm finalize -> T x (Gram -> polynomial -> update) -> apply
+// on the caller's stream.  No device memory is allocated here: everything
+// lives in the caller's workspace.  Descriptor tables are staged through a
+// small ring of pinned host buffers so the upload is truly asynchronous.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <type_traits>
+#include <vector>
+
+#include "../../include/muon.h"
+#include "muon_internal.h"
+
+using namespace muon;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+muon_status fail(muon_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+muon_status hip_fail(hipError_t e, const char* what) {
+    return fail(MUON_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t ALIGN = 256;
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// ---------------------------------------------------------------------------
+// Validation
+// ---------------------------------------------------------------------------
+
+muon_status check_hparams(const muon_hparams* hp, bool need_step_scalars) {
+    if (!hp) return fail(MUON_ERR_INVALID_ARG, "hp is NULL");
+    if (hp->dtype != MUON_F32 && hp->dtype != MUON_BF16)
+        return fail(MUON_ERR_INVALID_ARG, "unknown dtype %d", hp->dtype);
+    if (hp->ns_steps < 0 || hp->ns_steps > MUON_MAX_NS_STEPS)
+        return fail(MUON_ERR_INVALID_ARG, "ns_steps %d outside [0, %d]", hp->ns_steps, MUON_MAX_NS_STEPS);
+    if (hp->ns_steps > 0 && !hp->schedule) return fail(MUON_ERR_INVALID_ARG, "schedule is NULL");
+    for (int k = 0; k < hp->ns_steps; ++k) {
+        const muon_ns_coeffs& c = hp->schedule[k];
+        if (!std::isfinite(c.a) || !std::isfinite(c.b) || !std::isfinite(c.c))
+            return fail(MUON_ERR_INVALID_ARG, "schedule[%d] is not finite", k);
+    }
+    if (!std::isfinite(hp->eps) || hp->eps < 0.0f) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (need_step_scalars) {
+        if (!std::isfinite(hp->lr)) return fail(MUON_ERR_INVALID_ARG, "lr is not finite");
+        if (!std::isfinite(hp->beta)) return fail(MUON_ERR_INVALID_ARG, "beta is not finite");
+        if (!std::isfinite(hp->weight_decay)) return fail(MUON_ERR_INVALID_ARG, "weight_decay is not finite");
+        if (hp->scale_rule < MUON_SCALE_NAIVE || hp->scale_rule > MUON_SCALE_MOONLIGHT)
+            return fail(MUON_ERR_INVALID_ARG, "unknown scale_rule %d", hp->scale_rule);
+        if (hp->flags & ~MUON_FLAG_NESTEROV) return fail(MUON_ERR_INVALID_ARG, "unknown flags 0x%x", hp->flags);
+    }
+    return MUON_OK;
+}
+
+struct Interval {
+    uintptr_t lo, hi;
+    bool readonly;
+    int who;
+};
+
+muon_status check_overlaps(std::vector<Interval>& iv) {
+    std::sort(iv.begin(), iv.end(), [](const Interval& a, const Interval& b) { return a.lo < b.lo; });
+    // sweep: keep the furthest-reaching earlier interval of each kind
+    uintptr_t max_hi_rw = 0, max_hi_any = 0;
+    int who_rw = -1, who_any = -1;
+    for (const Interval& x : iv) {
+        if (x.lo < max_hi_rw) return fail(MUON_ERR_INVALID_ARG, "buffers of matrices %d and %d overlap", who_rw, x.who);
+        if (!x.readonly && x.lo < max_hi_any)
+            return fail(MUON_ERR_INVALID_ARG, "buffers of matrices %d and %d overlap", who_any, x.who);
+        if (!x.readonly && x.hi > max_hi_rw) { max_hi_rw = x.hi; who_rw = x.who; }
+        if (x.hi > max_hi_any) { max_hi_any = x.hi; who_any = x.who; }
+    }
+    return MUON_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Plan and workspace layout
+// ---------------------------------------------------------------------------
+
+struct Item {            // one active matrix, before sorting
+    int user_index;
+    const void* g;
+    void* w;
+    void* mom;
+    float* out;
+    int64_t rows, cols;
+};
+
+struct Plan {
+    std::vector<MatDesc> descs;
+    std::vector<int32_t> ew_prefix, sym_prefix, upd_prefix;
+    size_t off_descs = 0, off_prefix = 0, off_scal = 0, off_partials = 0, header_bytes = 0, total_bytes = 0;
+    int64_t total_ew = 0, total_sym = 0, total_upd = 0;
+};
+
+float scale_rule_value(int rule, int64_t rows, int64_t cols) {
+    const double d_out = static_cast<double>(rows), d_in = static_cast<double>(cols);
+    switch (rule) {
+        case MUON_SCALE_KELLER_JORDAN: return static_cast<float>(std::sqrt(std::max(1.0, d_out / d_in)));
+        case MUON_SCALE_MUP: return static_cast<float>(std::sqrt(d_out / d_in));
+        case MUON_SCALE_MOONLIGHT: return static_cast<float>(0.2 * std::sqrt(std::max(d_out, d_in)));
+        default: return 1.0f;
+    }
+}
+
+// Builds descriptors with workspace offsets (pointers are offsets until
+// `rebase` adds the workspace base).
+muon_status build_plan(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, Plan& pl) {
+    const int dtype = hp->dtype;
+    const size_t es = dtype == MUON_BF16 ? 2 : 4;
+    const int64_t pad = dtype == MUON_BF16 ? GEMM_TILE_BF16 : GEMM_TILE_F32;
+    const int nmat = static_cast<int>(items.size());
+
+    struct Shape { int64_t m, n, mp, np; };
+    std::vector<Shape> sh(nmat);
+    for (int i = 0; i < nmat; ++i) {
+        Shape& s = sh[i];
+        s.m = std::min(items[i].rows, items[i].cols);
+        s.n = std::max(items[i].rows, items[i].cols);
+        s.mp = round_up(s.m, pad);
+        s.np = round_up(s.n, pad);
+    }
+    // largest Newton-Schulz work first (stable for equal shapes)
+    std::vector<int> order(nmat);
+    for (int i = 0; i < nmat; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+        const double ca = static_cast<double>(sh[a].mp) * sh[a].mp * sh[a].np;
+        const double cb = static_cast<double>(sh[b].mp) * sh[b].mp * sh[b].np;
+        return ca > cb;
+    });
+
+    pl.descs.assign(nmat, MatDesc{});
+    pl.ew_prefix.assign(nmat + 1, 0);
+    pl.sym_prefix.assign(nmat + 1, 0);
+    pl.upd_prefix.assign(nmat + 1, 0);
+
+    size_t off = 0;
+    pl.off_descs = off;
+    off = align_up(off + sizeof(MatDesc) * nmat, ALIGN);
+    pl.off_prefix = off;
+    off = align_up(off + sizeof(int32_t) * 3 * (nmat + 1), ALIGN);
+    pl.header_bytes = off;                       // uploaded from the host
+    pl.off_scal = off;
+    off = align_up(off + sizeof(float) * 2 * nmat, ALIGN);
+
+    int64_t ew = 0, sym = 0, upd = 0;
+    for (int k = 0; k < nmat; ++k) {
+        const Item& it = items[order[k]];
+        const Shape& s = sh[order[k]];
+        MatDesc& d = pl.descs[k];
+        d.w = it.w;
+        d.g = it.g;
+        d.mom = it.mom;
+        d.out = it.out;
+        d.rows = static_cast<int32_t>(it.rows);
+        d.cols = static_cast<int32_t>(it.cols);
+        d.m = static_cast<int32_t>(s.m);
+        d.n = static_cast<int32_t>(s.n);
+        d.mp = static_cast<int32_t>(s.mp);
+        d.np = static_cast<int32_t>(s.np);
+        d.tall = it.rows > it.cols ? 1 : 0;
+        const int64_t ewt = (s.mp / EW_TILE) * (s.np / EW_TILE);
+        const int64_t tm = s.mp / pad, tn = s.np / pad;
+        const int64_t symt = tm * (tm + 1) / 2, updt = tm * tn;
+        d.ew_tile0 = static_cast<int32_t>(ew);
+        d.ew_tiles = static_cast<int32_t>(ewt);
+        d.sym_tile0 = static_cast<int32_t>(sym);
+        d.sym_tiles = static_cast<int32_t>(symt);
+        d.upd_tile0 = static_cast<int32_t>(upd);
+        d.upd_tiles = static_cast<int32_t>(updt);
+        ew += ewt;
+        sym += symt;
+        upd += updt;
+        if (ew > INT32_MAX || sym > INT32_MAX || upd > INT32_MAX)
+            return fail(MUON_ERR_UNSUPPORTED, "too many tiles in one call (split the matrix list)");
+        pl.ew_prefix[k + 1] = static_cast<int32_t>(ew);
+        pl.sym_prefix[k + 1] = static_cast<int32_t>(sym);
+        pl.upd_prefix[k + 1] = static_cast<int32_t>(upd);
+        if (ns_only) {
+            d.apply_coef = 0.0f;
+            d.decay = 1.0f;
+        } else {
+            const double lr = hp->lr, wd = hp->weight_decay;
+            d.apply_coef = static_cast<float>(lr * static_cast<double>(scale_rule_value(hp->scale_rule, it.rows, it.cols)));
+            d.decay = static_cast<float>(1.0 - lr * wd);
+        }
+        d.scal = reinterpret_cast<float*>(pl.off_scal + sizeof(float) * 2 * k);
+    }
+    pl.total_ew = ew;
+    pl.total_sym = sym;
+    pl.total_upd = upd;
+    pl.off_partials = off;
+    off = align_up(off + sizeof(float) * ew, ALIGN);
+
+    for (int k = 0; k < nmat; ++k) {
+        MatDesc& d = pl.descs[k];
+        const size_t mn = static_cast<size_t>(d.mp) * d.np, mm = static_cast<size_t>(d.mp) * d.mp;
+        d.x32 = reinterpret_cast<float*>(off);
+        off = align_up(off + mn * 4, ALIGN);
+        if (dtype == MUON_BF16) {
+            d.xop = reinterpret_cast<void*>(off);
+            off = align_up(off + mn * es, ALIGN);
+        } else {
+            d.xop = d.x32;
+        }
+        for (int p = 0; p < 2; ++p) {
+            d.xopT[p] = reinterpret_cast<void*>(off);
+            off = align_up(off + mn * es, ALIGN);
+        }
+        d.amat = reinterpret_cast<void*>(off);
+        off = align_up(off + mm * es, ALIGN);
+        d.bmat = reinterpret_cast<void*>(off);
+        off = align_up(off + mm * es, ALIGN);
+    }
+    pl.total_bytes = off;
+    return MUON_OK;
+}
+
+void rebase(Plan& pl, char* base) {
+    auto fix = [base](auto*& p) {
+        using P = std::remove_reference_t<decltype(p)>;
+        p = reinterpret_cast<P>(base + reinterpret_cast<uintptr_t>(p));
+    };
+    for (MatDesc& d : pl.descs) {
+        fix(d.x32);
+        fix(d.xop);
+        fix(d.xopT[0]);
+        fix(d.xopT[1]);
+        fix(d.amat);
+        fix(d.bmat);
+        fix(d.scal);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Device checks, pinned staging, profiling
+// ---------------------------------------------------------------------------
+
+std::mutex g_mu;
+
+muon_status check_device(int* dev_out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    static std::vector<int> ok_cache;   // -1 unknown, 0 no, 1 yes
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (static_cast<int>(ok_cache.size()) <= dev) ok_cache.resize(dev + 1, -1);
+    if (ok_cache[dev] < 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+        ok_cache[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+        if (!ok_cache[dev]) {
+            g_last_error = std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950";
+        }
+    }
+    if (!ok_cache[dev]) return fail(MUON_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    *dev_out = dev;
+    return MUON_OK;
+}
+
+struct PinnedSlot {
+    void* host = nullptr;
+    size_t cap = 0;
+    hipEvent_t ev = nullptr;
+    bool pending = false;
+};
+struct PinnedRing {
+    PinnedSlot slot[4];
+    int next = 0;
+};
+std::vector<PinnedRing> g_rings;
+
+// Copy `bytes` of host data to device `dst` asynchronously on `s`.
+muon_status upload(int dev, void* dst, const void* src, size_t bytes, hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (static_cast<int>(g_rings.size()) <= dev) g_rings.resize(dev + 1);
+    PinnedRing& ring = g_rings[dev];
+    PinnedSlot& sl = ring.slot[ring.next];
+    ring.next = (ring.next + 1) % 4;
+    hipError_t e;
+    if (sl.pending) {
+        e = hipEventSynchronize(sl.ev);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(staging)");
+        sl.pending = false;
+    }
+    if (!sl.ev) {
+        e = hipEventCreateWithFlags(&sl.ev, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+    }
+    if (sl.cap < bytes) {
+        if (sl.host) (void)hipHostFree(sl.host);
+        sl.host = nullptr;
+        sl.cap = 0;
+        const size_t cap = std::max<size_t>(align_up(bytes, 65536), 65536);
+        e = hipHostMalloc(&sl.host, cap, hipHostMallocDefault);
+        if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(staging)");
+        sl.cap = cap;
+    }
+    std::memcpy(sl.host, src, bytes);
+    e = hipMemcpyAsync(dst, sl.host, bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(descriptors)");
+    e = hipEventRecord(sl.ev, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(staging)");
+    sl.pending = true;
+    return MUON_OK;
+}
+
+struct ProfRec { int cls; hipEvent_t a, b; };
+struct ProfState {
+    bool on = false;
+    std::vector<ProfRec> recs;
+    std::vector<hipEvent_t> pool;
+} g_prof;
+
+hipEvent_t prof_event() {
+    if (!g_prof.pool.empty()) {
+        hipEvent_t e = g_prof.pool.back();
+        g_prof.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <typename F>
+muon_status timed_launch(int cls, hipStream_t s, const char* what, F launch) {
+    hipEvent_t a = nullptr, b = nullptr;
+    bool prof;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        prof = g_prof.on;
+        if (prof) { a = prof_event(); b = prof_event(); }
+    }
+    if (prof && a) (void)hipEventRecord(a, s);
+    hipError_t e = launch();
+    if (e != hipSuccess) return hip_fail(e, what);
+    if (prof && b) {
+        (void)hipEventRecord(b, s);
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_prof.recs.push_back({cls, a, b});
+    }
+    return MUON_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The launch sequence shared by muon_step and muon_ns
+// ---------------------------------------------------------------------------
+
+muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, void* workspace,
+                size_t ws_bytes, hipStream_t stream) {
+    Plan pl;
+    muon_status st = build_plan(items, hp, ns_only, pl);
+    if (st != MUON_OK) return st;
+    if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % ALIGN)
+        return fail(MUON_ERR_WORKSPACE, "workspace is not %zu-byte aligned", ALIGN);
+    if (ws_bytes < pl.total_bytes)
+        return fail(MUON_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, pl.total_bytes);
+    {
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(workspace), hi = lo + pl.total_bytes;
+        for (const Item& it : items) {
+            const size_t es = hp->dtype == MUON_BF16 ? 2 : 4;
+            const size_t bytes = static_cast<size_t>(it.rows) * it.cols;
+            const void* ptrs[4] = {it.w, it.g, it.mom, it.out};
+            const size_t sz[4] = {bytes * es, bytes * es, bytes * es, bytes * 4};
+            for (int q = 0; q < 4; ++q) {
+                const uintptr_t p = reinterpret_cast<uintptr_t>(ptrs[q]);
+                if (p && p < hi && p + sz[q] > lo)
+                    return fail(MUON_ERR_INVALID_ARG, "matrix %d overlaps the workspace", it.user_index);
+            }
+        }
+    }
+    int dev = 0;
+    st = check_device(&dev);
+    if (st != MUON_OK) return st;
+
+    char* base = static_cast<char*>(workspace);
+    rebase(pl, base);
+    const int nmat = static_cast<int>(pl.descs.size());
+
+    // header: descriptors + prefix sums
+    std::vector<char> header(pl.header_bytes, 0);
+    std::memcpy(header.data() + pl.off_descs, pl.descs.data(), sizeof(MatDesc) * nmat);
+    int32_t* pre = reinterpret_cast<int32_t*>(header.data() + pl.off_prefix);
+    std::memcpy(pre, pl.ew_prefix.data(), sizeof(int32_t) * (nmat + 1));
+    std::memcpy(pre + (nmat + 1), pl.sym_prefix.data(), sizeof(int32_t) * (nmat + 1));
+    std::memcpy(pre + 2 * (nmat + 1), pl.upd_prefix.data(), sizeof(int32_t) * (nmat + 1));
+    st = upload(dev, base, header.data(), pl.header_bytes, stream);
+    if (st != MUON_OK) return st;
+
+    const MatDesc* d_descs = reinterpret_cast<const MatDesc*>(base + pl.off_descs);
+    const int32_t* d_pre = reinterpret_cast<const int32_t*>(base + pl.off_prefix);
+    float* d_partials = reinterpret_cast<float*>(base + pl.off_partials);
+
+    EwArgs ew{};
+    ew.descs = d_descs;
+    ew.prefix = d_pre;
+    ew.partials = d_partials;
+    ew.nmat = nmat;
+    ew.total = static_cast<int32_t>(pl.total_ew);
+    const int target_blocks = 256 * 8;
+    ew.tiles_per_block = static_cast<int32_t>(std::max<int64_t>(1, (pl.total_ew + target_blocks - 1) / target_blocks));
+    ew.beta = ns_only ? 0.0f : hp->beta;
+    ew.nesterov = (!ns_only && (hp->flags & MUON_FLAG_NESTEROV)) ? 1 : 0;
+    ew.ns_zero = hp->ns_steps == 0 ? 1 : 0;
+    const int ew_grid = static_cast<int>((pl.total_ew + ew.tiles_per_block - 1) / ew.tiles_per_block);
+    const int dtype = hp->dtype;
+
+    st = timed_launch(0, stream, "momentum/norm kernel", [&] { return launch_momentum_norm(dtype, ns_only, ew, ew_grid, stream); });
+    if (st != MUON_OK) return st;
+    st = timed_launch(1, stream, "norm finalize kernel", [&] { return launch_norm_finalize(d_descs, d_partials, nmat, hp->eps, stream); });
+    if (st != MUON_OK) return st;
+
+    NsArgs na{};
+    na.descs = d_descs;
+    na.nmat = nmat;
+    for (int k = 0; k < hp->ns_steps; ++k) {
+        na.a = hp->schedule[k].a;
+        na.b = hp->schedule[k].b;
+        na.c = hp->schedule[k].c;
+        na.first = k == 0;
+        na.last = k == hp->ns_steps - 1;
+        na.ping = k & 1;
+        na.prefix = d_pre + (nmat + 1);
+        na.total = static_cast<int32_t>(pl.total_sym);
+        st = timed_launch(2, stream, "Gram kernel", [&] { return launch_gram(dtype, na, stream); });
+        if (st != MUON_OK) return st;
+        st = timed_launch(3, stream, "polynomial kernel", [&] { return launch_poly(dtype, na, stream); });
+        if (st != MUON_OK) return st;
+        na.prefix = d_pre + 2 * (nmat + 1);
+        na.total = static_cast<int32_t>(pl.total_upd);
+        st = timed_launch(4, stream, "update kernel", [&] { return launch_update(dtype, na, stream); });
+        if (st != MUON_OK) return st;
+    }
+    st = timed_launch(5, stream, "apply kernel", [&] { return launch_apply(dtype, ns_only, ew, ew_grid, stream); });
+    if (st != MUON_OK) return st;
+    g_last_error.clear();
+    return MUON_OK;
+}
+
+muon_status collect_step(const muon_matrix* mats, int32_t n, const muon_hparams* hp, std::vector<Item>& items) {
+    if (n < 0 || n > MUON_MAX_MATRICES) return fail(MUON_ERR_INVALID_ARG, "n = %d outside [0, %d]", n, MUON_MAX_MATRICES);
+    if (n > 0 && !mats) return fail(MUON_ERR_INVALID_ARG, "mats is NULL");
+    muon_status st = check_hparams(hp, true);
+    if (st != MUON_OK) return st;
+    const size_t es = hp->dtype == MUON_BF16 ? 2 : 4;
+    std::vector<Interval> iv;
+    for (int i = 0; i < n; ++i) {
+        const muon_matrix& m = mats[i];
+        if (!m.grad) continue;
+        if (m.rows < 1 || m.cols < 1 || m.rows > MUON_MAX_DIM || m.cols > MUON_MAX_DIM)
+            return fail(MUON_ERR_INVALID_ARG, "matrix %d has shape %lld x %lld", i, (long long)m.rows, (long long)m.cols);
+        if (!m.weight || !m.momentum) return fail(MUON_ERR_INVALID_ARG, "matrix %d: weight or momentum is NULL", i);
+        const uintptr_t pw = reinterpret_cast<uintptr_t>(m.weight), pg = reinterpret_cast<uintptr_t>(m.grad),
+                        pm = reinterpret_cast<uintptr_t>(m.momentum);
+        if (pw % es || pg % es || pm % es) return fail(MUON_ERR_INVALID_ARG, "matrix %d: misaligned pointer", i);
+        const size_t bytes = static_cast<size_t>(m.rows) * static_cast<size_t>(m.cols) * es;
+        iv.push_back({pw, pw + bytes, false, i});
+        iv.push_back({pm, pm + bytes, false, i});
+        iv.push_back({pg, pg + bytes, true, i});
+        items.push_back({i, m.grad, m.weight, m.momentum, nullptr, m.rows, m.cols});
+    }
+    return check_overlaps(iv);
+}
+
+muon_status collect_ns(const muon_ns_matrix* mats, int32_t n, const muon_hparams* hp, std::vector<Item>& items) {
+    if (n < 0 || n > MUON_MAX_MATRICES) return fail(MUON_ERR_INVALID_ARG, "n = %d outside [0, %d]", n, MUON_MAX_MATRICES);
+    if (n > 0 && !mats) return fail(MUON_ERR_INVALID_ARG, "mats is NULL");
+    muon_status st = check_hparams(hp, false);
+    if (st != MUON_OK) return st;
+    const size_t es = hp->dtype == MUON_BF16 ? 2 : 4;
+    std::vector<Interval> iv;
+    for (int i = 0; i < n; ++i) {
+        const muon_ns_matrix& m = mats[i];
+        if (m.rows < 1 || m.cols < 1 || m.rows > MUON_MAX_DIM || m.cols > MUON_MAX_DIM)
+            return fail(MUON_ERR_INVALID_ARG, "matrix %d has shape %lld x %lld", i, (long long)m.rows, (long long)m.cols);
+        if (!m.in || !m.out) return fail(MUON_ERR_INVALID_ARG, "matrix %d: in or out is NULL", i);
+        const uintptr_t pi = reinterpret_cast<uintptr_t>(m.in), po = reinterpret_cast<uintptr_t>(m.out);
+        if (pi % es || po % 4) return fail(MUON_ERR_INVALID_ARG, "matrix %d: misaligned pointer", i);
+        const size_t cnt = static_cast<size_t>(m.rows) * static_cast<size_t>(m.cols);
+        iv.push_back({pi, pi + cnt * es, true, i});
+        iv.push_back({po, po + cnt * 4, false, i});
+        items.push_back({i, m.in, nullptr, nullptr, m.out, m.rows, m.cols});
+    }
+    return check_overlaps(iv);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t muon_workspace_bytes(const muon_matrix* mats, int32_t n, const muon_hparams* hp) {
+    std::vector<Item> items;
+    if (collect_step(mats, n, hp, items) != MUON_OK) return 0;
+    if (items.empty()) return ALIGN;
+    Plan pl;
+    if (build_plan(items, hp, false, pl) != MUON_OK) return 0;
+    return pl.total_bytes;
+}
+
+muon_status muon_step(const muon_matrix* mats, int32_t n, const muon_hparams* hp, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    std::vector<Item> items;
+    muon_status st = collect_step(mats, n, hp, items);
+    if (st != MUON_OK) return st;
+    if (items.empty()) { g_last_error.clear(); return MUON_OK; }
+    return run(items, hp, false, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t muon_ns_workspace_bytes(const muon_ns_matrix* mats, int32_t n, const muon_hparams* hp) {
+    std::vector<Item> items;
+    if (collect_ns(mats, n, hp, items) != MUON_OK) return 0;
+    if (items.empty()) return ALIGN;
+    Plan pl;
+    if (build_plan(items, hp, true, pl) != MUON_OK) return 0;
+    return pl.total_bytes;
+}
+
+muon_status muon_ns(const muon_ns_matrix* mats, int32_t n, const muon_hparams* hp, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    std::vector<Item> items;
+    muon_status st = collect_ns(mats, n, hp, items);
+    if (st != MUON_OK) return st;
+    if (items.empty()) { g_last_error.clear(); return MUON_OK; }
+    return run(items, hp, true, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+const char* muon_status_string(int32_t status) {
+    switch (status) {
+        case MUON_OK: return "MUON_OK";
+        case MUON_ERR_INVALID_ARG: return "MUON_ERR_INVALID_ARG: invalid argument";
+        case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED: unsupported device or size";
+        case MUON_ERR_WORKSPACE: return "MUON_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case MUON_ERR_HIP: return "MUON_ERR_HIP: HIP runtime error";
+        default: return "unknown muon_status";
+    }
+}
+
+const char* muon_last_error_message(void) { return g_last_error.c_str(); }
+
+muon_status muon_profile_enable(int32_t on) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_prof.on = on != 0;
+    return MUON_OK;
+}
+
+muon_status muon_profile_read(muon_profile* out) {
+    if (!out) return fail(MUON_ERR_INVALID_ARG, "out is NULL");
+    std::vector<ProfRec> recs;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        recs.swap(g_prof.recs);
+    }
+    std::memset(out, 0, sizeof(*out));
+    muon_status st = MUON_OK;
+    for (const ProfRec& r : recs) {
+        hipError_t e = hipEventSynchronize(r.b);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess && st == MUON_OK) st = hip_fail(e, "hipEventElapsedTime");
+        out->ms[r.cls] += ms;
+        out->launches[r.cls] += 1;
+    }
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (const ProfRec& r : recs) { g_prof.pool.push_back(r.a); g_prof.pool.push_back(r.b); }
+    return st;
+}
+
+int32_t muon_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// Internal types shared by the host orchestration (muon_api.hip) and the
+// gfx950 kernels (momentum_apply.hip, ns_gemm.hip).  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+// Elementwise kernels walk the Newton-Schulz frame in EW_TILE x EW_TILE tiles.
+constexpr int EW_TILE = 64;
+constexpr int EW_THREADS = 256;
+
+// Block tile of the MFMA GEMM engine, by operand type.  Every Newton-Schulz
+// buffer in the workspace is zero-padded to a multiple of it in both
+// dimensions, so the GEMM kernels never need edge masks.
+constexpr int GEMM_TILE_BF16 = 256;
+constexpr int GEMM_TILE_F32 = 128;
+constexpr int GEMM_THREADS = 256;
+
+enum Dtype : int32_t { DT_F32 = 0, DT_BF16 = 1 };
+
+// One active matrix.  "User frame" is the caller's rows x cols layout;
+// the "NS frame" is m x n with m = min(rows, cols) <= n: tall matrices
+// (rows > cols) are stored transposed there, so the Gram matrix is always
+// formed on the smaller side.
+struct MatDesc {
+    // caller buffers (user frame)
+    void* w;            // weight (muon_step) or nullptr (muon_ns)
+    const void* g;      // gradient (muon_step) or input (muon_ns)
+    void* mom;          // momentum state (muon_step) or nullptr
+    float* out;         // fp32 output (muon_ns) or nullptr
+    int32_t rows, cols;
+    int32_t m, n;       // NS frame
+    int32_t mp, np;     // NS frame padded to the GEMM tile
+    int32_t tall;       // 1 if rows > cols
+    int32_t pad0;
+    // workspace buffers (NS frame, zero-padded)
+    float* x32;         // mp x np fp32 iterate
+    void* xop;          // mp x np operand copy (bf16); equals x32 for fp32
+    void* xopT[2];      // np x mp operand copies of X^T, ping-pong between steps
+    void* amat;         // mp x mp, A = X X^T (symmetric, stored in full)
+    void* bmat;         // mp x mp, B = b A + c A A (symmetric, stored in full)
+    float* scal;        // [0] = 1 / (||U||_F + eps), [1] = ||U||_F
+    float apply_coef;   // lr * scale_rule(rows, cols)
+    float decay;        // 1 - lr * weight_decay
+    int32_t ew_tile0, ew_tiles;    // elementwise tiles: first global index, count
+    int32_t sym_tile0, sym_tiles;  // Gram / polynomial half tiles
+    int32_t upd_tile0, upd_tiles;  // update tiles
+};
+
+struct EwArgs {
+    const MatDesc* descs;
+    const int32_t* prefix;   // nmat + 1 exclusive prefix sums of ew_tiles
+    float* partials;         // one sum of squares per elementwise tile
+    int32_t nmat;
+    int32_t total;
+    int32_t tiles_per_block;
+    float beta;
+    int32_t nesterov;
+    int32_t ns_zero;         // 1 when ns_steps == 0 (output is the normalized input)
+};
+
+struct NsArgs {
+    const MatDesc* descs;
+    const int32_t* prefix;   // nmat + 1 exclusive prefix sums for this phase
+    int32_t nmat;
+    int32_t total;
+    float a, b, c;           // this step's coefficients
+    int32_t first;           // first step: fold the normalization scale in
+    int32_t last;            // last step: only the fp32 iterate is needed
+    int32_t ping;            // xopT[ping] is read, xopT[ping ^ 1] written
+};
+
+// Kernel launchers (defined next to the kernels).
+hipError_t launch_momentum_norm(int dtype, bool ns_only, const EwArgs& args, int grid, hipStream_t s);
+hipError_t launch_norm_finalize(const MatDesc* descs, const float* partials, int nmat, float eps,
+                                hipStream_t s);
+hipError_t launch_apply(int dtype, bool ns_only, const EwArgs& args, int grid, hipStream_t s);
+hipError_t launch_gram(int dtype, const NsArgs& args, hipStream_t s);
+hipError_t launch_poly(int dtype, const NsArgs& args, hipStream_t s);
+hipError_t launch_update(int dtype, const NsArgs& args, hipStream_t s);
+
+// Index of the matrix that owns global tile t: the largest i with
+// prefix[i] <= t (prefix has nmat + 1 entries, prefix[0] = 0).
+__device__ inline int find_matrix(const int32_t* prefix, int nmat, int t) {
+    int lo = 0, hi = nmat - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// bf16 <-> fp32 (bf16 kept as its 16-bit pattern).
+__device__ inline float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round to nearest, ties to even; NaN stays NaN.
+__device__ inline uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+}  // namespace muon

@@ -1,0 +1,157 @@
+"""The C-ABI library on a CPU host: it loads, exports every declared symbol,
+and rejects bad arguments synchronously before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import matrix_aware_optimizer_amd as mao
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(muon_[a-z_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = mao.load()
+    declared = _declared_functions()
+    assert len(declared) >= 9
+    for name in declared:
+        assert hasattr(lib, name), name
+    # the binding knows every declared symbol's signature, and nothing else
+    assert sorted(mao.SIGNATURES) == declared
+
+
+def test_version_and_status_strings():
+    assert mao.muon_version() >= 100
+    for code in (0, -1, -2, -3, -4):
+        assert mao.muon_status_string(code).startswith("MUON_")
+    assert "unknown" in mao.muon_status_string(7)
+
+
+def _hp(**kw):
+    hp, keep = mao.make_hparams(schedule=[(3.4445, -4.775, 2.0315)] * 5, **kw)
+    return hp, keep
+
+
+def _mats(specs):
+    arr = (mao.MuonMatrix * len(specs))()
+    for i, (w, g, m, r, c) in enumerate(specs):
+        arr[i] = mao.MuonMatrix(w, g, m, r, c)
+    return arr
+
+
+FAKE = 1 << 40   # host-side validation never dereferences device pointers
+
+
+def test_workspace_bytes_is_host_only_and_grows_with_work():
+    lib = mao.load()
+    hp, keep = _hp(dtype=mao.MUON_BF16)
+    one = _mats([(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 2048, 2048)])
+    two = _mats([(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 2048, 2048),
+                 (FAKE + (3 << 30), FAKE + (4 << 30), FAKE + (5 << 30), 8192, 2048)])
+    b1 = lib.muon_workspace_bytes(one, 1, ctypes.byref(hp))
+    b2 = lib.muon_workspace_bytes(two, 2, ctypes.byref(hp))
+    assert b1 > 0 and b2 > b1
+    # fp32 iterate + bf16 copy + two bf16 transposed copies + A and B, at least
+    assert b1 >= 2048 * 2048 * (4 + 2 + 2 + 2) + 2 * 2048 * 2048 * 2
+    # a skipped matrix (grad NULL) costs nothing
+    skip = _mats([(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 2048, 2048),
+                  (FAKE + (3 << 30), None, FAKE + (5 << 30), 8192, 2048)])
+    assert lib.muon_workspace_bytes(skip, 2, ctypes.byref(hp)) == b1
+
+
+@pytest.mark.parametrize("case", [
+    "null_hp", "bad_dtype", "bad_rule", "steps_high", "steps_neg", "nan_lr", "inf_coeff",
+    "neg_eps", "bad_flags", "zero_rows", "null_weight", "overlap", "misaligned", "null_schedule",
+])
+def test_invalid_arguments_are_rejected_before_any_gpu_work(case):
+    lib = mao.load()
+    kw = {}
+    specs = [(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 64, 96)]
+    hp, keep = _hp(dtype=mao.MUON_BF16)
+    if case == "bad_dtype":
+        hp.dtype = 7
+    elif case == "bad_rule":
+        hp.scale_rule = 9
+    elif case == "steps_high":
+        hp.ns_steps = 65
+    elif case == "steps_neg":
+        hp.ns_steps = -1
+    elif case == "nan_lr":
+        hp.lr = float("nan")
+    elif case == "inf_coeff":
+        keep[2] = mao.MuonNsCoeffs(float("inf"), 0.0, 0.0)
+    elif case == "neg_eps":
+        hp.eps = -1.0
+    elif case == "bad_flags":
+        hp.flags = 6
+    elif case == "zero_rows":
+        specs = [(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 0, 96)]
+    elif case == "null_weight":
+        specs = [(None, FAKE + (1 << 30), FAKE + (2 << 30), 64, 96)]
+    elif case == "overlap":
+        specs = [(FAKE, FAKE + 64, FAKE + (2 << 30), 64, 96)]
+    elif case == "misaligned":
+        specs = [(FAKE + 1, FAKE + (1 << 30), FAKE + (2 << 30), 64, 96)]
+    elif case == "null_schedule":
+        hp.schedule = ctypes.POINTER(mao.MuonNsCoeffs)()
+    arr = _mats(specs)
+    hpp = None if case == "null_hp" else ctypes.byref(hp)
+    st = lib.muon_step(arr, 1, hpp, ctypes.c_void_p(FAKE + (8 << 30)), 1 << 40, None)
+    assert st == mao.MUON_ERR_INVALID_ARG, (case, st, mao.muon_last_error_message())
+    assert mao.muon_last_error_message() != ""
+    assert lib.muon_workspace_bytes(arr, 1, hpp) == 0
+
+
+def test_workspace_errors():
+    lib = mao.load()
+    hp, keep = _hp(dtype=mao.MUON_BF16)
+    arr = _mats([(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 64, 96)])
+    need = lib.muon_workspace_bytes(arr, 1, ctypes.byref(hp))
+    ws = FAKE + (8 << 30)
+    assert lib.muon_step(arr, 1, ctypes.byref(hp), None, need, None) == mao.MUON_ERR_WORKSPACE
+    assert lib.muon_step(arr, 1, ctypes.byref(hp), ctypes.c_void_p(ws), need - 1, None) == mao.MUON_ERR_WORKSPACE
+    assert lib.muon_step(arr, 1, ctypes.byref(hp), ctypes.c_void_p(ws + 16), need, None) == mao.MUON_ERR_WORKSPACE
+    # a workspace overlapping a matrix is an argument error
+    st = lib.muon_step(arr, 1, ctypes.byref(hp), ctypes.c_void_p(FAKE), need, None)
+    assert st == mao.MUON_ERR_INVALID_ARG
+
+
+def test_empty_list_and_all_skipped_are_noops():
+    lib = mao.load()
+    hp, keep = _hp(dtype=mao.MUON_F32)
+    assert lib.muon_step(None, 0, ctypes.byref(hp), None, 0, None) == mao.MUON_OK
+    arr = _mats([(FAKE, None, FAKE + (2 << 30), 64, 96)])
+    assert lib.muon_step(arr, 1, ctypes.byref(hp), None, 0, None) == mao.MUON_OK
+
+
+def test_ns_entry_validation():
+    lib = mao.load()
+    hp, keep = _hp(dtype=mao.MUON_BF16)
+    arr = (mao.MuonNsMatrix * 1)()
+    arr[0] = mao.MuonNsMatrix(FAKE, FAKE + 8, 16, 16)          # in and out overlap
+    assert lib.muon_ns(arr, 1, ctypes.byref(hp), ctypes.c_void_p(FAKE + (8 << 30)), 1 << 40, None) \
+        == mao.MUON_ERR_INVALID_ARG
+    arr[0] = mao.MuonNsMatrix(FAKE, FAKE + (1 << 30) + 2, 16, 16)  # fp32 out misaligned
+    assert lib.muon_ns(arr, 1, ctypes.byref(hp), ctypes.c_void_p(FAKE + (8 << 30)), 1 << 40, None) \
+        == mao.MUON_ERR_INVALID_ARG
+    arr[0] = mao.MuonNsMatrix(FAKE, FAKE + (1 << 30), 16, 16)
+    assert lib.muon_ns_workspace_bytes(arr, 1, ctypes.byref(hp)) > 0
+
+
+def test_binding_rejects_non_2d_and_non_contiguous():
+    torch = pytest.importorskip("torch")
+    w = torch.zeros(4, 4, 4)
+    with pytest.raises(ValueError):
+        mao.muon_workspace_bytes([w], [w], [w], schedule=[(1.0, 0.0, 0.0)])
+    w2 = torch.zeros(8, 6).t()
+    with pytest.raises(ValueError):
+        mao.muon_workspace_bytes([w2], [w2], [w2], schedule=[(1.0, 0.0, 0.0)])

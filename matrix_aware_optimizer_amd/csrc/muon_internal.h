@@ -16,7 +16,7 @@ constexpr int EW_THREADS = 256;
 // dimensions, so the GEMM kernels never need edge masks.
 constexpr int GEMM_TILE_BF16 = 256;
 constexpr int GEMM_TILE_F32 = 128;
-constexpr int GEMM_THREADS = 256;
+constexpr int GEMM_THREADS = 512;   // 8 waves: two per SIMD
 
 enum Dtype : int32_t { DT_F32 = 0, DT_BF16 = 1 };
 

@@ -12,12 +12,18 @@
 // workspace keeps a transposed operand copy of X for that).
 //
 // Engine: a 256 x 256 (bf16) or 128 x 128 (fp32) block tile per workgroup of
-// 4 waves (2 x 2), each wave owning a 128 x 128 (64 x 64) sub-tile built from
+// 8 waves (2 x 4, two waves per SIMD so one can issue MFMAs while the other
+// waits on memory); each wave owns a 128 x 64 (64 x 32) sub-tile built from
 // 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x2_f32,
 // fp32 accumulation).  Each k-step stages 128 bytes of every operand row in
-// LDS (double-buffered, XOR-swizzled 16-byte chunks); global loads for the
-// next k-step are issued before the MFMAs of the current one.  Buffers are
-// zero-padded to the block tile, so there are no edge masks.
+// LDS with direct global->LDS loads (global_load_lds_dwordx4, no VGPR
+// staging), double-buffered; the loads of the next k-step are spread between
+// the MFMA groups of the current one.  16-byte chunks are XOR-swizzled with
+// bits 1..3 of the row, which keeps ds_read_b128 fragment reads free of bank
+// conflicts on gfx950's LDS (measured with SQ_LDS_BANK_CONFLICT).  MFMA
+// fragments are double-buffered in registers: the reads for the next k-slice
+// are issued between the MFMAs of the current one, at most 8 in flight.
+// Buffers are zero-padded to the block tile, so there are no edge masks.
 //
 // Grouping: one launch covers every matrix of the call.  The grid is the
 // concatenation of all matrices' tiles (per-matrix prefix sums, largest
@@ -43,10 +49,14 @@ template <> struct Cfg<float> {         // 16-byte chunk = 4 fp32 along k
     static constexpr int BM = GEMM_TILE_F32, BN = GEMM_TILE_F32;
 };
 
-constexpr int WAVES_M = 2, WAVES_N = 2;
+constexpr int WAVES_M = 2, WAVES_N = 4;
+constexpr int NWAVES = WAVES_M * WAVES_N;
+static_assert(NWAVES * 64 == GEMM_THREADS, "GEMM_THREADS must match the wave layout");
 constexpr int CHUNKS_PER_ROW = 8;            // 8 x 16 B = 128 B of k per row per k-step
 constexpr int XCD_COUNT = 8;
 constexpr int XCD_RUN = 32;                  // consecutive tiles kept on one XCD
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // One 16-byte chunk per lane of both operands, accumulated into a 32 x 32 block.
 __device__ inline void mfma_chunk(f32x16_t& acc, const u32x4& a, const u32x4& b, uint16_t) {
@@ -60,6 +70,9 @@ __device__ inline void mfma_chunk(f32x16_t& acc, const u32x4& a, const u32x4& b,
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
+
+// Physical position of logical 16-byte chunk c of LDS row `row`.
+__device__ __forceinline__ int swz(int row, int c) { return row * CHUNKS_PER_ROW + (c ^ ((row >> 1) & 7)); }
 
 __device__ inline int xcd_remap(int b, int nb) {
     const int full = (nb / (XCD_COUNT * XCD_RUN)) * (XCD_COUNT * XCD_RUN);
@@ -82,25 +95,36 @@ struct Engine {
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int SM = WM / 32, SN = WN / 32;
     static constexpr int ROWS = BM + BN;                              // P rows then Q rows
-    static constexpr int STAGE = ROWS * CHUNKS_PER_ROW;               // uint4 per stage
-    static constexpr int LOADS = STAGE / GEMM_THREADS;                // 16-B loads per thread per k-step
+    static constexpr int STAGE = ROWS * CHUNKS_PER_ROW;               // 16-byte chunks per stage
+    static constexpr int ROWS_PER_LOAD = 64 / CHUNKS_PER_ROW;         // one wave load = 1 KB = 8 rows
+    static constexpr int LOADS = STAGE / 64 / NWAVES;                 // loads per wave per k-step
+    static constexpr int SUB = CHUNKS_PER_ROW / 2;                    // MFMA k-slices per k-step
+    static constexpr int GROUPS = SUB * SM;                           // MFMA groups per k-step
+    static_assert(LOADS <= GROUPS, "one load per MFMA group at most");
+    static_assert(SM >= SN, "fragment prefetch pairs A row i with B row i");
 
-    // acc[i][j] += sum_k P[row0 + i][k] * Q[col0 + j][k] over the whole k range.
+    // acc[i][j] = sum_k P[row0 + i][k] * Q[col0 + j][k] over the whole k range.
     static __device__ __attribute__((always_inline)) void run(const char* __restrict__ P, size_t ldp, const char* __restrict__ Q,
                                       size_t ldq, int ksteps, u32x4* lds, f32x16_t (&acc)[SM][SN]) {
         const int tid = threadIdx.x;
         const int lane = tid & 63, wave = tid >> 6;
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-        const int c16 = tid & 7;                    // this thread's chunk column for loads
 
+        // Load j of this wave fills LDS chunks [(wave*LOADS + j)*64, +64) of a stage in
+        // lane order: lane l lands in row r = l / 8 of that 1 KB block at physical chunk
+        // l % 8, which holds the row's logical chunk (l % 8) ^ ((r >> 1) & 7).
         const char* src[LOADS];
-        int dst[LOADS];
 #pragma unroll
-        for (int p = 0; p < LOADS; ++p) {
-            const int row = (tid >> 3) + (GEMM_THREADS / CHUNKS_PER_ROW) * p;
-            src[p] = row < BM ? P + row * ldp + c16 * 16 : Q + (row - BM) * ldq + c16 * 16;
-            dst[p] = row * CHUNKS_PER_ROW + (c16 ^ (row & 7));
+        for (int j = 0; j < LOADS; ++j) {
+            const int row = (wave * LOADS + j) * ROWS_PER_LOAD + lane / CHUNKS_PER_ROW;
+            const int lc = (lane % CHUNKS_PER_ROW) ^ ((row >> 1) & 7);
+            src[j] = (row < BM ? P + row * ldp : Q + (row - BM) * ldq) + lc * 16;
         }
+        auto issue = [&](int kt, int j) {
+            lds_ptr_t d = (lds_ptr_t)(lds + (kt & 1) * STAGE + (wave * LOADS + j) * 64);
+            __builtin_amdgcn_global_load_lds((const void*)(src[j] + static_cast<size_t>(kt) * (CHUNKS_PER_ROW * 16)),
+                                             d, 16, 0, 0);
+        };
 #pragma unroll
         for (int i = 0; i < SM; ++i)
 #pragma unroll
@@ -108,45 +132,40 @@ struct Engine {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-        u32x4 stage[LOADS];
 #pragma unroll
-        for (int p = 0; p < LOADS; ++p) stage[p] = *reinterpret_cast<const u32x4*>(src[p]);
-#pragma unroll
-        for (int p = 0; p < LOADS; ++p) lds[dst[p]] = stage[p];
-        __syncthreads();
+        for (int j = 0; j < LOADS; ++j) issue(0, j);
 
-        const int r32 = lane & 31, half = lane >> 5;
-        // Branch-free body (the staging registers stay in VGPRs): the last
-        // iteration re-fetches its own k-step into the idle buffer.
+        const int half = lane >> 5;
+        const int arow = wm * WM + (lane & 31), brow = BM + wn * WN + (lane & 31);
         for (int kt = 0; kt < ksteps; ++kt) {
+            // this wave's loads of stage kt are done; the barrier makes every wave's visible
+            // and guarantees stage (kt + 1) & 1 is no longer being read
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            asm volatile("s_barrier" ::: "memory");
             const u32x4* L = lds + (kt & 1) * STAGE;
-            const size_t koff = static_cast<size_t>(min(kt + 1, ksteps - 1)) * (CHUNKS_PER_ROW * 16);
+            const bool more = kt + 1 < ksteps;
+            u32x4 fa[2][SM], fb[2][SN];
 #pragma unroll
-            for (int p = 0; p < LOADS; ++p) stage[p] = *reinterpret_cast<const u32x4*>(src[p] + koff);
-            __builtin_amdgcn_sched_barrier(0);   // keep the prefetch ahead of the MFMAs
+            for (int i = 0; i < SM; ++i) fa[0][i] = L[swz(arow + i * 32, half)];
 #pragma unroll
-            for (int s = 0; s < CHUNKS_PER_ROW / 2; ++s) {
-                const int c = 2 * s + half;
-                u32x4 af[SM], bfr[SN];
+            for (int j = 0; j < SN; ++j) fb[0][j] = L[swz(brow + j * 32, half)];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < SUB; ++s) {
+                const int cn = 2 * (s + 1) + half;
 #pragma unroll
                 for (int i = 0; i < SM; ++i) {
-                    const int row = wm * WM + i * 32 + r32;
-                    af[i] = L[row * CHUNKS_PER_ROW + (c ^ (row & 7))];
+#pragma unroll
+                    for (int j = 0; j < SN; ++j) mfma_chunk(acc[i][j], fa[s & 1][i], fb[s & 1][j], T{});
+                    if (s + 1 < SUB) {
+                        fa[(s + 1) & 1][i] = L[swz(arow + i * 32, cn)];
+                        if (i < SN) fb[(s + 1) & 1][i] = L[swz(brow + i * 32, cn)];
+                    }
+                    const int g = s * SM + i;
+                    if (g < LOADS && more) issue(kt + 1, g);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-#pragma unroll
-                for (int j = 0; j < SN; ++j) {
-                    const int row = BM + wn * WN + j * 32 + r32;
-                    bfr[j] = L[row * CHUNKS_PER_ROW + (c ^ (row & 7))];
-                }
-#pragma unroll
-                for (int i = 0; i < SM; ++i)
-#pragma unroll
-                    for (int j = 0; j < SN; ++j) mfma_chunk(acc[i][j], af[i], bfr[j], T{});
             }
-            u32x4* Ln = lds + ((kt + 1) & 1) * STAGE;
-#pragma unroll
-            for (int p = 0; p < LOADS; ++p) Ln[dst[p]] = stage[p];
-            __syncthreads();
         }
     }
 };

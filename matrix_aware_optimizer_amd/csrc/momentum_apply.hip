@@ -20,28 +20,26 @@ namespace {
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {
-    static __device__ inline float load(const void* p, size_t i) { return static_cast<const float*>(p)[i]; }
-    static __device__ inline void store(void* p, size_t i, float v) { static_cast<float*>(p)[i] = v; }
+    static __device__ inline float load(const void* p, size_t i) { return G(static_cast<const float*>(p))[i]; }
+    static __device__ inline void store(void* p, size_t i, float v) { G(static_cast<float*>(p))[i] = v; }
 };
 template <> struct Elem<uint16_t> {
     static __device__ inline float load(const void* p, size_t i) {
-        return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+        return bf16_to_f32(G(static_cast<const uint16_t*>(p))[i]);
     }
     static __device__ inline void store(void* p, size_t i, float v) {
-        static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+        G(static_cast<uint16_t*>(p))[i] = f32_to_bf16(v);
     }
 };
 
 // Store 4 consecutive values of the operand dtype (8-byte or 16-byte store).
 template <typename T> __device__ inline void store4(void* base, size_t idx, float v0, float v1, float v2, float v3);
 template <> __device__ inline void store4<float>(void* base, size_t idx, float v0, float v1, float v2, float v3) {
-    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = make_float4(v0, v1, v2, v3);
+    st_f4(static_cast<float*>(base) + idx, make_float4(v0, v1, v2, v3));
 }
 template <> __device__ inline void store4<uint16_t>(void* base, size_t idx, float v0, float v1, float v2, float v3) {
-    uint2 p;
-    p.x = static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
-    p.y = static_cast<uint32_t>(f32_to_bf16(v2)) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = p;
+    const u32x2_t p = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+    st_u2(static_cast<uint16_t*>(base) + idx, p);
 }
 
 // Deterministic block sum (fixed shuffle pattern, fixed wave order).
@@ -125,7 +123,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
                 sq = fmaf(v0, v0, sq); sq = fmaf(v1, v1, sq);
                 sq = fmaf(v2, v2, sq); sq = fmaf(v3, v3, sq);
                 const size_t idx = static_cast<size_t>(i0 + il) * d.np + (j0 + jl);
-                *reinterpret_cast<float4*>(d.x32 + idx) = make_float4(v0, v1, v2, v3);
+                st_f4(d.x32 + idx, make_float4(v0, v1, v2, v3));
                 if (sizeof(T) == 2) store4<T>(d.xop, idx, v0, v1, v2, v3);
             }
         }
@@ -140,7 +138,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
             }
         }
         const float total = block_sum_256(sq, red);   // also orders LDS reuse
-        if (tid == 0) args.partials[t] = total;
+        if (tid == 0) G(args.partials)[t] = total;
     }
 }
 
@@ -162,8 +160,8 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* descs
     }
     if (threadIdx.x == 0) {
         const double nrm = sqrt(red[0]);
-        d.scal[0] = static_cast<float>(1.0 / (nrm + static_cast<double>(eps)));
-        d.scal[1] = static_cast<float>(nrm);
+        G(d.scal)[0] = static_cast<float>(1.0 / (nrm + static_cast<double>(eps)));
+        G(d.scal)[1] = static_cast<float>(nrm);
     }
 }
 
@@ -190,13 +188,13 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(EwArgs args) {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int il = (tid >> 4) + 16 * p;
-                const float4 v = *reinterpret_cast<const float4*>(d.x32 + static_cast<size_t>(i0 + il) * d.np + (j0 + jl));
+                const float4 v = ld_f4(d.x32 + static_cast<size_t>(i0 + il) * d.np + (j0 + jl));
                 tile[il][jl] = v.x; tile[il][jl + 1] = v.y; tile[il][jl + 2] = v.z; tile[il][jl + 3] = v.w;
             }
         }
         __syncthreads();
         // with no Newton-Schulz step the output is the normalized input
-        const float oscale = args.ns_zero ? d.scal[0] : 1.0f;
+        const float oscale = args.ns_zero ? G(d.scal)[0] : 1.0f;
         const int ur0 = d.tall ? j0 : i0;
         const int uc0 = d.tall ? i0 : j0;
         const float coef = d.apply_coef * oscale;
@@ -210,7 +208,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(EwArgs args) {
                 const float o = d.tall ? tile[lc][lr] : tile[lr][lc];
                 const size_t idx = static_cast<size_t>(ur) * d.cols + uc;
                 if (NS_ONLY) {
-                    d.out[idx] = o * oscale;
+                    G(d.out)[idx] = o * oscale;
                 } else {
                     const float w = Elem<T>::load(d.w, idx);
                     Elem<T>::store(d.w, idx, fmaf(-coef, o, decay * w));

@@ -92,16 +92,42 @@ __device__ inline int find_matrix(const int32_t* prefix, int nmat, int t) {
     return lo;
 }
 
+// Pointers reached through the descriptor table are generic; viewing them in
+// the global address space lets the compiler emit global_* (not flat_*)
+// memory instructions, which only count against vmcnt.
+#define MUON_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ MUON_GLOBAL T* G(T* p) { return (MUON_GLOBAL T*)p; }
+
+// Native vectors for global accesses (HIP's float4 / uint2 wrappers cannot be
+// assigned across address spaces).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 ld_f4(const float* p) {
+    const f32x4_t v = G(reinterpret_cast<const f32x4_t*>(p))[0];
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_f4(float* p, float4 v) {
+    const f32x4_t w = {v.x, v.y, v.z, v.w};
+    G(reinterpret_cast<f32x4_t*>(p))[0] = w;
+}
+__device__ __forceinline__ u32x2_t ld_u2(const void* p) { return G(static_cast<const u32x2_t*>(p))[0]; }
+__device__ __forceinline__ void st_u2(void* p, u32x2_t v) { G(static_cast<u32x2_t*>(p))[0] = v; }
+
 // bf16 <-> fp32 (bf16 kept as its 16-bit pattern).
-__device__ inline float bf16_to_f32(uint16_t h) {
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
-// Round to nearest, ties to even; NaN stays NaN.
-__device__ inline uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+// Round to nearest, ties to even (v_cvt_pk_bf16_f32 on gfx950); NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// Two values packed into one dword, low half first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 }  // namespace muon

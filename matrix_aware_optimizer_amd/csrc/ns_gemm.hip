@@ -173,27 +173,25 @@ struct Engine {
 // 4 consecutive elements along a row: load / store in the operand dtype.
 template <typename T> __device__ inline float4 ld_quad(const void* p, size_t i);
 template <> __device__ inline float4 ld_quad<float>(const void* p, size_t i) {
-    return *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    return ld_f4(static_cast<const float*>(p) + i);
 }
 template <> __device__ inline float4 ld_quad<uint16_t>(const void* p, size_t i) {
-    const uint2 q = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    const u32x2_t q = ld_u2(static_cast<const uint16_t*>(p) + i);
     return make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xffff0000u),
                        __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xffff0000u));
 }
 template <typename T> __device__ inline void st_quad(void* p, size_t i, float4 v);
 template <> __device__ inline void st_quad<float>(void* p, size_t i, float4 v) {
-    *reinterpret_cast<float4*>(static_cast<float*>(p) + i) = v;
+    st_f4(static_cast<float*>(p) + i, v);
 }
 template <> __device__ inline void st_quad<uint16_t>(void* p, size_t i, float4 v) {
-    uint2 q;
-    q.x = static_cast<uint32_t>(f32_to_bf16(v.x)) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
-    q.y = static_cast<uint32_t>(f32_to_bf16(v.z)) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p) + i) = q;
+    const u32x2_t q = {pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+    st_u2(static_cast<uint16_t*>(p) + i, q);
 }
 template <typename T> __device__ inline void st_elem(void* p, size_t i, float v);
-template <> __device__ inline void st_elem<float>(void* p, size_t i, float v) { static_cast<float*>(p)[i] = v; }
+template <> __device__ inline void st_elem<float>(void* p, size_t i, float v) { G(static_cast<float*>(p))[i] = v; }
 template <> __device__ inline void st_elem<uint16_t>(void* p, size_t i, float v) {
-    static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+    G(static_cast<uint16_t*>(p))[i] = f32_to_bf16(v);
 }
 __device__ inline float f4get(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
 
@@ -234,6 +232,7 @@ __device__ __attribute__((always_inline)) void epilogue(f32x16_t (&acc)[E::SM][E
                 sbuf[sr * L::LDW + sc] = acc[i][j][r];
             }
         __syncthreads();
+#pragma unroll
         for (int it = 0; it < L::ROW_ITERS; ++it) {
             const int q = tid + GEMM_THREADS * it;
             const int sr = q / (E::BN / 4), sc = (q % (E::BN / 4)) * 4;
@@ -245,6 +244,7 @@ __device__ __attribute__((always_inline)) void epilogue(f32x16_t (&acc)[E::SM][E
         }
         if (op.transposed) {
             __syncthreads();
+#pragma unroll
             for (int it = 0; it < L::COL_ITERS; ++it) {
                 const int q = tid + GEMM_THREADS * it;
                 const int kq = q & 7, rest = q >> 3;
@@ -324,10 +324,10 @@ struct UpdateOp {
     bool transposed;
     __device__ inline void row(int gi, int gj, float4& v) const {
         const size_t idx = static_cast<size_t>(gi) * np + gj;
-        const float4 x = *reinterpret_cast<const float4*>(x32 + idx);
+        const float4 x = ld_f4(x32 + idx);
         v.x = u * fmaf(a, x.x, v.x); v.y = u * fmaf(a, x.y, v.y);
         v.z = u * fmaf(a, x.z, v.z); v.w = u * fmaf(a, x.w, v.w);
-        *reinterpret_cast<float4*>(x32 + idx) = v;
+        st_f4(x32 + idx, v);
         if (sizeof(T) == 2 && transposed) st_quad<T>(xop, idx, v);
     }
     __device__ inline void col(int gj, int gi, const float4& v) const {
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void ns_gemm_kernel(NsArgs args) {
         GramOp<T> op;
         op.dst = d.amat; op.ld = mp; op.diag = ti == tj;
         // first step: X0 = s * M' is folded in as A0 = s^2 M' M'^T
-        op.scale = args.first ? d.scal[0] * d.scal[0] : 1.0f;
+        op.scale = args.first ? G(d.scal)[0] * G(d.scal)[0] : 1.0f;
         epilogue<E>(acc, sbuf, row0, col0, op);
     } else if (PHASE == PH_POLY) {
         const char* A = static_cast<const char*>(d.amat);
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void ns_gemm_kernel(NsArgs args) {
         op.x32 = d.x32; op.xop = d.xop; op.xnT = d.xopT[args.ping ^ 1];
         op.np = np; op.mp = mp; op.a = args.a;
         // first step: X1 = s (a M' + B0 M') with M' unscaled in x32 / xop
-        op.u = args.first ? d.scal[0] : 1.0f;
+        op.u = args.first ? G(d.scal)[0] : 1.0f;
         op.transposed = !args.last;
         epilogue<E>(acc, sbuf, row0, col0, op);
     }

@@ -383,3 +383,14 @@ def test_full_moe_expert_set(gpu_lib):
     _say("full MoE set, 192 matrices")
     # expert 0 gate, expert 7 down, expert 63 up (different per-expert scales)
     _full_workload_check(gpu_lib, wl, [0, 23, 190])
+
+
+def test_bf16_state_rounding_is_round_to_nearest_even(gpu_lib):
+    # beta = 1: M' = M + G is exact in fp32 for bf16 inputs of similar magnitude,
+    # so the stored bf16 state must equal the once-rounded exact sum bit for bit
+    # (ties included: sums of two bf16 values hit exact halfway points often).
+    wl = wk.custom_workload([(96, 160)], dtype="bf16", wid=212)
+    h = wk.host_matrix(wl, 0)
+    _, Mg = _step_gpu(gpu_lib, [h], "bf16", dict(wl.hp, beta=1.0, lr=0.0))
+    exact = h["M"].astype(np.float64) + h["G"].astype(np.float64)
+    assert np.array_equal(Mg[0], orc.rne(exact, "bf16"))

@@ -21,6 +21,7 @@ of the same workload on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +33,44 @@ sys.path.insert(0, ROOT)
 BF16_PEAK_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 F32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix
 HBM_PEAK_GBS = 8000.0
+
+
+KERNEL_SOURCES = ("matrix_aware_optimizer_amd/csrc/ns_gemm.hip", "matrix_aware_optimizer_amd/csrc/muon_internal.h")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "update_kernel_transformer_traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_id):
+    """HBM bytes per update launch from the committed counter runs, if they
+    were taken on the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash() or t.get("workload_id") != workload_id:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def calibrate_copy(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    x.fill_(1.0)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}), flush=True)
 
 
 def ns_flops(shapes, steps):
@@ -96,7 +135,13 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="workload id (1-5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU sharding of the "
@@ -192,7 +237,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(upd_tflops / peak, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
             "avg_launch_ms": round(upd_ms, 4),
             "flops_per_launch": update_flops_per_launch(wl.shapes),
         },

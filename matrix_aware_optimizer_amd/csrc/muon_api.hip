@@ -15,7 +15,7 @@
 #include <type_traits>
 #include <vector>
 
-#include "../../include/muon.h"
+#include "muon.h"
 #include "muon_internal.h"
 
 using namespace muon;
@@ -256,24 +256,27 @@ void rebase(Plan& pl, char* base) {
 
 std::mutex g_mu;
 
-muon_status check_device(int* dev_out) {
+muon_status check_device(int* dev_out, int* cu_count) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     static std::vector<int> ok_cache;   // -1 unknown, 0 no, 1 yes
+    static std::vector<int> cus;
     std::lock_guard<std::mutex> lk(g_mu);
-    if (static_cast<int>(ok_cache.size()) <= dev) ok_cache.resize(dev + 1, -1);
+    if (static_cast<int>(ok_cache.size()) <= dev) { ok_cache.resize(dev + 1, -1); cus.resize(dev + 1, 0); }
     if (ok_cache[dev] < 0) {
         hipDeviceProp_t prop;
         e = hipGetDeviceProperties(&prop, dev);
         if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
         ok_cache[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+        cus[dev] = prop.multiProcessorCount;
         if (!ok_cache[dev]) {
             g_last_error = std::string("device is ") + prop.gcnArchName + ", this library is built for gfx950";
         }
     }
     if (!ok_cache[dev]) return fail(MUON_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
     *dev_out = dev;
+    *cu_count = cus[dev];
     return MUON_OK;
 }
 
@@ -390,8 +393,8 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
             }
         }
     }
-    int dev = 0;
-    st = check_device(&dev);
+    int dev = 0, cu_count = 0;
+    st = check_device(&dev, &cu_count);
     if (st != MUON_OK) return st;
 
     char* base = static_cast<char*>(workspace);
@@ -418,7 +421,7 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
     ew.partials = d_partials;
     ew.nmat = nmat;
     ew.total = static_cast<int32_t>(pl.total_ew);
-    const int target_blocks = 256 * 8;
+    const int target_blocks = std::max(cu_count, 1) * 8;
     ew.tiles_per_block = static_cast<int32_t>(std::max<int64_t>(1, (pl.total_ew + target_blocks - 1) / target_blocks));
     ew.beta = ns_only ? 0.0f : hp->beta;
     ew.nesterov = (!ns_only && (hp->flags & MUON_FLAG_NESTEROV)) ? 1 : 0;

@@ -81,6 +81,14 @@ hipError_t launch_gram(int dtype, const NsArgs& args, hipStream_t s);
 hipError_t launch_poly(int dtype, const NsArgs& args, hipStream_t s);
 hipError_t launch_update(int dtype, const NsArgs& args, hipStream_t s);
 
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also fences
+// global memory, i.e. waits until every store the wave has issued is
+// acknowledged; in the store-heavy epilogues that wait dominated.  Here only
+// LDS operations are waited for, so global stores stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Index of the matrix that owns global tile t: the largest i with
 // prefix[i] <= t (prefix has nmat + 1 entries, prefix[0] = 0).
 __device__ inline int find_matrix(const int32_t* prefix, int nmat, int t) {

@@ -25,11 +25,12 @@
 // are issued between the MFMAs of the current one, at most 8 in flight.
 // Buffers are zero-padded to the block tile, so there are no edge masks.
 //
-// Grouping: one launch covers every matrix of the call.  The grid is the
+// Grouping: one launch covers every matrix of the call.  The tile space is the
 // concatenation of all matrices' tiles (per-matrix prefix sums, largest
-// matrices first); block ids are remapped so that runs of consecutive tiles
-// land on one XCD (the hardware deals workgroups round-robin over the 8 XCDs)
-// and share its L2.
+// matrices first), one workgroup per tile.  The hardware deals workgroups
+// round-robin over the 8 XCDs, so tiles that are close in this order run at
+// the same time; the update's tile order (grouped_decode) keeps such tiles on
+// shared operand blocks.
 #include "muon_internal.h"
 
 namespace muon {
@@ -53,8 +54,6 @@ constexpr int WAVES_M = 2, WAVES_N = 4;
 constexpr int NWAVES = WAVES_M * WAVES_N;
 static_assert(NWAVES * 64 == GEMM_THREADS, "GEMM_THREADS must match the wave layout");
 constexpr int CHUNKS_PER_ROW = 8;            // 8 x 16 B = 128 B of k per row per k-step
-constexpr int XCD_COUNT = 8;
-constexpr int XCD_RUN = 32;                  // consecutive tiles kept on one XCD
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -74,11 +73,19 @@ __device__ inline void mfma_chunk(f32x16_t& acc, const u32x4& a, const u32x4& b,
 // Physical position of logical 16-byte chunk c of LDS row `row`.
 __device__ __forceinline__ int swz(int row, int c) { return row * CHUNKS_PER_ROW + (c ^ ((row >> 1) & 7)); }
 
-__device__ inline int xcd_remap(int b, int nb) {
-    const int full = (nb / (XCD_COUNT * XCD_RUN)) * (XCD_COUNT * XCD_RUN);
-    if (b >= full) return b;
-    const int xcd = b % XCD_COUNT, slot = b / XCD_COUNT;
-    return ((slot / XCD_RUN) * XCD_COUNT + xcd) * XCD_RUN + slot % XCD_RUN;
+
+// Update-tile decode: tiles are ordered in groups of GROUP_M tile rows, column-
+// major inside a group, so a run of 32 consecutive tiles (what one XCD works
+// on at a time) is a GROUP_M x (32 / GROUP_M) block that shares GROUP_M row
+// blocks of B and 32 / GROUP_M row blocks of X^T in its L2.
+constexpr int GROUP_M = 4;
+__device__ inline void grouped_decode(int q, int tm, int tn, int& ti, int& tj) {
+    const int per_group = GROUP_M * tn;
+    const int g = q / per_group, r = q % per_group;
+    const int first = g * GROUP_M;
+    const int gsize = min(tm - first, GROUP_M);
+    ti = first + r % gsize;
+    tj = r / gsize;
 }
 
 // Upper-triangle tile decode: local index -> (ti, tj), ti <= tj, row-major.
@@ -220,7 +227,14 @@ __device__ __attribute__((always_inline)) void epilogue(f32x16_t (&acc)[E::SM][E
     using L = EpiLayout<E>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    __syncthreads();   // the k-loop's last LDS reads are done
+    auto rq = [&](int i, int it, int& gi, int& sc, int& sr) {   // the row pass's quads
+        const int q = tid + GEMM_THREADS * it;
+        sr = q / (E::BN / 4);
+        sc = (q % (E::BN / 4)) * 4;
+        gi = row0 + (sr >> 5) * E::WM + i * 32 + (sr & 31);
+    };
+    float4 pre[L::ROW_ITERS];
+    lds_barrier();   // the k-loop's last LDS reads are done
 #pragma unroll
     for (int i = 0; i < E::SM; ++i) {
 #pragma unroll
@@ -231,19 +245,28 @@ __device__ __attribute__((always_inline)) void epilogue(f32x16_t (&acc)[E::SM][E
                 const int sc = wn * E::WN + j * 32 + (lane & 31);
                 sbuf[sr * L::LDW + sc] = acc[i][j][r];
             }
-        __syncthreads();
+        // acc[i] is in LDS now; its registers take this pass's operands from
+        // memory, whose latency overlaps the barrier
+        if (Op::PREFETCH) {
+#pragma unroll
+            for (int it = 0; it < L::ROW_ITERS; ++it) {
+                int gi, sc, sr;
+                rq(i, it, gi, sc, sr);
+                pre[it] = op.fetch(gi, col0 + sc);
+            }
+        }
+        lds_barrier();
 #pragma unroll
         for (int it = 0; it < L::ROW_ITERS; ++it) {
-            const int q = tid + GEMM_THREADS * it;
-            const int sr = q / (E::BN / 4), sc = (q % (E::BN / 4)) * 4;
-            const int gi = row0 + (sr >> 5) * E::WM + i * 32 + (sr & 31);
+            int gi, sc, sr;
+            rq(i, it, gi, sc, sr);
             float4* cell = reinterpret_cast<float4*>(sbuf + sr * L::LDW + sc);
             float4 v = *cell;
-            op.row(gi, col0 + sc, v);
+            op.row(gi, col0 + sc, v, pre[it]);
             *cell = v;
         }
         if (op.transposed) {
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int it = 0; it < L::COL_ITERS; ++it) {
                 const int q = tid + GEMM_THREADS * it;
@@ -255,7 +278,7 @@ __device__ __attribute__((always_inline)) void epilogue(f32x16_t (&acc)[E::SM][E
                 op.col(col0 + sc, row0 + strip * E::WM + i * 32 + kq * 4, v);
             }
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -293,8 +316,10 @@ struct SymStore {
 
 template <typename T>
 struct GramOp : SymStore<T> {
+    static constexpr bool PREFETCH = false;
     float scale;
-    __device__ inline void row(int gi, int gj, float4& v) const {
+    __device__ inline float4 fetch(int, int) const { return make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ inline void row(int gi, int gj, float4& v, const float4&) const {
         v.x *= scale; v.y *= scale; v.z *= scale; v.w *= scale;
         this->put_row(gi, gj, v);
     }
@@ -302,29 +327,33 @@ struct GramOp : SymStore<T> {
 
 template <typename T>
 struct PolyOp : SymStore<T> {
+    static constexpr bool PREFETCH = true;
     const void* a;
     float b, c;
-    __device__ inline void row(int gi, int gj, float4& v) const {
-        const float4 av = ld_quad<T>(a, static_cast<size_t>(gi) * this->ld + gj);
+    __device__ inline float4 fetch(int gi, int gj) const { return ld_quad<T>(a, static_cast<size_t>(gi) * this->ld + gj); }
+    __device__ inline void row(int gi, int gj, float4& v, const float4& av) const {
         v.x = fmaf(c, v.x, b * av.x); v.y = fmaf(c, v.y, b * av.y);
         v.z = fmaf(c, v.z, b * av.z); v.w = fmaf(c, v.w, b * av.w);
         this->put_row(gi, gj, v);
     }
 };
 
-// X' = u (a X + B X): fp32 iterate in place, bf16 operand copy, transposed
-// operand copy for the next step (skipped after the last step).
+// X' = u (a X + B X): the epilogue adds a X (fp32 iterate, requested while
+// the pass is staged), scales by u and writes the fp32 iterate in place, its
+// bf16 operand copy and the transposed operand copy for the next step (both
+// skipped after the last step).
 template <typename T>
 struct UpdateOp {
+    static constexpr bool PREFETCH = true;
     float* x32;
     void* xop;
     void* xnT;
     size_t np, mp;
     float a, u;
     bool transposed;
-    __device__ inline void row(int gi, int gj, float4& v) const {
+    __device__ inline float4 fetch(int gi, int gj) const { return ld_f4(x32 + static_cast<size_t>(gi) * np + gj); }
+    __device__ inline void row(int gi, int gj, float4& v, const float4& x) const {
         const size_t idx = static_cast<size_t>(gi) * np + gj;
-        const float4 x = ld_f4(x32 + idx);
         v.x = u * fmaf(a, x.x, v.x); v.y = u * fmaf(a, x.y, v.y);
         v.z = u * fmaf(a, x.z, v.z); v.w = u * fmaf(a, x.w, v.w);
         st_f4(x32 + idx, v);
@@ -336,13 +365,8 @@ struct UpdateOp {
 };
 
 template <typename T, int PHASE>
-__global__ __launch_bounds__(GEMM_THREADS, 1) void ns_gemm_kernel(NsArgs args) {
+__device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, int t, u32x4* lds) {
     using E = Engine<T>;
-    static_assert(EpiLayout<E>::FLOATS * 4 <= 2 * E::STAGE * 16, "epilogue staging exceeds LDS");
-    __shared__ u32x4 lds[2 * E::STAGE];
-
-    const int t = xcd_remap(blockIdx.x, gridDim.x);
-    if (t >= args.total) return;
     const int mi = find_matrix(args.prefix, args.nmat, t);
     const MatDesc& d = args.descs[mi];
     const int local = t - args.prefix[mi];
@@ -350,9 +374,7 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void ns_gemm_kernel(NsArgs args) {
 
     int ti, tj;
     if (PHASE == PH_UPDATE) {
-        const int tn = np / E::BN;
-        ti = local / tn;
-        tj = local % tn;
+        grouped_decode(local, mp / E::BM, np / E::BN, ti, tj);
     } else {
         sym_decode(local, mp / E::BM, ti, tj);
     }
@@ -390,6 +412,14 @@ __global__ __launch_bounds__(GEMM_THREADS, 1) void ns_gemm_kernel(NsArgs args) {
         op.transposed = !args.last;
         epilogue<E>(acc, sbuf, row0, col0, op);
     }
+}
+
+template <typename T, int PHASE>
+__global__ __launch_bounds__(GEMM_THREADS, 1) void ns_gemm_kernel(NsArgs args) {
+    using E = Engine<T>;
+    static_assert(EpiLayout<E>::FLOATS * 4 <= 2 * E::STAGE * 16, "epilogue staging exceeds LDS");
+    __shared__ u32x4 lds[2 * E::STAGE];
+    if (static_cast<int>(blockIdx.x) < args.total) process_tile<T, PHASE>(args, blockIdx.x, lds);
 }
 
 template <int PHASE>

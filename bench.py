@@ -35,6 +35,22 @@ F32_PEAK_TFLOPS = 157.3       # MI355X fp32 matrix
 HBM_PEAK_GBS = 8000.0
 
 
+# The rocprofv3 session the profiles/ summaries come from (run from the repository root).
+PROFILE_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp",
+    "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o transformer "
+    "-- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"ns_gemm_kernel<unsigned short, 2>\" --output-format csv "
+    "-d $R/gpurun_out/prof/fetch -o upd -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"ns_gemm_kernel<unsigned short, 2>\" --output-format csv "
+    "-d $R/gpurun_out/prof/write -o upd -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/cfetch -o copy "
+    "-- python3 $R/bench.py --calibrate-copy",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/cwrite -o copy "
+    "-- python3 $R/bench.py --calibrate-copy",
+    "python3 bench.py --summarize-profiles gpurun_out/prof",
+]
+
 KERNEL_SOURCES = ("matrix_aware_optimizer_amd/csrc/ns_gemm.hip", "matrix_aware_optimizer_amd/csrc/muon_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "update_kernel_transformer_traffic.json")
 
@@ -73,6 +89,81 @@ def calibrate_copy(nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}), flush=True)
 
 
+def _counter_rows(path, name_part=None):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(path, "*counter_collection.csv"))):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if name_part is None or name_part in r["Kernel_Name"]:
+                    rows.append(r)
+    return rows
+
+
+UPDATE_KERNEL = "ns_gemm_kernel<unsigned short, 2>"
+
+
+def summarize_profiles(prof_dir, workload_id, commands):
+    """Turn one rocprofv3 session (kernel trace, FETCH_SIZE and WRITE_SIZE runs of
+    the update kernel, and the same two counters on a 1 GiB device copy) into
+    the text summaries kept under profiles/."""
+    import csv
+    import glob
+    stats = sorted(glob.glob(os.path.join(prof_dir, "trace", "*_kernel_stats.csv")))[0]
+    with open(stats) as fh:
+        krows = list(csv.DictReader(fh))
+    copy_bytes = 1 << 30
+    cf = [float(r["Counter_Value"]) for r in _counter_rows(os.path.join(prof_dir, "cfetch"), "copyBuffer")]
+    cw = [float(r["Counter_Value"]) for r in _counter_rows(os.path.join(prof_dir, "cwrite"), "copyBuffer")]
+    fetch_factor = copy_bytes / (sum(cf) / len(cf) * 1024.0)
+    write_factor = copy_bytes / (sum(cw) / len(cw) * 1024.0)
+    uf = [float(r["Counter_Value"]) for r in _counter_rows(os.path.join(prof_dir, "fetch"), UPDATE_KERNEL)]
+    uw = [float(r["Counter_Value"]) for r in _counter_rows(os.path.join(prof_dir, "write"), UPDATE_KERNEL)]
+    # launches per step: ns_steps; the last one writes only the fp32 iterate
+    import workloads as wk
+    wl = wk.WORKLOADS[workload_id]
+    T = len(wl.hp["schedule"])
+    read_b = sum(uf) / len(uf) * 1024.0 * fetch_factor
+    write_b = sum(uw) / len(uw) * 1024.0 * write_factor
+    traffic = {
+        "workload_id": workload_id,
+        "kernel": UPDATE_KERNEL,
+        "source_hash": kernel_source_hash(),
+        "dispatches": len(uf),
+        "fetch_kib_per_dispatch_raw": round(sum(uf) / len(uf), 1),
+        "write_kib_per_dispatch_raw": round(sum(uw) / len(uw), 1),
+        "fetch_scale": round(fetch_factor, 4),
+        "write_scale": round(write_factor, 4),
+        "read_bytes_per_launch": int(read_b),
+        "write_bytes_per_launch": int(write_b),
+        "bytes_per_launch": int(read_b + write_b),
+        "note": f"average over all update launches, {T} per step (the last writes only the fp32 iterate)",
+        "commands": commands,
+    }
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(traffic, fh, indent=1)
+        fh.write("\n")
+    lines = [f"# Kernel time per launch, {wl.name}", "",
+             "rocprofv3 --kernel-trace --stats summary (`*_kernel_stats.csv`), library kernels only.", "",
+             "Commands (from the repository root; `R` is its absolute path):", ""]
+    lines += [f"    {c}" for c in commands] + [""]
+    lines += ["| kernel | calls | avg ms | min ms | max ms | % of GPU time |", "|---|---|---|---|---|---|"]
+    for r in krows:
+        if "muon::" not in r["Name"]:
+            continue
+        nm = r["Name"].replace("void ", "").replace("muon::(anonymous namespace)::", "").split("(")[0]
+        lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | {float(r['MinNs']) / 1e6:.4f} | "
+                     f"{float(r['MaxNs']) / 1e6:.4f} | {float(r['Percentage']):.2f} |")
+    lines += ["", f"Update kernel HBM traffic per launch (FETCH_SIZE x {fetch_factor:.3f}, WRITE_SIZE x "
+              f"{write_factor:.3f}, factors from a 1 GiB device copy): read {read_b / 1e9:.3f} GB, "
+              f"write {write_b / 1e9:.3f} GB.", ""]
+    out = os.path.join(ROOT, "profiles", f"kernels_{wk.short_name(workload_id)}.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print(json.dumps({"written": [os.path.relpath(out, ROOT), os.path.relpath(TRAFFIC_FILE, ROOT)]}))
+
+
 def ns_flops(shapes, steps):
     tot = 0
     for r, c in shapes:
@@ -87,7 +178,6 @@ def update_flops_per_launch(shapes):
 
 def cpu_baseline(wl, budget_s=20.0):
     """Time the fp64 oracle on a bounded sample of the workload's matrices."""
-    import numpy as np
     import oracle as orc
     import workloads as wk
     try:
@@ -95,17 +185,9 @@ def cpu_baseline(wl, budget_s=20.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    # keep the workload's shape mix: walk distinct shapes round-robin
-    by_shape = {}
-    for i, s in enumerate(wl.shapes):
-        by_shape.setdefault(s, []).append(i)
-    counts = {s: len(v) for s, v in by_shape.items()}
-    order = []
-    total = sum(counts.values())
-    # proportional sample: for c3 this is 4 square : 1 up : 1 down
-    g = min(counts.values())
-    for s, v in by_shape.items():
-        order.extend(v[: max(1, counts[s] // g)])
+    # workload order keeps the shape mix (per layer: Q, K, V, O, up, down; per expert: gate, up, down)
+    total = len(wl.shapes)
+    order = range(total)
     hp = wl.hp
     done, t_used, names = 0, 0.0, []
     for i in order:
@@ -118,12 +200,17 @@ def cpu_baseline(wl, budget_s=20.0):
         names.append("x".join(map(str, wl.shapes[i])))
         if t_used > budget_s:
             break
+    shapes = {}
+    for nm in names:
+        shapes[nm] = shapes.get(nm, 0) + 1
     return {
         "value": done / t_used,
         "unit": "matrices/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{done} of {total} matrices ({', '.join(names)}), fp64 numpy, {t_used:.1f} s",
+        "sample": f"first {done} of {total} matrices in workload order "
+                  f"({', '.join(f'{c} x {k}' for k, c in shapes.items())}), full muon_step each, "
+                  f"fp64 numpy, {t_used:.1f} s",
     }
 
 
@@ -137,10 +224,15 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write the profiles/ summaries from a rocprofv3 session under DIR (no GPU)")
     args = ap.parse_args()
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload, PROFILE_COMMANDS)
         return
 
     if args.gpus != 1:

@@ -96,6 +96,15 @@ WORKLOADS = {
 }
 
 
+SHORT_NAMES = {1: "single_f32_128x256", 2: "single_bf16_4096_lowrank", 3: "transformer_d2048_24l",
+               4: "moe_64_experts", 5: "mlp_16x28672x8192"}
+
+
+def short_name(wid):
+    """File-name friendly label of a workload."""
+    return SHORT_NAMES.get(wid, f"workload{wid}")
+
+
 def custom_workload(shapes, dtype="bf16", grad="gauss", grad_std=1.0, rank=0, noise_std=0.0,
                     momentum="same", wid=100, **hp):
     """A workload with arbitrary shapes (tests use it for ragged and edge cases)."""

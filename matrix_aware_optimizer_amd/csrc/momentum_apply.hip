@@ -64,9 +64,9 @@ __device__ inline void ew_tile_origin(const MatDesc& d, int local, int& i0, int&
 // ----------------------------------------------------------------------------
 // Momentum + norm partials + operand copies.
 //   user-frame load (coalesced) -> fp32 M' (state store) -> U into LDS in the
-//   NS frame -> X32 / Xop rows (coalesced) and Xop^T rows (coalesced), with
-//   the sum of squares taken in NS-frame order so the result does not depend
-//   on the caller's orientation.
+//   NS frame -> rows of the fp32 iterate and its bf16 operand copy
+//   (coalesced), with the sum of squares taken in NS-frame order so the
+//   result does not depend on the caller's orientation.
 // ----------------------------------------------------------------------------
 template <typename T, bool NS_ONLY>
 __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) {
@@ -123,18 +123,8 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
                 sq = fmaf(v0, v0, sq); sq = fmaf(v1, v1, sq);
                 sq = fmaf(v2, v2, sq); sq = fmaf(v3, v3, sq);
                 const size_t idx = static_cast<size_t>(i0 + il) * d.np + (j0 + jl);
-                st_f4(d.x32 + idx, make_float4(v0, v1, v2, v3));
-                if (sizeof(T) == 2) store4<T>(d.xop, idx, v0, v1, v2, v3);
-            }
-        }
-        // ---- NS-frame transposed rows: Xop^T (ping 0)
-        {
-            const int il = (tid & 15) * 4;
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int jl = (tid >> 4) + 16 * p;
-                const size_t idx = static_cast<size_t>(j0 + jl) * d.mp + (i0 + il);
-                store4<T>(d.xopT[0], idx, tile[il][jl], tile[il + 1][jl], tile[il + 2][jl], tile[il + 3][jl]);
+                st_f4(d.x32[0] + idx, make_float4(v0, v1, v2, v3));
+                if (sizeof(T) == 2) store4<T>(d.xop[0], idx, v0, v1, v2, v3);
             }
         }
         const float total = block_sum_256(sq, red);   // also orders LDS reuse
@@ -188,7 +178,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(EwArgs args) {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int il = (tid >> 4) + 16 * p;
-                const float4 v = ld_f4(d.x32 + static_cast<size_t>(i0 + il) * d.np + (j0 + jl));
+                const float4 v = ld_f4(d.x32[args.fin] + static_cast<size_t>(i0 + il) * d.np + (j0 + jl));
                 tile[il][jl] = v.x; tile[il][jl + 1] = v.y; tile[il][jl + 2] = v.z; tile[il][jl + 3] = v.w;
             }
         }

@@ -213,17 +213,21 @@ muon_status build_plan(std::vector<Item>& items, const muon_hparams* hp, bool ns
     for (int k = 0; k < nmat; ++k) {
         MatDesc& d = pl.descs[k];
         const size_t mn = static_cast<size_t>(d.mp) * d.np, mm = static_cast<size_t>(d.mp) * d.mp;
-        d.x32 = reinterpret_cast<float*>(off);
+        // bf16: one fp32 iterate (updated in place) and two bf16 operand copies;
+        // fp32: two iterates that are their own operands
+        d.x32[0] = reinterpret_cast<float*>(off);
         off = align_up(off + mn * 4, ALIGN);
         if (dtype == MUON_BF16) {
-            d.xop = reinterpret_cast<void*>(off);
-            off = align_up(off + mn * es, ALIGN);
+            d.x32[1] = d.x32[0];
+            for (int p = 0; p < 2; ++p) {
+                d.xop[p] = reinterpret_cast<void*>(off);
+                off = align_up(off + mn * es, ALIGN);
+            }
         } else {
-            d.xop = d.x32;
-        }
-        for (int p = 0; p < 2; ++p) {
-            d.xopT[p] = reinterpret_cast<void*>(off);
-            off = align_up(off + mn * es, ALIGN);
+            d.x32[1] = reinterpret_cast<float*>(off);
+            off = align_up(off + mn * 4, ALIGN);
+            d.xop[0] = d.x32[0];
+            d.xop[1] = d.x32[1];
         }
         d.amat = reinterpret_cast<void*>(off);
         off = align_up(off + mm * es, ALIGN);
@@ -240,10 +244,10 @@ void rebase(Plan& pl, char* base) {
         p = reinterpret_cast<P>(base + reinterpret_cast<uintptr_t>(p));
     };
     for (MatDesc& d : pl.descs) {
-        fix(d.x32);
-        fix(d.xop);
-        fix(d.xopT[0]);
-        fix(d.xopT[1]);
+        fix(d.x32[0]);
+        fix(d.x32[1]);
+        fix(d.xop[0]);
+        fix(d.xop[1]);
         fix(d.amat);
         fix(d.bmat);
         fix(d.scal);
@@ -426,6 +430,7 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
     ew.beta = ns_only ? 0.0f : hp->beta;
     ew.nesterov = (!ns_only && (hp->flags & MUON_FLAG_NESTEROV)) ? 1 : 0;
     ew.ns_zero = hp->ns_steps == 0 ? 1 : 0;
+    ew.fin = hp->ns_steps & 1;
     const int ew_grid = static_cast<int>((pl.total_ew + ew.tiles_per_block - 1) / ew.tiles_per_block);
     const int dtype = hp->dtype;
 

@@ -35,10 +35,11 @@ struct MatDesc {
     int32_t mp, np;     // NS frame padded to the GEMM tile
     int32_t tall;       // 1 if rows > cols
     int32_t pad0;
-    // workspace buffers (NS frame, zero-padded)
-    float* x32;         // mp x np fp32 iterate
-    void* xop;          // mp x np operand copy (bf16); equals x32 for fp32
-    void* xopT[2];      // np x mp operand copies of X^T, ping-pong between steps
+    // workspace buffers (NS frame, zero-padded).  Step k reads index k & 1 and
+    // writes index (k & 1) ^ 1.
+    float* x32[2];      // mp x np fp32 iterate: one buffer updated in place (bf16, both
+                        // entries equal) or a ping-pong pair (fp32, read as the operand)
+    void* xop[2];       // mp x np bf16 operand copies, ping-pong; equal to x32 for fp32
     void* amat;         // mp x mp, A = X X^T (symmetric, stored in full)
     void* bmat;         // mp x mp, B = b A + c A A (symmetric, stored in full)
     float* scal;        // [0] = 1 / (||U||_F + eps), [1] = ||U||_F
@@ -59,6 +60,7 @@ struct EwArgs {
     float beta;
     int32_t nesterov;
     int32_t ns_zero;         // 1 when ns_steps == 0 (output is the normalized input)
+    int32_t fin;             // x32[fin] holds the last step's iterate (ns_steps & 1)
 };
 
 struct NsArgs {
@@ -69,7 +71,7 @@ struct NsArgs {
     float a, b, c;           // this step's coefficients
     int32_t first;           // first step: fold the normalization scale in
     int32_t last;            // last step: only the fp32 iterate is needed
-    int32_t ping;            // xopT[ping] is read, xopT[ping ^ 1] written
+    int32_t ping;            // x32 / xop index read by this step; ping ^ 1 is written
 };
 
 // Kernel launchers (defined next to the kernels).

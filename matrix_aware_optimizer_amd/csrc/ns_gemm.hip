@@ -3,34 +3,45 @@
 // One step of the quintic iteration ([Muon优化器] linsight.cn/f25d614e.html,
 // zeropower_via_newtonschulz and section "Newton-Schulz 迭代——高效实现与系数
 // 优化") on the NS-frame iterate X (m x n, m <= n):
-//     A  = X X^T                 (gram_kernel: symmetric, upper half tiles)
-//     B  = b A + c A A           (poly_kernel: A A = A A^T, upper half tiles)
-//     X' = a X + B X             (update_kernel)
-// All three are "TN" products C[i][j] = sum_k P[i][k] Q[j][k] with both
-// operands stored k-contiguous: P = Q = X for the Gram, P = Q = A for the
-// polynomial (A is symmetric), and P = B, Q = X^T for the update (the
-// workspace keeps a transposed operand copy of X for that).
+//     A  = X X^T                 (Gram: symmetric, upper half tiles)
+//     B  = b A + c A A           (polynomial: A A = A A^T, upper half tiles)
+//     X' = a X + B X             (update)
+// Products C[i][j] = sum_k P[i][k] Q[k][j].  P is always stored k-contiguous
+// (rows of X for the Gram, of A for the polynomial, of B for the update).  Q
+// is k-contiguous too for the Gram and the polynomial (Q^T = X and A), and
+// k-major for the update, where Q = X is read in its own row-major layout.
 //
 // Engine: a 256 x 256 (bf16) or 128 x 128 (fp32) block tile per workgroup of
-// 8 waves (2 x 4, two waves per SIMD so one can issue MFMAs while the other
-// waits on memory); each wave owns a 128 x 64 (64 x 32) sub-tile built from
-// 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x2_f32,
-// fp32 accumulation).  Each k-step stages 128 bytes of every operand row in
-// LDS with direct global->LDS loads (global_load_lds_dwordx4, no VGPR
-// staging), double-buffered; the loads of the next k-step are spread between
-// the MFMA groups of the current one.  16-byte chunks are XOR-swizzled with
-// bits 1..3 of the row, which keeps ds_read_b128 fragment reads free of bank
-// conflicts on gfx950's LDS (measured with SQ_LDS_BANK_CONFLICT).  MFMA
-// fragments are double-buffered in registers: the reads for the next k-slice
-// are issued between the MFMAs of the current one, at most 8 in flight.
+// 8 waves (2 x 4, two waves per SIMD); each wave owns a 128 x 64 (64 x 32)
+// sub-tile of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16 /
+// v_mfma_f32_32x32x2_f32, fp32 accumulation).  A k-step stages 128 bytes of
+// every k-contiguous operand row (or 64 / 32 k-rows of a k-major operand, one
+// 512-byte tile row each) in LDS with direct global->LDS loads
+// (global_load_lds_dwordx4, no VGPR staging), double-buffered; the next
+// k-step's loads are spread between the current one's MFMA groups, and MFMA
+// fragments are double-buffered in registers.
+//
+// LDS layouts.  k-contiguous rows: 16-byte chunks XOR-swizzled with bits 1..3
+// of the row, so 32-row ds_read_b128 fragment reads are free of bank
+// conflicts.  k-major rows: chunks swizzled with (row & 3) << 2, which moves
+// the 64-byte piece a wave reads from each of 8 k-rows into all four 64-byte
+// bank windows.  k-major bf16 fragments are read with ds_read_b64_tr_b16:
+// within each group of 16 lanes the instruction hands lane l element (l & 3)
+// of the 8 bytes addressed by lane 4e + (l >> 2) as its element e, so lanes
+// addressing X[k0 + i/4][n0 + 4 (i%4)] receive column n0 + l, rows k0..k0+3:
+// two such reads form the 8-element k-slice of an MFMA B operand.
+//
+// Epilogues work from registers: a 4 x 4 transpose inside each lane quad
+// (DPP) turns a lane's 4 rows x 1 column of a 32 x 32 block into 1 row x 4
+// columns, for 16-byte (fp32) and 8-byte (bf16) row-contiguous accesses.  The
+// mirrored half of a symmetric output is stored from the untransposed layout.
 // Buffers are zero-padded to the block tile, so there are no edge masks.
 //
 // Grouping: one launch covers every matrix of the call.  The tile space is the
 // concatenation of all matrices' tiles (per-matrix prefix sums, largest
 // matrices first), one workgroup per tile.  The hardware deals workgroups
-// round-robin over the 8 XCDs, so tiles that are close in this order run at
-// the same time; the update's tile order (grouped_decode) keeps such tiles on
-// shared operand blocks.
+// round-robin over the 8 XCDs; block ids are remapped so that each XCD works
+// on runs of 32 consecutive tiles, whose operand blocks then share its L2.
 #include "muon_internal.h"
 
 namespace muon {
@@ -41,6 +52,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // native 16-byte vector (HIP's uint4 is a wrapper struct that defeats register promotion)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 template <typename T> struct Cfg;
 template <> struct Cfg<uint16_t> {      // 16-byte chunk = 8 bf16 along k
@@ -54,8 +66,13 @@ constexpr int WAVES_M = 2, WAVES_N = 4;
 constexpr int NWAVES = WAVES_M * WAVES_N;
 static_assert(NWAVES * 64 == GEMM_THREADS, "GEMM_THREADS must match the wave layout");
 constexpr int CHUNKS_PER_ROW = 8;            // 8 x 16 B = 128 B of k per row per k-step
+constexpr int QROW_CHUNKS = 32;              // k-major rows: 512 B = one tile width
+constexpr int XCD_COUNT = 8, XCD_RUN = 32;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) char lds_byte_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) float lds_float_t;
 
 // One 16-byte chunk per lane of both operands, accumulated into a 32 x 32 block.
 __device__ inline void mfma_chunk(f32x16_t& acc, const u32x4& a, const u32x4& b, uint16_t) {
@@ -70,14 +87,24 @@ __device__ inline void mfma_chunk(f32x16_t& acc, const u32x4& a, const u32x4& b,
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
-// Physical position of logical 16-byte chunk c of LDS row `row`.
+// Physical position of logical 16-byte chunk c of k-contiguous LDS row `row`.
 __device__ __forceinline__ int swz(int row, int c) { return row * CHUNKS_PER_ROW + (c ^ ((row >> 1) & 7)); }
+// Physical position of logical 16-byte chunk c of k-major LDS row `kr` (relative to the region).
+__device__ __forceinline__ int qswz(int kr, int c) { return kr * QROW_CHUNKS + (c ^ ((kr & 3) << 2)); }
 
+// Runs of XCD_RUN consecutive tiles on one XCD: block b runs on XCD b % 8.
+// A bijection on [0, nb); the tail beyond the last full round keeps its ids.
+__device__ inline int xcd_run_remap(int b, int nb) {
+    const int full = (nb / (XCD_COUNT * XCD_RUN)) * (XCD_COUNT * XCD_RUN);
+    if (b >= full) return b;
+    const int xcd = b % XCD_COUNT, slot = b / XCD_COUNT;
+    return ((slot / XCD_RUN) * XCD_COUNT + xcd) * XCD_RUN + slot % XCD_RUN;
+}
 
 // Update-tile decode: tiles are ordered in groups of GROUP_M tile rows, column-
 // major inside a group, so a run of 32 consecutive tiles (what one XCD works
 // on at a time) is a GROUP_M x (32 / GROUP_M) block that shares GROUP_M row
-// blocks of B and 32 / GROUP_M row blocks of X^T in its L2.
+// blocks of B and 32 / GROUP_M column blocks of X in its L2.
 constexpr int GROUP_M = 4;
 __device__ inline void grouped_decode(int q, int tm, int tn, int& ti, int& tj) {
     const int per_group = GROUP_M * tn;
@@ -96,41 +123,59 @@ __device__ inline void sym_decode(int q, int T, int& ti, int& tj) {
     tj = i + q;
 }
 
-template <typename T>
+// QK: Q is k-major (row k holds BN consecutive columns), else k-contiguous.
+template <typename T, bool QK>
 struct Engine {
     static constexpr int BM = Cfg<T>::BM, BN = Cfg<T>::BN;
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int SM = WM / 32, SN = WN / 32;
-    static constexpr int ROWS = BM + BN;                              // P rows then Q rows
-    static constexpr int STAGE = ROWS * CHUNKS_PER_ROW;               // 16-byte chunks per stage
-    static constexpr int ROWS_PER_LOAD = 64 / CHUNKS_PER_ROW;         // one wave load = 1 KB = 8 rows
+    static constexpr int KS = CHUNKS_PER_ROW * 16 / static_cast<int>(sizeof(T));   // k per k-step
+    static constexpr int P_CHUNKS = BM * CHUNKS_PER_ROW;              // P rows first, then Q
+    static constexpr int STAGE = (BM + BN) * CHUNKS_PER_ROW;          // 16-byte chunks per stage
     static constexpr int LOADS = STAGE / 64 / NWAVES;                 // loads per wave per k-step
     static constexpr int SUB = CHUNKS_PER_ROW / 2;                    // MFMA k-slices per k-step
     static constexpr int GROUPS = SUB * SM;                           // MFMA groups per k-step
     static_assert(LOADS <= GROUPS, "one load per MFMA group at most");
     static_assert(SM >= SN, "fragment prefetch pairs A row i with B row i");
+    static_assert((P_CHUNKS / 64) % LOADS == 0, "a wave loads P rows only or Q rows only");
+    static_assert(!QK || BN * static_cast<int>(sizeof(T)) == QROW_CHUNKS * 16, "k-major rows are one tile wide");
+    static_assert(!QK || KS * QROW_CHUNKS == BN * CHUNKS_PER_ROW, "k-major region fills the Q part of a stage");
 
-    // acc[i][j] = sum_k P[row0 + i][k] * Q[col0 + j][k] over the whole k range.
+    // acc[i][j] = sum_k P[row0 + i][k] * Q(k, col0 + j) over the whole k range, where
+    // P points at row row0 (pitch ldp bytes) and Q at row col0 (k-contiguous) or at
+    // column col0 of k-row 0 (k-major), pitch ldq bytes.
     static __device__ __attribute__((always_inline)) void run(const char* __restrict__ P, size_t ldp, const char* __restrict__ Q,
                                       size_t ldq, int ksteps, u32x4* lds, f32x16_t (&acc)[SM][SN]) {
         const int tid = threadIdx.x;
         const int lane = tid & 63, wave = tid >> 6;
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-        // Load j of this wave fills LDS chunks [(wave*LOADS + j)*64, +64) of a stage in
-        // lane order: lane l lands in row r = l / 8 of that 1 KB block at physical chunk
-        // l % 8, which holds the row's logical chunk (l % 8) ^ ((r >> 1) & 7).
+        // Load j of this wave fills stage chunks [(wave*LOADS + j)*64, +64) in lane order;
+        // the source address holds the logical chunk that the swizzle puts there.
         const char* src[LOADS];
+        const bool wave_q = wave * LOADS * 64 >= P_CHUNKS;
+        const size_t step = (wave_q && QK) ? static_cast<size_t>(KS) * ldq : static_cast<size_t>(CHUNKS_PER_ROW * 16);
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
-            const int row = (wave * LOADS + j) * ROWS_PER_LOAD + lane / CHUNKS_PER_ROW;
-            const int lc = (lane % CHUNKS_PER_ROW) ^ ((row >> 1) & 7);
-            src[j] = (row < BM ? P + row * ldp : Q + (row - BM) * ldq) + lc * 16;
+            const int chunk = (wave * LOADS + j) * 64 + lane;
+            if (!wave_q) {
+                const int row = chunk / CHUNKS_PER_ROW;
+                const int lc = (chunk % CHUNKS_PER_ROW) ^ ((row >> 1) & 7);
+                src[j] = P + row * ldp + lc * 16;
+            } else if (!QK) {
+                const int row = chunk / CHUNKS_PER_ROW;            // stage row, Q row = row - BM
+                const int lc = (chunk % CHUNKS_PER_ROW) ^ ((row >> 1) & 7);
+                src[j] = Q + (row - BM) * ldq + lc * 16;
+            } else {
+                const int qc = chunk - P_CHUNKS;
+                const int kr = qc / QROW_CHUNKS;
+                const int lc = (qc % QROW_CHUNKS) ^ ((kr & 3) << 2);
+                src[j] = Q + kr * ldq + lc * 16;
+            }
         }
         auto issue = [&](int kt, int j) {
             lds_ptr_t d = (lds_ptr_t)(lds + (kt & 1) * STAGE + (wave * LOADS + j) * 64);
-            __builtin_amdgcn_global_load_lds((const void*)(src[j] + static_cast<size_t>(kt) * (CHUNKS_PER_ROW * 16)),
-                                             d, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(src[j] + static_cast<size_t>(kt) * step), d, 16, 0, 0);
         };
 #pragma unroll
         for (int i = 0; i < SM; ++i)
@@ -150,12 +195,40 @@ struct Engine {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             asm volatile("s_barrier" ::: "memory");
             const u32x4* L = lds + (kt & 1) * STAGE;
+            const lds_byte_t* Lq = (const lds_byte_t*)(L + P_CHUNKS);
+            // B operand of k-slice s (16 bf16 or 8 fp32 of k) for 32-column block j
+            auto read_b = [&](int j, int s) -> u32x4 {
+                if (!QK) return L[swz(brow + j * 32, 2 * s + half)];
+                if (sizeof(T) == 2) {
+                    const int i16 = lane & 15, g16 = lane >> 4;
+                    const int col = wn * WN + j * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
+                    const int kr = 16 * s + 8 * (g16 >> 1) + (i16 >> 2);
+                    const int cb = (col & 7) * 2;
+                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4_t*)(Lq + qswz(kr, col >> 3) * 16 + cb));
+                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4_t*)(Lq + qswz(kr + 4, col >> 3) * 16 + cb));
+                    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+                    return u32x4{l2.x, l2.y, h2.x, h2.y};
+                } else {
+                    // MFMA e of the chunk pair uses k = 8 s + 4 half + e
+                    const int col = wn * WN + j * 32 + (lane & 31);
+                    const int kr = 8 * s + 4 * half;
+                    const int cb = (col & 3) * 4;
+                    u32x4 v;
+                    v.x = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 0, col >> 2) * 16 + cb));
+                    v.y = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 1, col >> 2) * 16 + cb));
+                    v.z = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 2, col >> 2) * 16 + cb));
+                    v.w = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 3, col >> 2) * 16 + cb));
+                    return v;
+                }
+            };
             const bool more = kt + 1 < ksteps;
             u32x4 fa[2][SM], fb[2][SN];
 #pragma unroll
             for (int i = 0; i < SM; ++i) fa[0][i] = L[swz(arow + i * 32, half)];
 #pragma unroll
-            for (int j = 0; j < SN; ++j) fb[0][j] = L[swz(brow + j * 32, half)];
+            for (int j = 0; j < SN; ++j) fb[0][j] = read_b(j, 0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < SUB; ++s) {
@@ -166,7 +239,7 @@ struct Engine {
                     for (int j = 0; j < SN; ++j) mfma_chunk(acc[i][j], fa[s & 1][i], fb[s & 1][j], T{});
                     if (s + 1 < SUB) {
                         fa[(s + 1) & 1][i] = L[swz(arow + i * 32, cn)];
-                        if (i < SN) fb[(s + 1) & 1][i] = L[swz(brow + i * 32, cn)];
+                        if (i < SN) fb[(s + 1) & 1][i] = read_b(i, s + 1);
                     }
                     const int g = s * SM + i;
                     if (g < LOADS && more) issue(kt + 1, g);
@@ -201,176 +274,169 @@ template <> __device__ inline void st_elem<uint16_t>(void* p, size_t i, float v)
     G(static_cast<uint16_t*>(p))[i] = f32_to_bf16(v);
 }
 __device__ inline float f4get(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+// Elements e with bit e of `mask` set; a whole-quad store when all are.
+template <typename T> __device__ inline void st_quad_masked(void* p, size_t i, const float4& v, unsigned mask) {
+    if (mask == 0xFu) {
+        st_quad<T>(p, i, v);
+    } else if (mask) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (mask & (1u << e)) st_elem<T>(p, i + e, f4get(v, e));
+    }
+}
 
 enum Phase { PH_GRAM = 0, PH_POLY = 1, PH_UPDATE = 2 };
 
 // ----------------------------------------------------------------------------
-// Epilogue.  The accumulators leave the registers through LDS in SM passes:
-// pass i stages the i-th 32-row block of every wave (WAVES_M strips of 32
-// rows x BN columns, fp32).  A row pass then finalizes 4 consecutive columns
-// per thread (coalesced along the output row) and writes the final values
-// back; an optional column pass stores the same values transposed, 4
-// consecutive rows per thread, 8 threads per 32-row column segment.
+// Epilogue helpers.  Accumulator register r of 32 x 32 block (i, j) holds, in
+// lane l, element (8 (r >> 2) + 4 (l >> 5) + (r & 3), l & 31) of the block:
+// for g = r >> 2 a lane holds 4 consecutive rows of one column.
 // ----------------------------------------------------------------------------
+template <int CTRL> __device__ __forceinline__ float qperm(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// 4 x 4 transpose inside each quad of lanes: on entry lane t of the quad holds
+// column t (v[p] = M[p][t]), on exit row t (v[p] = M[t][p]).
+__device__ __forceinline__ void quad_transpose(float (&v)[4]) {
+    const int t = threadIdx.x & 3;
+    float s[4], x[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) s[p] = qperm<0xB1>(v[p]);   // from lane t ^ 1
+#pragma unroll
+    for (int p = 0; p < 4; ++p) x[p] = ((p ^ t) & 1) ? s[p ^ 1] : v[p];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) s[p] = qperm<0x4E>(x[p]);   // from lane t ^ 2
+#pragma unroll
+    for (int p = 0; p < 4; ++p) v[p] = ((p ^ t) & 2) ? s[p ^ 2] : x[p];
+}
+
+// Per-lane coordinates inside a wave's sub-tile.
 template <typename E>
-struct EpiLayout {
-    static constexpr int STRIP_ROWS = 32 * WAVES_M;
-    static constexpr int LDW = E::BN + 4;                 // row stride in floats
-    static constexpr int FLOATS = STRIP_ROWS * LDW;
-    static constexpr int ROW_ITERS = STRIP_ROWS * (E::BN / 4) / GEMM_THREADS;
-    static constexpr int COL_ITERS = WAVES_M * E::BN * 8 / GEMM_THREADS;
+struct Coords {
+    int raw_row, raw_col;   // untransposed: rows raw_row + 32 i + 8 g + (0..3), column raw_col + 32 j
+    int tr_row, tr_col;     // transposed:   row tr_row + 32 i + 8 g, columns tr_col + 32 j + (0..3)
+    __device__ Coords(int row0, int col0) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+        const int c = lane & 31, h = lane >> 5;
+        raw_row = row0 + wm * E::WM + 4 * h;
+        raw_col = col0 + wn * E::WN + c;
+        tr_row = raw_row + (c & 3);
+        tr_col = col0 + wn * E::WN + (c & ~3);
+    }
 };
 
-template <typename E, typename Op>
-__device__ __attribute__((always_inline)) void epilogue(f32x16_t (&acc)[E::SM][E::SN], float* sbuf, int row0,
-                                                        int col0, Op& op) {
-    using L = EpiLayout<E>;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    auto rq = [&](int i, int it, int& gi, int& sc, int& sr) {   // the row pass's quads
-        const int q = tid + GEMM_THREADS * it;
-        sr = q / (E::BN / 4);
-        sc = (q % (E::BN / 4)) * 4;
-        gi = row0 + (sr >> 5) * E::WM + i * 32 + (sr & 31);
-    };
-    float4 pre[L::ROW_ITERS];
-    lds_barrier();   // the k-loop's last LDS reads are done
-#pragma unroll
-    for (int i = 0; i < E::SM; ++i) {
+// Symmetric output (A or B): tile (ti, tj), ti <= tj, stored at (ti, tj) from
+// the transposed layout and mirrored at (tj, ti) from the untransposed one.  A
+// diagonal tile stores its upper triangle directly and its strictly upper
+// triangle mirrored, so the stored matrix is exactly symmetric.
+//   Gram:        value = scale * acc
+//   polynomial:  value = b * A + c * acc   (A read at the mirrored position,
+//                                            equal to the direct one by symmetry)
+template <typename E, typename T, bool POLY>
+__device__ __attribute__((always_inline)) void sym_epilogue(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
+                                                            bool diag, void* dst, size_t ld, float scale,
+                                                            const void* amat, float b, float c) {
+    const Coords<E> q(row0, col0);
+    float4 cur[E::SN * 4], nxt[E::SN * 4];
+    auto fetch = [&](float4 (&buf)[E::SN * 4], int i) {
 #pragma unroll
         for (int j = 0; j < E::SN; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int sr = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int sc = wn * E::WN + j * 32 + (lane & 31);
-                sbuf[sr * L::LDW + sc] = acc[i][j][r];
-            }
-        // acc[i] is in LDS now; its registers take this pass's operands from
-        // memory, whose latency overlaps the barrier
-        if (Op::PREFETCH) {
+            for (int g = 0; g < 4; ++g)
+                buf[j * 4 + g] = ld_quad<T>(amat, static_cast<size_t>(q.raw_col + 32 * j) * ld + q.raw_row + 32 * i + 8 * g);
+    };
+    if (POLY) fetch(cur, 0);
 #pragma unroll
-            for (int it = 0; it < L::ROW_ITERS; ++it) {
-                int gi, sc, sr;
-                rq(i, it, gi, sc, sr);
-                pre[it] = op.fetch(gi, col0 + sc);
-            }
-        }
-        lds_barrier();
+    for (int i = 0; i < E::SM; ++i) {
+        if (POLY && i + 1 < E::SM) fetch(nxt, i + 1);
 #pragma unroll
-        for (int it = 0; it < L::ROW_ITERS; ++it) {
-            int gi, sc, sr;
-            rq(i, it, gi, sc, sr);
-            float4* cell = reinterpret_cast<float4*>(sbuf + sr * L::LDW + sc);
-            float4 v = *cell;
-            op.row(gi, col0 + sc, v, pre[it]);
-            *cell = v;
-        }
-        if (op.transposed) {
-            lds_barrier();
+        for (int j = 0; j < E::SN; ++j)
 #pragma unroll
-            for (int it = 0; it < L::COL_ITERS; ++it) {
-                const int q = tid + GEMM_THREADS * it;
-                const int kq = q & 7, rest = q >> 3;
-                const int sc = rest % E::BN, strip = rest / E::BN;
-                const int sr = strip * 32 + kq * 4;
-                const float4 v = make_float4(sbuf[sr * L::LDW + sc], sbuf[(sr + 1) * L::LDW + sc],
-                                             sbuf[(sr + 2) * L::LDW + sc], sbuf[(sr + 3) * L::LDW + sc]);
-                op.col(col0 + sc, row0 + strip * E::WM + i * 32 + kq * 4, v);
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float x = acc[i][j][4 * g + p];
+                    v[p] = POLY ? fmaf(c, x, b * f4get(cur[j * 4 + g], p)) : scale * x;
+                }
+                // mirrored: elements (rr + p, cc) go to row cc, columns rr .. rr + 3
+                const int rr = q.raw_row + 32 * i + 8 * g, cc = q.raw_col + 32 * j;
+                unsigned mm = 0xFu;
+                if (diag) {
+                    mm = 0;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) mm |= (rr + p < cc) ? (1u << p) : 0u;
+                }
+                st_quad_masked<T>(dst, static_cast<size_t>(cc) * ld + rr, make_float4(v[0], v[1], v[2], v[3]), mm);
+                // direct: row tr, columns tc .. tc + 3
+                quad_transpose(v);
+                const int tr = q.tr_row + 32 * i + 8 * g, tc = q.tr_col + 32 * j;
+                unsigned md = 0xFu;
+                if (diag) {
+                    md = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) md |= (tr <= tc + e) ? (1u << e) : 0u;
+                }
+                st_quad_masked<T>(dst, static_cast<size_t>(tr) * ld + tc, make_float4(v[0], v[1], v[2], v[3]), md);
             }
+        if (POLY) {
+#pragma unroll
+            for (int k = 0; k < E::SN * 4; ++k) cur[k] = nxt[k];
         }
-        lds_barrier();
     }
 }
 
-// Symmetric outputs (A, B): tile (ti, tj), ti <= tj, is stored at (ti, tj)
-// and mirrored at (tj, ti).  A diagonal tile writes its upper triangle's
-// values to both positions, so the stored matrix is exactly symmetric.
-template <typename T>
-struct SymStore {
-    void* dst;
-    size_t ld;
-    bool diag;
-    bool transposed = true;
-    __device__ inline void put_row(int gi, int gj, const float4& v) const {
-        const size_t idx = static_cast<size_t>(gi) * ld + gj;
-        if (!diag || gi <= gj) {
-            st_quad<T>(dst, idx, v);
-        } else {
+// X' = u (a X + acc): the fp32 iterate is read at xin and written at xout (the
+// same buffer for bf16, the other ping-pong buffer for fp32); for bf16 the
+// operand copy of X' is written to xnext (skipped after the last step).
+template <typename E, typename T>
+__device__ __attribute__((always_inline)) void update_epilogue(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
+                                                               const float* xin, float* xout, void* xnext,
+                                                               size_t np, float a, float u) {
+    const Coords<E> q(row0, col0);
+    float4 cur[E::SN * 4], nxt[E::SN * 4];
+    auto at = [&](int i, int j, int g) {
+        return static_cast<size_t>(q.tr_row + 32 * i + 8 * g) * np + q.tr_col + 32 * j;
+    };
+    auto fetch = [&](float4 (&buf)[E::SN * 4], int i) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (gi <= gj + e) st_elem<T>(dst, idx + e, f4get(v, e));
-        }
-    }
-    // v holds rows gi..gi+3 of column gj; stored as row gj of the mirror
-    __device__ inline void col(int gj, int gi, const float4& v) const {
-        const size_t idx = static_cast<size_t>(gj) * ld + gi;
-        if (!diag || gi + 3 < gj) {
-            st_quad<T>(dst, idx, v);
-        } else {
+        for (int j = 0; j < E::SN; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (gi + e < gj) st_elem<T>(dst, idx + e, f4get(v, e));
-        }
+            for (int g = 0; g < 4; ++g) buf[j * 4 + g] = ld_f4(xin + at(i, j, g));
+    };
+    fetch(cur, 0);
+#pragma unroll
+    for (int i = 0; i < E::SM; ++i) {
+        if (i + 1 < E::SM) fetch(nxt, i + 1);
+#pragma unroll
+        for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) v[p] = acc[i][j][4 * g + p];
+                quad_transpose(v);
+                const float4 x = cur[j * 4 + g];
+                const float4 o = make_float4(u * fmaf(a, x.x, v[0]), u * fmaf(a, x.y, v[1]),
+                                             u * fmaf(a, x.z, v[2]), u * fmaf(a, x.w, v[3]));
+                const size_t idx = at(i, j, g);
+                st_f4(xout + idx, o);
+                if (sizeof(T) == 2 && xnext) st_quad<T>(xnext, idx, o);
+            }
+#pragma unroll
+        for (int k = 0; k < E::SN * 4; ++k) cur[k] = nxt[k];
     }
-};
-
-template <typename T>
-struct GramOp : SymStore<T> {
-    static constexpr bool PREFETCH = false;
-    float scale;
-    __device__ inline float4 fetch(int, int) const { return make_float4(0.f, 0.f, 0.f, 0.f); }
-    __device__ inline void row(int gi, int gj, float4& v, const float4&) const {
-        v.x *= scale; v.y *= scale; v.z *= scale; v.w *= scale;
-        this->put_row(gi, gj, v);
-    }
-};
-
-template <typename T>
-struct PolyOp : SymStore<T> {
-    static constexpr bool PREFETCH = true;
-    const void* a;
-    float b, c;
-    __device__ inline float4 fetch(int gi, int gj) const { return ld_quad<T>(a, static_cast<size_t>(gi) * this->ld + gj); }
-    __device__ inline void row(int gi, int gj, float4& v, const float4& av) const {
-        v.x = fmaf(c, v.x, b * av.x); v.y = fmaf(c, v.y, b * av.y);
-        v.z = fmaf(c, v.z, b * av.z); v.w = fmaf(c, v.w, b * av.w);
-        this->put_row(gi, gj, v);
-    }
-};
-
-// X' = u (a X + B X): the epilogue adds a X (fp32 iterate, requested while
-// the pass is staged), scales by u and writes the fp32 iterate in place, its
-// bf16 operand copy and the transposed operand copy for the next step (both
-// skipped after the last step).
-template <typename T>
-struct UpdateOp {
-    static constexpr bool PREFETCH = true;
-    float* x32;
-    void* xop;
-    void* xnT;
-    size_t np, mp;
-    float a, u;
-    bool transposed;
-    __device__ inline float4 fetch(int gi, int gj) const { return ld_f4(x32 + static_cast<size_t>(gi) * np + gj); }
-    __device__ inline void row(int gi, int gj, float4& v, const float4& x) const {
-        const size_t idx = static_cast<size_t>(gi) * np + gj;
-        v.x = u * fmaf(a, x.x, v.x); v.y = u * fmaf(a, x.y, v.y);
-        v.z = u * fmaf(a, x.z, v.z); v.w = u * fmaf(a, x.w, v.w);
-        st_f4(x32 + idx, v);
-        if (sizeof(T) == 2 && transposed) st_quad<T>(xop, idx, v);
-    }
-    __device__ inline void col(int gj, int gi, const float4& v) const {
-        st_quad<T>(xnT, static_cast<size_t>(gj) * mp + gi, v);
-    }
-};
+}
 
 template <typename T, int PHASE>
 __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, int t, u32x4* lds) {
-    using E = Engine<T>;
+    using E = Engine<T, PHASE == PH_UPDATE>;
     const int mi = find_matrix(args.prefix, args.nmat, t);
     const MatDesc& d = args.descs[mi];
     const int local = t - args.prefix[mi];
     const int mp = d.mp, np = d.np;
+    const int ping = args.ping;
 
     int ti, tj;
     if (PHASE == PH_UPDATE) {
@@ -379,47 +445,38 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         sym_decode(local, mp / E::BM, ti, tj);
     }
     const int row0 = ti * E::BM, col0 = tj * E::BN;
-    float* sbuf = reinterpret_cast<float*>(lds);
 
     f32x16_t acc[E::SM][E::SN];
     if (PHASE == PH_GRAM) {
-        const char* X = static_cast<const char*>(d.xop);
+        const char* X = static_cast<const char*>(d.xop[ping]);
         const size_t ld = static_cast<size_t>(np) * sizeof(T);
         E::run(X + row0 * ld, ld, X + col0 * ld, ld, np * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc);
-        GramOp<T> op;
-        op.dst = d.amat; op.ld = mp; op.diag = ti == tj;
         // first step: X0 = s * M' is folded in as A0 = s^2 M' M'^T
-        op.scale = args.first ? G(d.scal)[0] * G(d.scal)[0] : 1.0f;
-        epilogue<E>(acc, sbuf, row0, col0, op);
+        const float scale = args.first ? G(d.scal)[0] * G(d.scal)[0] : 1.0f;
+        sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.amat, mp, scale, nullptr, 0.0f, 0.0f);
     } else if (PHASE == PH_POLY) {
         const char* A = static_cast<const char*>(d.amat);
         const size_t ld = static_cast<size_t>(mp) * sizeof(T);
         E::run(A + row0 * ld, ld, A + col0 * ld, ld, mp * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc);
-        PolyOp<T> op;
-        op.dst = d.bmat; op.ld = mp; op.diag = ti == tj;
-        op.a = d.amat; op.b = args.b; op.c = args.c;
-        epilogue<E>(acc, sbuf, row0, col0, op);
+        sym_epilogue<E, T, true>(acc, row0, col0, ti == tj, d.bmat, mp, 1.0f, d.amat, args.b, args.c);
     } else {
         const char* B = static_cast<const char*>(d.bmat);
-        const char* XT = static_cast<const char*>(d.xopT[args.ping]);
-        const size_t ld = static_cast<size_t>(mp) * sizeof(T);
-        E::run(B + row0 * ld, ld, XT + col0 * ld, ld, mp * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc);
-        UpdateOp<T> op;
-        op.x32 = d.x32; op.xop = d.xop; op.xnT = d.xopT[args.ping ^ 1];
-        op.np = np; op.mp = mp; op.a = args.a;
-        // first step: X1 = s (a M' + B0 M') with M' unscaled in x32 / xop
-        op.u = args.first ? G(d.scal)[0] : 1.0f;
-        op.transposed = !args.last;
-        epilogue<E>(acc, sbuf, row0, col0, op);
+        const char* X = static_cast<const char*>(d.xop[ping]);
+        const size_t ldb = static_cast<size_t>(mp) * sizeof(T), ldx = static_cast<size_t>(np) * sizeof(T);
+        E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, mp / E::KS, lds, acc);
+        // first step: X1 = s (a M' + B0 M') with M' unscaled in the iterate and operand copy
+        const float u = args.first ? G(d.scal)[0] : 1.0f;
+        void* xnext = (sizeof(T) == 2 && !args.last) ? d.xop[ping ^ 1] : nullptr;
+        update_epilogue<E, T>(acc, row0, col0, d.x32[ping], d.x32[ping ^ 1], xnext, np, args.a, u);
     }
 }
 
 template <typename T, int PHASE>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void ns_gemm_kernel(NsArgs args) {
-    using E = Engine<T>;
-    static_assert(EpiLayout<E>::FLOATS * 4 <= 2 * E::STAGE * 16, "epilogue staging exceeds LDS");
+    using E = Engine<T, PHASE == PH_UPDATE>;
     __shared__ u32x4 lds[2 * E::STAGE];
-    if (static_cast<int>(blockIdx.x) < args.total) process_tile<T, PHASE>(args, blockIdx.x, lds);
+    const int t = xcd_run_remap(blockIdx.x, gridDim.x);
+    if (t < args.total) process_tile<T, PHASE>(args, t, lds);
 }
 
 template <int PHASE>

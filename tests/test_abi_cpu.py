@@ -60,8 +60,12 @@ def test_workspace_bytes_is_host_only_and_grows_with_work():
     b1 = lib.muon_workspace_bytes(one, 1, ctypes.byref(hp))
     b2 = lib.muon_workspace_bytes(two, 2, ctypes.byref(hp))
     assert b1 > 0 and b2 > b1
-    # fp32 iterate + bf16 copy + two bf16 transposed copies + A and B, at least
-    assert b1 >= 2048 * 2048 * (4 + 2 + 2 + 2) + 2 * 2048 * 2048 * 2
+    # fp32 iterate + two bf16 operand copies + A and B (bf16), at least
+    assert b1 >= 2048 * 2048 * (4 + 2 + 2) + 2 * 2048 * 2048 * 2
+    # fp32: two fp32 iterates + A and B (fp32)
+    hp32, keep32 = _hp(dtype=mao.MUON_F32)
+    b32 = lib.muon_workspace_bytes(one, 1, ctypes.byref(hp32))
+    assert b32 >= 2048 * 2048 * (4 + 4) + 2 * 2048 * 2048 * 4
     # a skipped matrix (grad NULL) costs nothing
     skip = _mats([(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 2048, 2048),
                   (FAKE + (3 << 30), None, FAKE + (5 << 30), 8192, 2048)])

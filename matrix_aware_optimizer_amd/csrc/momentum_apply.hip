@@ -64,9 +64,9 @@ __device__ inline void ew_tile_origin(const MatDesc& d, int local, int& i0, int&
 // ----------------------------------------------------------------------------
 // Momentum + norm partials + operand copies.
 //   user-frame load (coalesced) -> fp32 M' (state store) -> U into LDS in the
-//   NS frame -> rows of the fp32 iterate and its bf16 operand copy
-//   (coalesced), with the sum of squares taken in NS-frame order so the
-//   result does not depend on the caller's orientation.
+//   NS frame -> rows of the iterate (fp32, or the bf16 pair hi + lo whose hi
+//   is the MFMA operand), coalesced, with the sum of squares taken in NS-frame
+//   order so the result does not depend on the caller's orientation.
 // ----------------------------------------------------------------------------
 template <typename T, bool NS_ONLY>
 __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) {
@@ -123,8 +123,16 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
                 sq = fmaf(v0, v0, sq); sq = fmaf(v1, v1, sq);
                 sq = fmaf(v2, v2, sq); sq = fmaf(v3, v3, sq);
                 const size_t idx = static_cast<size_t>(i0 + il) * d.np + (j0 + jl);
-                st_f4(d.x32[0] + idx, make_float4(v0, v1, v2, v3));
-                if (sizeof(T) == 2) store4<T>(d.xop[0], idx, v0, v1, v2, v3);
+                if (sizeof(T) == 2) {
+                    // the iterate as the pair hi + lo: hi = bf16(U), lo = bf16(U - hi)
+                    const uint32_t h01 = pack_bf16x2(v0, v1), h23 = pack_bf16x2(v2, v3);
+                    const float r0 = v0 - __uint_as_float(h01 << 16), r1 = v1 - __uint_as_float(h01 & 0xffff0000u);
+                    const float r2 = v2 - __uint_as_float(h23 << 16), r3 = v3 - __uint_as_float(h23 & 0xffff0000u);
+                    st_u2(static_cast<uint16_t*>(d.xop[0]) + idx, u32x2_t{h01, h23});
+                    store4<T>(d.xlo, idx, r0, r1, r2, r3);
+                } else {
+                    st_f4(d.x32[0] + idx, make_float4(v0, v1, v2, v3));
+                }
             }
         }
         const float total = block_sum_256(sq, red);   // also orders LDS reuse
@@ -178,7 +186,18 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(EwArgs args) {
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int il = (tid >> 4) + 16 * p;
-                const float4 v = ld_f4(d.x32[args.fin] + static_cast<size_t>(i0 + il) * d.np + (j0 + jl));
+                const size_t idx = static_cast<size_t>(i0 + il) * d.np + (j0 + jl);
+                float4 v;
+                if (sizeof(T) == 2) {   // X = hi + lo (exact in fp32)
+                    const u32x2_t h = ld_u2(static_cast<const uint16_t*>(d.xop[args.fin]) + idx);
+                    const u32x2_t l = ld_u2(d.xlo + idx);
+                    v = make_float4(__uint_as_float(h.x << 16) + __uint_as_float(l.x << 16),
+                                    __uint_as_float(h.x & 0xffff0000u) + __uint_as_float(l.x & 0xffff0000u),
+                                    __uint_as_float(h.y << 16) + __uint_as_float(l.y << 16),
+                                    __uint_as_float(h.y & 0xffff0000u) + __uint_as_float(l.y & 0xffff0000u));
+                } else {
+                    v = ld_f4(d.x32[args.fin] + idx);
+                }
                 tile[il][jl] = v.x; tile[il][jl + 1] = v.y; tile[il][jl + 2] = v.z; tile[il][jl + 3] = v.w;
             }
         }

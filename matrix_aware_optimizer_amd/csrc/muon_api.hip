@@ -213,21 +213,23 @@ muon_status build_plan(std::vector<Item>& items, const muon_hparams* hp, bool ns
     for (int k = 0; k < nmat; ++k) {
         MatDesc& d = pl.descs[k];
         const size_t mn = static_cast<size_t>(d.mp) * d.np, mm = static_cast<size_t>(d.mp) * d.mp;
-        // bf16: one fp32 iterate (updated in place) and two bf16 operand copies;
+        // bf16: the iterate as hi (two ping-pong operand copies) + lo (in place);
         // fp32: two iterates that are their own operands
-        d.x32[0] = reinterpret_cast<float*>(off);
-        off = align_up(off + mn * 4, ALIGN);
         if (dtype == MUON_BF16) {
-            d.x32[1] = d.x32[0];
+            d.x32[0] = d.x32[1] = nullptr;
             for (int p = 0; p < 2; ++p) {
                 d.xop[p] = reinterpret_cast<void*>(off);
-                off = align_up(off + mn * es, ALIGN);
+                off = align_up(off + mn * 2, ALIGN);
             }
+            d.xlo = reinterpret_cast<uint16_t*>(off);
+            off = align_up(off + mn * 2, ALIGN);
         } else {
-            d.x32[1] = reinterpret_cast<float*>(off);
-            off = align_up(off + mn * 4, ALIGN);
-            d.xop[0] = d.x32[0];
-            d.xop[1] = d.x32[1];
+            for (int p = 0; p < 2; ++p) {
+                d.x32[p] = reinterpret_cast<float*>(off);
+                off = align_up(off + mn * 4, ALIGN);
+                d.xop[p] = d.x32[p];
+            }
+            d.xlo = nullptr;
         }
         d.amat = reinterpret_cast<void*>(off);
         off = align_up(off + mm * es, ALIGN);
@@ -244,10 +246,16 @@ void rebase(Plan& pl, char* base) {
         p = reinterpret_cast<P>(base + reinterpret_cast<uintptr_t>(p));
     };
     for (MatDesc& d : pl.descs) {
-        fix(d.x32[0]);
-        fix(d.x32[1]);
-        fix(d.xop[0]);
-        fix(d.xop[1]);
+        if (d.xlo) {   // bf16
+            fix(d.xop[0]);
+            fix(d.xop[1]);
+            fix(d.xlo);
+        } else {
+            fix(d.x32[0]);
+            fix(d.x32[1]);
+            d.xop[0] = d.x32[0];
+            d.xop[1] = d.x32[1];
+        }
         fix(d.amat);
         fix(d.bmat);
         fix(d.scal);

@@ -35,11 +35,15 @@ struct MatDesc {
     int32_t mp, np;     // NS frame padded to the GEMM tile
     int32_t tall;       // 1 if rows > cols
     int32_t pad0;
-    // workspace buffers (NS frame, zero-padded).  Step k reads index k & 1 and
-    // writes index (k & 1) ^ 1.
-    float* x32[2];      // mp x np fp32 iterate: one buffer updated in place (bf16, both
-                        // entries equal) or a ping-pong pair (fp32, read as the operand)
-    void* xop[2];       // mp x np bf16 operand copies, ping-pong; equal to x32 for fp32
+    // workspace buffers (NS frame, mp x np, zero-padded).  Step k reads index
+    // k & 1 and writes index (k & 1) ^ 1.
+    //   fp32: the iterate is x32[k & 1], which is also the MFMA operand.
+    //   bf16: the iterate is the pair hi + lo with hi = bf16(X) = xop[k & 1]
+    //         (the MFMA operand) and lo = bf16(X - hi) = xlo (about 16
+    //         significant bits in all); x32 is unused.
+    float* x32[2];
+    void* xop[2];       // operand copies, ping-pong; equal to x32 for fp32
+    uint16_t* xlo;      // bf16 only, updated in place
     void* amat;         // mp x mp, A = X X^T (symmetric, stored in full)
     void* bmat;         // mp x mp, B = b A + c A A (symmetric, stored in full)
     float* scal;        // [0] = 1 / (||U||_F + eps), [1] = ||U||_F
@@ -60,7 +64,7 @@ struct EwArgs {
     float beta;
     int32_t nesterov;
     int32_t ns_zero;         // 1 when ns_steps == 0 (output is the normalized input)
-    int32_t fin;             // x32[fin] holds the last step's iterate (ns_steps & 1)
+    int32_t fin;             // index of the last step's iterate (ns_steps & 1)
 };
 
 struct NsArgs {

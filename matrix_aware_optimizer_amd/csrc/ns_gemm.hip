@@ -141,11 +141,15 @@ struct Engine {
     static_assert(!QK || BN * static_cast<int>(sizeof(T)) == QROW_CHUNKS * 16, "k-major rows are one tile wide");
     static_assert(!QK || KS * QROW_CHUNKS == BN * CHUNKS_PER_ROW, "k-major region fills the Q part of a stage");
 
-    // acc[i][j] = sum_k P[row0 + i][k] * Q(k, col0 + j) over the whole k range, where
-    // P points at row row0 (pitch ldp bytes) and Q at row col0 (k-contiguous) or at
-    // column col0 of k-row 0 (k-major), pitch ldq bytes.
+    // acc[i][j] = init[i][j] + sum_k P[row0 + i][k] * Q(k, col0 + j) over the whole k
+    // range, where P points at row row0 (pitch ldp bytes) and Q at row col0
+    // (k-contiguous) or at column col0 of k-row 0 (k-major), pitch ldq bytes.
+    // init(acc) fills the accumulators once the first stage's loads are in flight;
+    // hook(kt, Q region of the stage, acc) runs when stage kt is ready.
+    template <typename Init, typename Hook>
     static __device__ __attribute__((always_inline)) void run(const char* __restrict__ P, size_t ldp, const char* __restrict__ Q,
-                                      size_t ldq, int ksteps, u32x4* lds, f32x16_t (&acc)[SM][SN]) {
+                                      size_t ldq, int ksteps, u32x4* lds, f32x16_t (&acc)[SM][SN], Init init,
+                                      Hook hook) {
         const int tid = threadIdx.x;
         const int lane = tid & 63, wave = tid >> 6;
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -178,14 +182,8 @@ struct Engine {
             __builtin_amdgcn_global_load_lds((const void*)(src[j] + static_cast<size_t>(kt) * step), d, 16, 0, 0);
         };
 #pragma unroll
-        for (int i = 0; i < SM; ++i)
-#pragma unroll
-            for (int j = 0; j < SN; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-#pragma unroll
         for (int j = 0; j < LOADS; ++j) issue(0, j);
+        init(acc);
 
         const int half = lane >> 5;
         const int arow = wm * WM + (lane & 31), brow = BM + wn * WN + (lane & 31);
@@ -196,6 +194,7 @@ struct Engine {
             asm volatile("s_barrier" ::: "memory");
             const u32x4* L = lds + (kt & 1) * STAGE;
             const lds_byte_t* Lq = (const lds_byte_t*)(L + P_CHUNKS);
+            hook(kt, Lq, acc);
             // B operand of k-slice s (16 bf16 or 8 fp32 of k) for 32-column block j
             auto read_b = [&](int j, int s) -> u32x4 {
                 if (!QK) return L[swz(brow + j * 32, 2 * s + half)];
@@ -286,6 +285,21 @@ template <typename T> __device__ inline void st_quad_masked(void* p, size_t i, c
 }
 
 enum Phase { PH_GRAM = 0, PH_POLY = 1, PH_UPDATE = 2 };
+
+struct NoHook {
+    template <typename A> __device__ __forceinline__ void operator()(int, const lds_byte_t*, A&) const {}
+};
+
+struct ZeroInit {
+    template <typename A> __device__ __forceinline__ void operator()(A& acc) const {
+#pragma unroll
+        for (auto& row : acc)
+#pragma unroll
+            for (auto& blk : row)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) blk[r] = 0.0f;
+    }
+};
 
 // ----------------------------------------------------------------------------
 // Epilogue helpers.  Accumulator register r of 32 x 32 block (i, j) holds, in
@@ -387,28 +401,90 @@ __device__ __attribute__((always_inline)) void sym_epilogue(f32x16_t (&acc)[E::S
     }
 }
 
-// X' = u (a X + acc): the fp32 iterate is read at xin and written at xout (the
-// same buffer for bf16, the other ping-pong buffer for fp32); for bf16 the
-// operand copy of X' is written to xnext (skipped after the last step).
+// X' = u (a X + B X).  a X enters the accumulators before or during the
+// k-loop, so the epilogue only scales and stores.
+//   fp32: the iterate is x32[ping] (also the operand); a X is read into the
+//         accumulators while the first operand stage loads (UpdateInit), and
+//         X' goes to x32[ping ^ 1].
+//   bf16: the iterate is the pair hi + lo (hi = xop[ping], the operand copy,
+//         lo = xlo).  a lo is read into the accumulators at the start; a hi is
+//         added from LDS during the k-steps that stage the tile's own rows of
+//         X as operand k-rows (HiAddend).  X' is stored as hi' = bf16(X') to
+//         xop[ping ^ 1] and lo' = bf16(X' - hi') to xlo, in place.
+template <typename E, typename T>
+struct UpdateInit {
+    const void* src;    // x32[ping] (fp32) or xlo (bf16)
+    size_t np;
+    int row0, col0;
+    float a;
+    template <typename A> __device__ __forceinline__ void operator()(A& acc) const {
+        const Coords<E> q(row0, col0);
+#pragma unroll
+        for (int i = 0; i < E::SM; ++i)
+#pragma unroll
+            for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 x = ld_quad<T>(src, static_cast<size_t>(q.tr_row + 32 * i + 8 * g) * np + q.tr_col + 32 * j);
+                    float v[4] = {a * x.x, a * x.y, a * x.z, a * x.w};
+                    quad_transpose(v);   // row layout -> accumulator layout (an involution)
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) acc[i][j][4 * g + p] = v[p];
+                }
+    }
+};
+
+template <typename E>
+struct HiAddend {
+    int kt0;    // k-step whose k-rows are the tile's first output rows (row0 / KS)
+    float a;
+    // Stage kt holds X k-rows [kt KS, kt KS + KS) of the tile's columns; when they are
+    // output rows of this tile, the waves owning them add a * hi for those rows.  A
+    // transpose read per (i, j, g) delivers the accumulator layout directly: lane
+    // group g16 addresses rows 8 g + 4 (g16 >> 1) + (0..3) and 16 columns.
+    template <typename A> __device__ __forceinline__ void operator()(int kt, const lds_byte_t* Lq, A& acc) const {
+        const int rel = kt - kt0;
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+        if (rel < 0 || rel >= E::BM / E::KS || (rel * E::KS) / E::WM != wm) return;
+        const int ifirst = (rel * E::KS - wm * E::WM) / 32;
+        // k-row of this lane's first element: 32 (i - ifirst) + 8 g + kl; the swizzle only
+        // depends on kl & 3, so each column block needs one per-lane base offset
+        const int i16 = lane & 15, g16 = lane >> 4;
+        const int kl = 4 * (g16 >> 1) + (i16 >> 2);
+        int base[E::SN];
+#pragma unroll
+        for (int j = 0; j < E::SN; ++j) {
+            const int col = wn * E::WN + 32 * j + 16 * (g16 & 1) + 4 * (i16 & 3);
+            base[j] = qswz(kl, col >> 3) * 16 + (col & 7) * 2;
+        }
+        // one 32-row block at a time keeps the reads' registers few
+#pragma unroll
+        for (int i = 0; i < E::SM; ++i) {
+            if (i >= ifirst && i < ifirst + E::KS / 32) {
+                const int rowoff = 32 * (i - ifirst) * QROW_CHUNKS * 16;
+#pragma unroll
+                for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const i16x4_t h = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_i16x4_t*)(Lq + base[j] + rowoff + 8 * g * QROW_CHUNKS * 16));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[i][j][4 * g + e] = fmaf(a, bf16_to_f32(static_cast<uint16_t>(h[e])), acc[i][j][4 * g + e]);
+                    }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+};
+
 template <typename E, typename T>
 __device__ __attribute__((always_inline)) void update_epilogue(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
-                                                               const float* xin, float* xout, void* xnext,
-                                                               size_t np, float a, float u) {
+                                                               void* hi_out, uint16_t* lo_out, size_t np, float u) {
     const Coords<E> q(row0, col0);
-    float4 cur[E::SN * 4], nxt[E::SN * 4];
-    auto at = [&](int i, int j, int g) {
-        return static_cast<size_t>(q.tr_row + 32 * i + 8 * g) * np + q.tr_col + 32 * j;
-    };
-    auto fetch = [&](float4 (&buf)[E::SN * 4], int i) {
 #pragma unroll
-        for (int j = 0; j < E::SN; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) buf[j * 4 + g] = ld_f4(xin + at(i, j, g));
-    };
-    fetch(cur, 0);
-#pragma unroll
-    for (int i = 0; i < E::SM; ++i) {
-        if (i + 1 < E::SM) fetch(nxt, i + 1);
+    for (int i = 0; i < E::SM; ++i)
 #pragma unroll
         for (int j = 0; j < E::SN; ++j)
 #pragma unroll
@@ -417,16 +493,19 @@ __device__ __attribute__((always_inline)) void update_epilogue(f32x16_t (&acc)[E
 #pragma unroll
                 for (int p = 0; p < 4; ++p) v[p] = acc[i][j][4 * g + p];
                 quad_transpose(v);
-                const float4 x = cur[j * 4 + g];
-                const float4 o = make_float4(u * fmaf(a, x.x, v[0]), u * fmaf(a, x.y, v[1]),
-                                             u * fmaf(a, x.z, v[2]), u * fmaf(a, x.w, v[3]));
-                const size_t idx = at(i, j, g);
-                st_f4(xout + idx, o);
-                if (sizeof(T) == 2 && xnext) st_quad<T>(xnext, idx, o);
+                const float4 o = make_float4(u * v[0], u * v[1], u * v[2], u * v[3]);
+                const size_t idx = static_cast<size_t>(q.tr_row + 32 * i + 8 * g) * np + q.tr_col + 32 * j;
+                if (sizeof(T) == 4) {
+                    st_f4(static_cast<float*>(hi_out) + idx, o);
+                } else {
+                    const u32x2_t h = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+                    const float4 hf = make_float4(__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u),
+                                                  __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xffff0000u));
+                    const u32x2_t l = {pack_bf16x2(o.x - hf.x, o.y - hf.y), pack_bf16x2(o.z - hf.z, o.w - hf.w)};
+                    st_u2(static_cast<uint16_t*>(hi_out) + idx, h);
+                    st_u2(lo_out + idx, l);
+                }
             }
-#pragma unroll
-        for (int k = 0; k < E::SN * 4; ++k) cur[k] = nxt[k];
-    }
 }
 
 template <typename T, int PHASE>
@@ -450,24 +529,29 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
     if (PHASE == PH_GRAM) {
         const char* X = static_cast<const char*>(d.xop[ping]);
         const size_t ld = static_cast<size_t>(np) * sizeof(T);
-        E::run(X + row0 * ld, ld, X + col0 * ld, ld, np * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc);
+        E::run(X + row0 * ld, ld, X + col0 * ld, ld, np * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc, ZeroInit{}, NoHook{});
         // first step: X0 = s * M' is folded in as A0 = s^2 M' M'^T
         const float scale = args.first ? G(d.scal)[0] * G(d.scal)[0] : 1.0f;
         sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.amat, mp, scale, nullptr, 0.0f, 0.0f);
     } else if (PHASE == PH_POLY) {
         const char* A = static_cast<const char*>(d.amat);
         const size_t ld = static_cast<size_t>(mp) * sizeof(T);
-        E::run(A + row0 * ld, ld, A + col0 * ld, ld, mp * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc);
+        E::run(A + row0 * ld, ld, A + col0 * ld, ld, mp * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc, ZeroInit{}, NoHook{});
         sym_epilogue<E, T, true>(acc, row0, col0, ti == tj, d.bmat, mp, 1.0f, d.amat, args.b, args.c);
     } else {
         const char* B = static_cast<const char*>(d.bmat);
         const char* X = static_cast<const char*>(d.xop[ping]);
         const size_t ldb = static_cast<size_t>(mp) * sizeof(T), ldx = static_cast<size_t>(np) * sizeof(T);
-        E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, mp / E::KS, lds, acc);
+        const UpdateInit<E, T> init{sizeof(T) == 2 ? static_cast<const void*>(d.xlo) : static_cast<const void*>(d.x32[ping]),
+                                    static_cast<size_t>(np), row0, col0, args.a};
+        if (sizeof(T) == 2)
+            E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, mp / E::KS, lds, acc, init,
+                   HiAddend<E>{row0 / E::KS, args.a});
+        else
+            E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, mp / E::KS, lds, acc, init, NoHook{});
         // first step: X1 = s (a M' + B0 M') with M' unscaled in the iterate and operand copy
         const float u = args.first ? G(d.scal)[0] : 1.0f;
-        void* xnext = (sizeof(T) == 2 && !args.last) ? d.xop[ping ^ 1] : nullptr;
-        update_epilogue<E, T>(acc, row0, col0, d.x32[ping], d.x32[ping ^ 1], xnext, np, args.a, u);
+        update_epilogue<E, T>(acc, row0, col0, d.xop[ping ^ 1], d.xlo, np, u);
     }
 }
 

@@ -41,21 +41,27 @@ def mm_bf16(P, Q):
     return bf16(P) @ bf16(Q)
 
 
-def emulated_ns(U, schedule, eps=1e-7, store_bf16=False):
-    """Normalize and iterate with bf16 operands; X kept in fp32 unless store_bf16."""
+def bf16_pair(x):
+    """x stored as hi + lo, hi = bf16(x), lo = bf16(x - hi) (about 16 significant bits)."""
+    x = np.asarray(x, np.float32)
+    hi = bf16(x)
+    return (hi + bf16(x - hi)).astype(np.float32)
+
+
+def emulated_ns(U, schedule, eps=1e-7, store_bf16=False, store_pair=False):
+    """Normalize and iterate with bf16 operands; X kept in fp32 unless store_bf16 (X rounded
+    to bf16 between steps) or store_pair (X rounded to a bf16 hi + lo pair between steps)."""
     U = np.asarray(U, np.float32)
     tr = U.shape[0] > U.shape[1]
     if tr:
         U = U.T
     X = (U / (np.sqrt(np.sum(U.astype(np.float64) ** 2)) + eps)).astype(np.float32)
-    if store_bf16:
-        X = bf16(X)
+    store = bf16 if store_bf16 else (bf16_pair if store_pair else (lambda v: v))
+    X = store(X)
     for (a, b, c) in schedule:
         A = mm_bf16(X, X.T)
         B = (b * A + c * mm_bf16(A, A.T)).astype(np.float32)
-        X = (a * X + mm_bf16(B, X)).astype(np.float32)
-        if store_bf16:
-            X = bf16(X)
+        X = store((a * X + mm_bf16(B, X)).astype(np.float32))
     return X.T if tr else X
 
 
@@ -64,8 +70,9 @@ def compare(G, schedule):
     ref = orc.muon_ns(G.astype(np.float64), schedule)
     s_ref = np.linalg.svd(ref, compute_uv=False)
     out = {}
-    for name, store in (("bf16_storage", True), ("fp32_iterate", False)):
-        got = emulated_ns(G, schedule, store_bf16=store).astype(np.float64)
+    for name, kw in (("bf16_storage", dict(store_bf16=True)), ("fp32_iterate", {}),
+                     ("bf16_pair", dict(store_pair=True))):
+        got = emulated_ns(G, schedule, **kw).astype(np.float64)
         err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
         s = np.linalg.svd(got, compute_uv=False)
         band = max(0.0, s_ref.min() - s.min(), s.max() - s_ref.max())
@@ -98,13 +105,15 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--seeds", type=int, default=2)
     args = ap.parse_args()
-    print(f"{'case':52s} {'seed':>4s}  {'bf16 storage err / band':>24s}  {'fp32 iterate err / band':>24s}")
+    print(f"{'case':52s} {'seed':>4s}  {'bf16 storage err / band':>24s}  {'fp32 iterate err / band':>24s}"
+          f"  {'bf16 pair err / band':>24s}")
     for case in CASES:
         for seed in range(args.seeds):
             G, sched = make(case, seed)
             r = compare(G, sched)
-            b, f = r["bf16_storage"], r["fp32_iterate"]
-            print(f"{case:52s} {seed:4d}  {b[0]:12.3e} / {b[1]:9.3e}  {f[0]:12.3e} / {f[1]:9.3e}", flush=True)
+            b, f, h = r["bf16_storage"], r["fp32_iterate"], r["bf16_pair"]
+            print(f"{case:52s} {seed:4d}  {b[0]:12.3e} / {b[1]:9.3e}  {f[0]:12.3e} / {f[1]:9.3e}"
+                  f"  {h[0]:12.3e} / {h[1]:9.3e}", flush=True)
 
 
 if __name__ == "__main__":

@@ -60,8 +60,8 @@ def test_workspace_bytes_is_host_only_and_grows_with_work():
     b1 = lib.muon_workspace_bytes(one, 1, ctypes.byref(hp))
     b2 = lib.muon_workspace_bytes(two, 2, ctypes.byref(hp))
     assert b1 > 0 and b2 > b1
-    # fp32 iterate + two bf16 operand copies + A and B (bf16), at least
-    assert b1 >= 2048 * 2048 * (4 + 2 + 2) + 2 * 2048 * 2048 * 2
+    # the iterate as a bf16 pair (two ping-pong hi copies + lo) + A and B (bf16), at least
+    assert b1 >= 2048 * 2048 * (2 + 2 + 2) + 2 * 2048 * 2048 * 2
     # fp32: two fp32 iterates + A and B (fp32)
     hp32, keep32 = _hp(dtype=mao.MUON_F32)
     b32 = lib.muon_workspace_bytes(one, 1, ctypes.byref(hp32))

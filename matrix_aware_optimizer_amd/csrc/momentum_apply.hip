@@ -42,6 +42,18 @@ template <> __device__ inline void store4<uint16_t>(void* base, size_t idx, floa
     st_u2(static_cast<uint16_t*>(base) + idx, p);
 }
 
+// 4 consecutive elements of the caller's dtype as fp32 (8-byte or 16-byte load).
+template <typename T> __device__ inline float4 load4(const void* base, size_t idx);
+template <> __device__ inline float4 load4<float>(const void* base, size_t idx) {
+    return ld_f4(static_cast<const float*>(base) + idx);
+}
+template <> __device__ inline float4 load4<uint16_t>(const void* base, size_t idx) {
+    const u32x2_t q = ld_u2(static_cast<const uint16_t*>(base) + idx);
+    return make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xffff0000u),
+                       __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xffff0000u));
+}
+__device__ inline float f4at(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+
 // Deterministic block sum (fixed shuffle pattern, fixed wave order).
 __device__ inline float block_sum_256(float v, float* red) {
 #pragma unroll
@@ -88,26 +100,49 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
         const int uc0 = d.tall ? i0 : j0;
         const int rows = d.rows, cols = d.cols;
 
-        // ---- load phase: a wave reads one 64-element user row per pass
-#pragma unroll 4
-        for (int p = 0; p < EW_TILE * EW_TILE / EW_THREADS; ++p) {
+        // ---- load phase: 4 consecutive user columns per thread, 16 threads per 64-element row
+#pragma unroll
+        for (int p = 0; p < EW_TILE * EW_TILE / (4 * EW_THREADS); ++p) {
             const int q = tid + EW_THREADS * p;
-            const int lr = q >> 6, lc = q & 63;
+            const int lr = q >> 4, lc = (q & 15) * 4;
             const int ur = ur0 + lr, uc = uc0 + lc;
-            float u = 0.0f;
+            float u[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if (ur < rows && uc < cols) {
                 const size_t idx = static_cast<size_t>(ur) * cols + uc;
-                const float g = Elem<T>::load(d.g, idx);
-                if (NS_ONLY) {
-                    u = g;
+                if (d.uvec) {   // uc + 3 < cols: cols and uc are multiples of 4
+                    const float4 g = load4<T>(d.g, idx);
+                    if (NS_ONLY) {
+                        u[0] = g.x; u[1] = g.y; u[2] = g.z; u[3] = g.w;
+                    } else {
+                        const float4 m = load4<T>(d.mom, idx);
+                        float mn[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            mn[e] = fmaf(beta, f4at(m, e), f4at(g, e));
+                            u[e] = args.nesterov ? fmaf(beta, mn[e], f4at(g, e)) : mn[e];
+                        }
+                        store4<T>(d.mom, idx, mn[0], mn[1], mn[2], mn[3]);
+                    }
                 } else {
-                    const float m = Elem<T>::load(d.mom, idx);
-                    const float mn = fmaf(beta, m, g);
-                    Elem<T>::store(d.mom, idx, mn);
-                    u = args.nesterov ? fmaf(beta, mn, g) : mn;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (uc + e >= cols) break;
+                        const float g = Elem<T>::load(d.g, idx + e);
+                        if (NS_ONLY) {
+                            u[e] = g;
+                        } else {
+                            const float m = Elem<T>::load(d.mom, idx + e);
+                            const float mn = fmaf(beta, m, g);
+                            Elem<T>::store(d.mom, idx + e, mn);
+                            u[e] = args.nesterov ? fmaf(beta, mn, g) : mn;
+                        }
+                    }
                 }
             }
-            if (d.tall) tile[lc][lr] = u; else tile[lr][lc] = u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (d.tall) tile[lc + e][lr] = u[e]; else tile[lr][lc + e] = u[e];
+            }
         }
         __syncthreads();
 
@@ -208,6 +243,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(EwArgs args) {
         const int uc0 = d.tall ? i0 : j0;
         const float coef = d.apply_coef * oscale;
         const float decay = d.decay;
+        // one element per thread and pass: a wave writes one 64-element user row
 #pragma unroll 4
         for (int p = 0; p < EW_TILE * EW_TILE / EW_THREADS; ++p) {
             const int q = tid + EW_THREADS * p;

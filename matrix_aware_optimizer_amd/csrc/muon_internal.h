@@ -34,7 +34,7 @@ struct MatDesc {
     int32_t m, n;       // NS frame
     int32_t mp, np;     // NS frame padded to the GEMM tile
     int32_t tall;       // 1 if rows > cols
-    int32_t pad0;
+    int32_t uvec;       // 1 if cols % 4 == 0 and every caller pointer is 4-element aligned
     // workspace buffers (NS frame, mp x np, zero-padded).  Step k reads index
     // k & 1 and writes index (k & 1) ^ 1.
     //   fp32: the iterate is x32[k & 1], which is also the MFMA operand.

@@ -20,6 +20,12 @@ Sources (cited by page title and section; the page text is Chinese):
 * [Adam vs Muon essay] -- guanweilu.cn/article/354.html: the step is named
   ``muon_step(weight, grad, momentum, lr, beta)``; update = U V^T of the
   momentum.
+* [Muon在Stiefel流形上的精确闭式更新解析] -- mlqm.cn/news/1339166: the AdamW
+  half of a training step (section 4.3) and the Muon-Cayley update on the
+  Stiefel manifold (sections 1.3, 3.1-3.3, 6.2).
+
+Modules: ``muon_oracle`` (the Muon step), ``jacobi_svd`` (a pin for it),
+``adamw_oracle`` (AdamW for the non-matrix parameters).
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, invariants, a hand-written Jacobi SVD, library routines
@@ -44,3 +50,4 @@ from .muon_oracle import (  # noqa: F401
     hybrid_schedule,
 )
 from .jacobi_svd import jacobi_svd, msign_via_svd  # noqa: F401
+from .adamw_oracle import adamw_step  # noqa: F401

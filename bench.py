@@ -164,6 +164,43 @@ def summarize_profiles(prof_dir, workload_id, commands):
     print(json.dumps({"written": [os.path.relpath(out, ROOT), os.path.relpath(TRAFFIC_FILE, ROOT)]}))
 
 
+def measure_adamw(dev, steps, dtype="bf16"):
+    """The AdamW half of the step: the transformer's non-matrix parameters (token
+    embedding and head, 32000 x 2048 each, and 49 norm vectors of 2048), timed with
+    the library's HIP events.  Algorithmic bytes per element: read p, g and the two
+    fp32 moments, write p and the moments = 3 es + 16."""
+    import torch
+    import matrix_aware_optimizer_amd as mao
+    import workloads as wk
+    sizes = wk.transformer_adamw_sizes()
+    td = wk.torch_dtype(dtype)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    P = [(0.02 * torch.randn(n, generator=g, device=dev)).to(td) for n in sizes]
+    G = [(1e-3 * torch.randn(n, generator=g, device=dev)).to(td) for n in sizes]
+    M = [torch.zeros(n, dtype=torch.float32, device=dev) for n in sizes]
+    V = [torch.zeros(n, dtype=torch.float32, device=dev) for n in sizes]
+    kw = dict(lr=1e-3, betas=(0.9, 0.95), eps=1e-8, weight_decay=0.1)
+    ws = mao.allocate_workspace(mao.muon_adamw_workspace_bytes(P, G, M, V, step=1, **kw), dev)
+    for t in range(1, 3):
+        mao.muon_adamw_step(P, G, M, V, step=t, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    mao.muon_profile_enable(True)
+    mao.muon_profile_read()
+    for t in range(3, 3 + steps):
+        mao.muon_adamw_step(P, G, M, V, step=t, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    prof = mao.muon_profile_read()["adamw"]
+    mao.muon_profile_enable(False)
+    ms = prof["ms"] / max(1, prof["launches"])
+    es = 2 if dtype == "bf16" else 4
+    elems = sum(sizes)
+    gbs = (3 * es + 16) * elems / (ms * 1e-3) / 1e9
+    return {"workload": f"transformer non-matrix parameters ({len(sizes)} tensors, {elems} elements, {dtype})",
+            "ms_per_step": round(ms, 4), "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_element": 3 * es + 16}
+
+
 def ns_flops(shapes, steps):
     tot = 0
     for r, c in shapes:
@@ -334,6 +371,9 @@ def main():
             "flops_per_launch": update_flops_per_launch(wl.shapes),
         },
     }
+    # the other rows of the optimizer step, timed after the headline region
+    out["adamw"] = measure_adamw(dev, 10)
+
     if not args.no_cpu_baseline:
         print("# timing the fp64 oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

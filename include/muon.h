@@ -8,6 +8,7 @@
  *   X  <- a_k X + (b_k A + c_k A A) X,  A = X X^T,  k = 1..ns_steps
  *         (on the smaller side: matrices with rows > cols are transposed)
  *   W' = (1 - lr*wd) W - lr * s_rule(rows, cols) * X
+ * It also runs the AdamW step for the other parameters (muon_adamw_step).
  * Sources, cited by page title and section:
  *   [Muon优化器] linsight.cn/f25d614e.html -- the industrial Muon class
  *     (momentum, Nesterov, decay and apply), zeropower_via_newtonschulz
@@ -125,6 +126,45 @@ size_t muon_ns_workspace_bytes(const muon_ns_matrix* mats, int32_t n, const muon
 muon_status muon_ns(const muon_ns_matrix* mats, int32_t n, const muon_hparams* hp,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * AdamW for the parameters Muon does not take (embeddings, heads, biases,
+ * norms), as one grouped launch over a list of tensors:
+ *   m' = beta1 m + (1 - beta1) g
+ *   v' = beta2 v + (1 - beta2) g^2
+ *   p' = (1 - lr wd) p - lr (m' / (1 - beta1^t)) / (sqrt(v' / (1 - beta2^t)) + eps)
+ * Sources: [Muon优化器] section "AdamW的问题" (moments, bias corrections, the
+ * step); [DeepSeek V4 summary] section "Adam优化器的机制与AdamW的改进" (decay
+ * apart from the gradient update); [Muon在Stiefel流形上的精确闭式更新解析]
+ * section 4.3 (decay first, moments start at zero, t counts calls).
+ * Arithmetic is fp32; p' is rounded once (RNE) to the parameter dtype.
+ * --------------------------------------------------------------------------- */
+typedef struct {
+    void*       param;       /* in/out, numel elements of hp->dtype, contiguous */
+    const void* grad;        /* in, same dtype; NULL => the tensor is skipped (state untouched) */
+    float*      exp_avg;     /* in/out first moment, numel fp32 (zero before the first step) */
+    float*      exp_avg_sq;  /* in/out second moment, numel fp32 (zero before the first step) */
+    int64_t     numel;       /* >= 1, <= MUON_MAX_ADAMW_NUMEL */
+} muon_adamw_tensor;
+
+#define MUON_MAX_ADAMW_TENSORS 65536
+#define MUON_MAX_ADAMW_NUMEL   ((int64_t)1 << 40)
+
+typedef struct {
+    float lr;            /* finite */
+    float beta1, beta2;  /* in [0, 1) */
+    float eps;           /* finite, >= 0 */
+    float weight_decay;  /* finite */
+    int32_t step;        /* t >= 1: this call is the t-th step of these tensors */
+    int32_t dtype;       /* muon_dtype of param and grad */
+} muon_adamw_hparams;
+
+/* Device workspace bytes muon_adamw_step needs (0 on invalid arguments). */
+size_t muon_adamw_workspace_bytes(const muon_adamw_tensor* tensors, int32_t n, const muon_adamw_hparams* hp);
+/* One AdamW step over `n` tensors; the same validation, workspace and stream
+ * rules as muon_step.  Tensors must not overlap each other or the workspace. */
+muon_status muon_adamw_step(const muon_adamw_tensor* tensors, int32_t n, const muon_adamw_hparams* hp,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* muon_status_string(int32_t status);
 /* Detail of the calling thread's last failure ("" if none). */
@@ -135,8 +175,8 @@ const char* muon_last_error_message(void);
  * events; muon_profile_read synchronizes them and returns, per kernel class,
  * the summed duration in milliseconds and the number of launches, then
  * resets the counters.  Classes: 0 momentum+norm, 1 norm finalize, 2 Gram,
- * 3 polynomial, 4 update, 5 apply.  Host-side bookkeeping only. */
-#define MUON_KCLASS_COUNT 6
+ * 3 polynomial, 4 update, 5 apply, 6 AdamW.  Host-side bookkeeping only. */
+#define MUON_KCLASS_COUNT 7
 typedef struct {
     double  ms[MUON_KCLASS_COUNT];
     int64_t launches[MUON_KCLASS_COUNT];

@@ -7,7 +7,8 @@ built, or the device is not gfx950, the calls raise.
 
 The names mirror the C entry points:
 ``muon_step``, ``muon_ns``, ``muon_workspace_bytes``,
-``muon_ns_workspace_bytes``, ``muon_status_string``,
+``muon_ns_workspace_bytes``, ``muon_adamw_step``,
+``muon_adamw_workspace_bytes``, ``muon_status_string``,
 ``muon_last_error_message``, ``muon_profile_enable``, ``muon_profile_read``,
 ``muon_version``.
 """
@@ -31,8 +32,8 @@ MUON_BF16 = 1
 
 SCALE_RULES = {"naive": 0, "kellerjordan": 1, "mup": 2, "moonlight": 3}
 MUON_FLAG_NESTEROV = 1
-MUON_KCLASS_COUNT = 6
-KERNEL_CLASSES = ("momentum_norm", "norm_finalize", "gram", "poly", "update", "apply")
+MUON_KCLASS_COUNT = 7
+KERNEL_CLASSES = ("momentum_norm", "norm_finalize", "gram", "poly", "update", "apply", "adamw")
 
 
 class MuonMatrix(ctypes.Structure):
@@ -56,6 +57,17 @@ class MuonNsMatrix(ctypes.Structure):
                 ("cols", ctypes.c_int64)]
 
 
+class MuonAdamwTensor(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p),
+                ("exp_avg_sq", ctypes.c_void_p), ("numel", ctypes.c_int64)]
+
+
+class MuonAdamwHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
 class MuonProfile(ctypes.Structure):
     _fields_ = [("ms", ctypes.c_double * MUON_KCLASS_COUNT), ("launches", ctypes.c_int64 * MUON_KCLASS_COUNT)]
 
@@ -69,6 +81,11 @@ SIGNATURES = {
                                                   ctypes.POINTER(MuonHparams)]),
     "muon_ns": (ctypes.c_int32, [ctypes.POINTER(MuonNsMatrix), ctypes.c_int32, ctypes.POINTER(MuonHparams),
                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "muon_adamw_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MuonAdamwTensor), ctypes.c_int32,
+                                                     ctypes.POINTER(MuonAdamwHparams)]),
+    "muon_adamw_step": (ctypes.c_int32, [ctypes.POINTER(MuonAdamwTensor), ctypes.c_int32,
+                                         ctypes.POINTER(MuonAdamwHparams), ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p]),
     "muon_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "muon_last_error_message": (ctypes.c_char_p, []),
     "muon_profile_enable": (ctypes.c_int32, [ctypes.c_int32]),
@@ -281,6 +298,65 @@ def muon_ns(inputs, outputs, *, schedule, eps=1e-7, workspace=None, stream=None)
         raise MuonError(MUON_ERR_WORKSPACE, f"workspace has {workspace.numel()} bytes, {need} needed")
     _check(lib.muon_ns(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                        workspace.numel() * workspace.element_size(), _stream_handle(stream)))
+    return workspace
+
+
+def _adamw_tensors(params, grads, exp_avgs, exp_avg_sqs):
+    import torch
+    params, grads, exp_avgs, exp_avg_sqs = list(params), list(grads), list(exp_avgs), list(exp_avg_sqs)
+    if not (len(params) == len(grads) == len(exp_avgs) == len(exp_avg_sqs)):
+        raise ValueError("params, grads, exp_avgs and exp_avg_sqs must have equal lengths")
+    arr = (MuonAdamwTensor * max(1, len(params)))()
+    dtype = None
+    for i, (p, g, m, v) in enumerate(zip(params, grads, exp_avgs, exp_avg_sqs)):
+        for t, what in ((p, "param"), (m, "exp_avg"), (v, "exp_avg_sq")):
+            if not t.is_contiguous():
+                raise ValueError(f"{what}[{i}] must be contiguous")
+        if g is not None and (not g.is_contiguous() or g.shape != p.shape or g.dtype != p.dtype):
+            raise ValueError(f"grad[{i}] must be contiguous and match param[{i}] in shape and dtype")
+        for t, what in ((m, "exp_avg"), (v, "exp_avg_sq")):
+            if t.dtype != torch.float32 or t.numel() != p.numel():
+                raise ValueError(f"{what}[{i}] must be float32 with param[{i}]'s number of elements")
+        code = _dtype_code(p)
+        if dtype is None:
+            dtype = code
+        elif code != dtype:
+            raise ValueError("all params of one call must share a dtype")
+        arr[i] = MuonAdamwTensor(p.data_ptr(), g.data_ptr() if g is not None else None, m.data_ptr(),
+                                 v.data_ptr(), p.numel())
+    return arr, len(params), (MUON_BF16 if dtype is None else dtype)
+
+
+def muon_adamw_workspace_bytes(params, grads, exp_avgs, exp_avg_sqs, *, lr=1e-3, betas=(0.9, 0.999),
+                               eps=1e-8, weight_decay=0.0, step=1) -> int:
+    arr, n, dtype = _adamw_tensors(params, grads, exp_avgs, exp_avg_sqs)
+    hp = MuonAdamwHparams(lr, betas[0], betas[1], eps, weight_decay, int(step), dtype)
+    size = load().muon_adamw_workspace_bytes(arr, n, ctypes.byref(hp))
+    if size == 0:
+        raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error_message())
+    return int(size)
+
+
+def muon_adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr, betas=(0.9, 0.999), eps=1e-8,
+                    weight_decay=0.0, step, workspace=None, stream=None):
+    """One grouped AdamW step, in place on params and the fp32 moments.
+
+    ``step`` counts calls and starts at 1 (it sets the bias corrections).  A
+    ``None`` gradient skips its tensor.  Asynchronous on ``stream``.
+    """
+    params = list(params)
+    arr, n, dtype = _adamw_tensors(params, grads, exp_avgs, exp_avg_sqs)
+    hp = MuonAdamwHparams(lr, betas[0], betas[1], eps, weight_decay, int(step), dtype)
+    lib = load()
+    need = lib.muon_adamw_workspace_bytes(arr, n, ctypes.byref(hp))
+    if need == 0:
+        raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error_message())
+    if workspace is None:
+        workspace = allocate_workspace(need, params[0].device if params else None)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise MuonError(MUON_ERR_WORKSPACE, f"workspace has {workspace.numel()} bytes, {need} needed")
+    _check(lib.muon_adamw_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
+                               workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return workspace
 
 

@@ -527,9 +527,132 @@ muon_status collect_ns(const muon_ns_matrix* mats, int32_t n, const muon_hparams
     return check_overlaps(iv);
 }
 
+// ---------------------------------------------------------------------------
+// AdamW
+// ---------------------------------------------------------------------------
+
+muon_status collect_adamw(const muon_adamw_tensor* ts, int32_t n, const muon_adamw_hparams* hp,
+                          std::vector<AdamWDesc>& out) {
+    if (n < 0 || n > MUON_MAX_ADAMW_TENSORS)
+        return fail(MUON_ERR_INVALID_ARG, "n = %d outside [0, %d]", n, MUON_MAX_ADAMW_TENSORS);
+    if (n > 0 && !ts) return fail(MUON_ERR_INVALID_ARG, "tensors is NULL");
+    if (!hp) return fail(MUON_ERR_INVALID_ARG, "hp is NULL");
+    if (hp->dtype != MUON_F32 && hp->dtype != MUON_BF16) return fail(MUON_ERR_INVALID_ARG, "unknown dtype %d", hp->dtype);
+    if (!std::isfinite(hp->lr)) return fail(MUON_ERR_INVALID_ARG, "lr is not finite");
+    if (!std::isfinite(hp->weight_decay)) return fail(MUON_ERR_INVALID_ARG, "weight_decay is not finite");
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(MUON_ERR_INVALID_ARG, "beta1 and beta2 must lie in [0, 1)");
+    if (!std::isfinite(hp->eps) || hp->eps < 0.0f) return fail(MUON_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (hp->step < 1) return fail(MUON_ERR_INVALID_ARG, "step %d must be >= 1", hp->step);
+    const size_t es = hp->dtype == MUON_BF16 ? 2 : 4;
+    std::vector<Interval> iv;
+    for (int i = 0; i < n; ++i) {
+        const muon_adamw_tensor& t = ts[i];
+        if (!t.grad) continue;
+        if (t.numel < 1 || t.numel > MUON_MAX_ADAMW_NUMEL)
+            return fail(MUON_ERR_INVALID_ARG, "tensor %d has numel %lld", i, (long long)t.numel);
+        if (!t.param || !t.exp_avg || !t.exp_avg_sq) return fail(MUON_ERR_INVALID_ARG, "tensor %d: a buffer is NULL", i);
+        const uintptr_t pp = reinterpret_cast<uintptr_t>(t.param), pg = reinterpret_cast<uintptr_t>(t.grad),
+                        pm = reinterpret_cast<uintptr_t>(t.exp_avg), pv = reinterpret_cast<uintptr_t>(t.exp_avg_sq);
+        if (pp % es || pg % es || pm % 4 || pv % 4) return fail(MUON_ERR_INVALID_ARG, "tensor %d: misaligned pointer", i);
+        const size_t cnt = static_cast<size_t>(t.numel);
+        iv.push_back({pp, pp + cnt * es, false, i});
+        iv.push_back({pg, pg + cnt * es, true, i});
+        iv.push_back({pm, pm + cnt * 4, false, i});
+        iv.push_back({pv, pv + cnt * 4, false, i});
+        AdamWDesc d{};
+        d.p = t.param;
+        d.g = t.grad;
+        d.m = t.exp_avg;
+        d.v = t.exp_avg_sq;
+        d.numel = t.numel;
+        d.vec = (pp % (4 * es) == 0 && pg % (4 * es) == 0 && pm % 16 == 0 && pv % 16 == 0) ? 1 : 0;
+        out.push_back(d);
+    }
+    return check_overlaps(iv);
+}
+
+size_t adamw_header_bytes(size_t n) {
+    return align_up(align_up(sizeof(AdamWDesc) * n, ALIGN) + sizeof(int32_t) * (n + 1), ALIGN);
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t muon_adamw_workspace_bytes(const muon_adamw_tensor* tensors, int32_t n, const muon_adamw_hparams* hp) {
+    std::vector<AdamWDesc> descs;
+    if (collect_adamw(tensors, n, hp, descs) != MUON_OK) return 0;
+    return std::max(adamw_header_bytes(descs.size()), ALIGN);
+}
+
+muon_status muon_adamw_step(const muon_adamw_tensor* tensors, int32_t n, const muon_adamw_hparams* hp,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    std::vector<AdamWDesc> descs;
+    muon_status st = collect_adamw(tensors, n, hp, descs);
+    if (st != MUON_OK) return st;
+    if (descs.empty()) { g_last_error.clear(); return MUON_OK; }
+    const size_t need = adamw_header_bytes(descs.size());
+    if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % ALIGN)
+        return fail(MUON_ERR_WORKSPACE, "workspace is not %zu-byte aligned", ALIGN);
+    if (workspace_bytes < need) return fail(MUON_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    {
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(workspace), hi = lo + need;
+        const size_t es = hp->dtype == MUON_BF16 ? 2 : 4;
+        for (const AdamWDesc& d : descs) {
+            const size_t cnt = static_cast<size_t>(d.numel);
+            const void* ptrs[4] = {d.p, d.g, d.m, d.v};
+            const size_t sz[4] = {cnt * es, cnt * es, cnt * 4, cnt * 4};
+            for (int q = 0; q < 4; ++q) {
+                const uintptr_t p = reinterpret_cast<uintptr_t>(ptrs[q]);
+                if (p < hi && p + sz[q] > lo) return fail(MUON_ERR_INVALID_ARG, "a tensor overlaps the workspace");
+            }
+        }
+    }
+    // chunk prefix sums (int32 chunk indices)
+    const size_t nt = descs.size();
+    std::vector<int32_t> prefix(nt + 1, 0);
+    int64_t total = 0;
+    for (size_t i = 0; i < nt; ++i) {
+        total += (descs[i].numel + ADAMW_CHUNK - 1) / ADAMW_CHUNK;
+        if (total > INT32_MAX) return fail(MUON_ERR_UNSUPPORTED, "too many elements in one call (split the list)");
+        prefix[i + 1] = static_cast<int32_t>(total);
+    }
+    int dev = 0, cu_count = 0;
+    st = check_device(&dev, &cu_count);
+    if (st != MUON_OK) return st;
+    const size_t off_prefix = align_up(sizeof(AdamWDesc) * nt, ALIGN);
+    std::vector<char> header(off_prefix + sizeof(int32_t) * (nt + 1), 0);
+    std::memcpy(header.data(), descs.data(), sizeof(AdamWDesc) * nt);
+    std::memcpy(header.data() + off_prefix, prefix.data(), sizeof(int32_t) * (nt + 1));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = upload(dev, workspace, header.data(), header.size(), s);
+    if (st != MUON_OK) return st;
+
+    // per-call scalars in fp64 from the fp32 hyperparameters
+    const double lr = hp->lr, b1 = hp->beta1, b2 = hp->beta2, wd = hp->weight_decay;
+    const double bc1 = 1.0 - std::pow(b1, static_cast<double>(hp->step));
+    const double bc2 = 1.0 - std::pow(b2, static_cast<double>(hp->step));
+    AdamWArgs a{};
+    a.descs = static_cast<const AdamWDesc*>(workspace);
+    a.prefix = reinterpret_cast<const int32_t*>(static_cast<char*>(workspace) + off_prefix);
+    a.n = static_cast<int32_t>(nt);
+    a.total = static_cast<int32_t>(total);
+    a.beta1 = hp->beta1;
+    a.beta2 = hp->beta2;
+    a.one_m_beta1 = static_cast<float>(1.0 - b1);
+    a.one_m_beta2 = static_cast<float>(1.0 - b2);
+    a.eps = hp->eps;
+    a.decay = static_cast<float>(1.0 - lr * wd);
+    a.step_size = static_cast<float>(lr / bc1);
+    a.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
+    const int grid = static_cast<int>(std::min<int64_t>(total, static_cast<int64_t>(std::max(cu_count, 1)) * 8));
+    st = timed_launch(6, s, "AdamW kernel", [&] { return launch_adamw(hp->dtype, a, grid, s); });
+    if (st != MUON_OK) return st;
+    g_last_error.clear();
+    return MUON_OK;
+}
 
 size_t muon_workspace_bytes(const muon_matrix* mats, int32_t n, const muon_hparams* hp) {
     std::vector<Item> items;

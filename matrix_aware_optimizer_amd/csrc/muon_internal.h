@@ -78,7 +78,31 @@ struct NsArgs {
     int32_t ping;            // x32 / xop index read by this step; ping ^ 1 is written
 };
 
+// AdamW: one tensor of the list; work is split into ADAMW_CHUNK-element chunks.
+constexpr int ADAMW_THREADS = 256;
+constexpr int ADAMW_CHUNK = ADAMW_THREADS * 16;
+struct AdamWDesc {
+    void* p;
+    const void* g;
+    float* m;
+    float* v;
+    int64_t numel;
+    int32_t vec;        // 1 if p, g are 4-element aligned and m, v 16-byte aligned
+    int32_t pad0;
+};
+struct AdamWArgs {
+    const AdamWDesc* descs;
+    const int32_t* prefix;   // n + 1 exclusive prefix sums of chunks
+    int32_t n;
+    int32_t total;           // chunks
+    float beta1, beta2, one_m_beta1, one_m_beta2;
+    float eps, decay;        // decay = 1 - lr * weight_decay
+    float step_size;         // lr / (1 - beta1^t)
+    float inv_sqrt_bc2;      // 1 / sqrt(1 - beta2^t)
+};
+
 // Kernel launchers (defined next to the kernels).
+hipError_t launch_adamw(int dtype, const AdamWArgs& args, int grid, hipStream_t s);
 hipError_t launch_momentum_norm(int dtype, bool ns_only, const EwArgs& args, int grid, hipStream_t s);
 hipError_t launch_norm_finalize(const MatDesc* descs, const float* partials, int nmat, float eps,
                                 hipStream_t s);

@@ -159,3 +159,79 @@ def test_binding_rejects_non_2d_and_non_contiguous():
     w2 = torch.zeros(8, 6).t()
     with pytest.raises(ValueError):
         mao.muon_workspace_bytes([w2], [w2], [w2], schedule=[(1.0, 0.0, 0.0)])
+
+
+# ----------------------------------------------------------------------------
+# AdamW entry points
+# ----------------------------------------------------------------------------
+
+def _adamw(specs):
+    arr = (mao.MuonAdamwTensor * max(1, len(specs)))()
+    for i, (p, g, m, v, n) in enumerate(specs):
+        arr[i] = mao.MuonAdamwTensor(p, g, m, v, n)
+    return arr
+
+
+def _adamw_hp(**kw):
+    base = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, step=1, dtype=mao.MUON_BF16)
+    base.update(kw)
+    return mao.MuonAdamwHparams(base["lr"], base["beta1"], base["beta2"], base["eps"], base["weight_decay"],
+                                base["step"], base["dtype"])
+
+
+GOOD = (FAKE, FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30), 1000)
+
+
+@pytest.mark.parametrize("case", ["null_hp", "bad_dtype", "beta1_one", "beta2_neg", "nan_lr", "inf_wd", "neg_eps",
+                                  "step_zero", "numel_zero", "null_param", "misaligned_moment", "overlap",
+                                  "moment_overlaps_param"])
+def test_adamw_invalid_arguments_are_rejected(case):
+    lib = mao.load()
+    spec = list(GOOD)
+    hp = _adamw_hp()
+    if case == "bad_dtype":
+        hp.dtype = 5
+    elif case == "beta1_one":
+        hp.beta1 = 1.0
+    elif case == "beta2_neg":
+        hp.beta2 = -0.1
+    elif case == "nan_lr":
+        hp.lr = float("nan")
+    elif case == "inf_wd":
+        hp.weight_decay = float("inf")
+    elif case == "neg_eps":
+        hp.eps = -1e-8
+    elif case == "step_zero":
+        hp.step = 0
+    elif case == "numel_zero":
+        spec[4] = 0
+    elif case == "null_param":
+        spec[0] = None
+    elif case == "misaligned_moment":
+        spec[2] = FAKE + (2 << 30) + 2
+    elif case == "overlap":
+        spec[3] = FAKE + (2 << 30) + 8    # the two moments overlap
+    elif case == "moment_overlaps_param":
+        spec[2] = FAKE + 16
+    arr = _adamw([tuple(spec)])
+    hpp = None if case == "null_hp" else ctypes.byref(hp)
+    st = lib.muon_adamw_step(arr, 1, hpp, ctypes.c_void_p(FAKE + (8 << 30)), 1 << 40, None)
+    assert st == mao.MUON_ERR_INVALID_ARG, (case, st, mao.muon_last_error_message())
+    assert lib.muon_adamw_workspace_bytes(arr, 1, hpp) == 0
+
+
+def test_adamw_workspace_errors_and_noops():
+    lib = mao.load()
+    hp = _adamw_hp()
+    arr = _adamw([GOOD, (FAKE + (4 << 30), FAKE + (5 << 30), FAKE + (6 << 30), FAKE + (7 << 30), 77)])
+    need = lib.muon_adamw_workspace_bytes(arr, 2, ctypes.byref(hp))
+    assert need >= 256
+    ws = FAKE + (8 << 30)
+    assert lib.muon_adamw_step(arr, 2, ctypes.byref(hp), None, need, None) == mao.MUON_ERR_WORKSPACE
+    assert lib.muon_adamw_step(arr, 2, ctypes.byref(hp), ctypes.c_void_p(ws), need - 1, None) == mao.MUON_ERR_WORKSPACE
+    assert lib.muon_adamw_step(arr, 2, ctypes.byref(hp), ctypes.c_void_p(ws + 8), need, None) == mao.MUON_ERR_WORKSPACE
+    assert lib.muon_adamw_step(arr, 2, ctypes.byref(hp), ctypes.c_void_p(FAKE), need, None) == mao.MUON_ERR_INVALID_ARG
+    # empty list and all-skipped lists do nothing
+    assert lib.muon_adamw_step(None, 0, ctypes.byref(hp), None, 0, None) == mao.MUON_OK
+    skip = _adamw([(FAKE, None, FAKE + (2 << 30), FAKE + (3 << 30), 1000)])
+    assert lib.muon_adamw_step(skip, 1, ctypes.byref(hp), None, 0, None) == mao.MUON_OK

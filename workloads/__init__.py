@@ -221,3 +221,38 @@ def device_matrix(wl: Workload, index: int, device):
     G = grad_like().to(td)
     M = torch.zeros((rows, cols), device=device, dtype=td) if wl.momentum == "zero" else grad_like().to(td)
     return {"W": W.contiguous(), "G": G.contiguous(), "M": M.contiguous()}
+
+
+# --------------------------------------------------------------------------
+# AdamW tensors (the parameters Muon does not take).
+# --------------------------------------------------------------------------
+
+def transformer_adamw_sizes(d=2048, layers=24, vocab=32000):
+    """Non-matrix parameters of the d=2048, 24-layer transformer: token embedding and
+    output head (vocab x d each; the pages route both to AdamW), two norm weight
+    vectors per layer and a final norm.  The pages give no vocabulary size; 32000 is
+    a stated stand-in."""
+    return [vocab * d, vocab * d] + [d] * (2 * layers + 1)
+
+
+def adamw_host_tensors(sizes, dtype="bf16", seed=0, step=1):
+    """Seeded host arrays p, g (dtype values as float32) and m, v (float32) per tensor.
+
+    p ~ N(0, 0.02^2), g ~ N(0, 1e-3^2) times a per-tensor scale 10^U(-1, 1); the
+    moments are those of a run already under way when step > 1: m ~ N(0, 1e-3^2),
+    v ~ U(0, 2e-6); zero when step == 1.
+    """
+    out = []
+    for i, n in enumerate(sizes):
+        rng = np.random.default_rng([9000 + seed, i])
+        scale = 10.0 ** rng.uniform(-1.0, 1.0)
+        p = _store(0.02 * rng.standard_normal(n), dtype)
+        g = _store(1e-3 * scale * rng.standard_normal(n), dtype)
+        if step > 1:
+            m = (1e-3 * rng.standard_normal(n)).astype(np.float32)
+            v = rng.uniform(0.0, 2e-6, n).astype(np.float32)
+        else:
+            m = np.zeros(n, np.float32)
+            v = np.zeros(n, np.float32)
+        out.append({"p": p, "g": g, "m": m, "v": v})
+    return out

@@ -25,7 +25,8 @@ Sources (cited by page title and section; the page text is Chinese):
   Stiefel manifold (sections 1.3, 3.1-3.3, 6.2).
 
 Modules: ``muon_oracle`` (the Muon step), ``jacobi_svd`` (a pin for it),
-``adamw_oracle`` (AdamW for the non-matrix parameters).
+``adamw_oracle`` (AdamW for the non-matrix parameters), ``cayley_oracle``
+(Muon-Cayley on the Stiefel manifold).
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, invariants, a hand-written Jacobi SVD, library routines
@@ -51,3 +52,11 @@ from .muon_oracle import (  # noqa: F401
 )
 from .jacobi_svd import jacobi_svd, msign_via_svd  # noqa: F401
 from .adamw_oracle import adamw_step  # noqa: F401
+from .cayley_oracle import (  # noqa: F401
+    cayley_retraction,
+    cayley_retraction_woodbury,
+    cayley_step,
+    center_columns,
+    orthogonality_error,
+    project_tangent,
+)

@@ -1,0 +1,153 @@
+"""Pins for the fp64 Muon-Cayley oracle (CPU only).
+
+* 2 x 1 closed form: W = e1, V = v e2 gives a plane rotation,
+  W' = ((1 - t^2), -2 t) / (1 + t^2) with t = lr v / 2.
+* Orthogonality: W'^T W' = I to rounding for any lr (the page's section 3.1).
+* Tangent space (section 1.3): W^T V + V^T W = 0; the projection is idempotent
+  and leaves tangent vectors unchanged.
+* First order: (W'(lr) - W) / lr -> -(V - W V^T W) as lr -> 0, which fixes the
+  sign of A and c = lr / 2.
+* The page's Woodbury form (section 6.2) equals the n x n solve.
+* Momentum of centered constant gradients: M_t = (1 - beta^t) G_centered.
+* Planted mistakes are each caught.
+"""
+import numpy as np
+import pytest
+
+import oracle as orc
+import oracle.cayley_oracle as co
+
+
+def _stiefel(rng, n, k):
+    q, r = np.linalg.qr(rng.standard_normal((n, k)))
+    return q * np.sign(np.diag(r))
+
+
+def test_two_by_one_is_a_plane_rotation():
+    W = np.array([[1.0], [0.0]])
+    for v, lr in [(0.3, 0.1), (2.0, 0.5), (-1.5, 2.0)]:
+        V = np.array([[0.0], [v]])
+        t = lr * v / 2
+        expect = np.array([[(1 - t * t)], [-2 * t]]) / (1 + t * t)
+        assert np.max(np.abs(orc.cayley_retraction(W, V, lr) - expect)) < 1e-15
+
+
+@pytest.mark.parametrize("lr", [1e-3, 0.1, 3.0])
+def test_retraction_keeps_columns_orthonormal(lr):
+    rng = np.random.default_rng(1)
+    W = _stiefel(rng, 40, 7)
+    V = orc.project_tangent(W, rng.standard_normal((40, 7)))
+    assert orc.orthogonality_error(orc.cayley_retraction(W, V, lr)) < 1e-13
+
+
+def test_projection_is_onto_the_tangent_space():
+    rng = np.random.default_rng(2)
+    W = _stiefel(rng, 30, 6)
+    X = rng.standard_normal((30, 6))
+    V = orc.project_tangent(W, X)
+    assert np.max(np.abs(W.T @ V + V.T @ W)) < 1e-14
+    assert np.max(np.abs(orc.project_tangent(W, V) - V)) < 1e-14
+    # a tangent vector with a nonzero skew part W^T T is left unchanged
+    S = rng.standard_normal((6, 6))
+    T = W @ (S - S.T) + (np.eye(30) - W @ W.T) @ rng.standard_normal((30, 6))
+    assert np.max(np.abs(orc.project_tangent(W, T) - T)) < 1e-13
+
+
+def test_first_order_direction():
+    rng = np.random.default_rng(3)
+    W = _stiefel(rng, 25, 5)
+    V = orc.project_tangent(W, rng.standard_normal((25, 5)))
+    lr = 1e-7
+    d = (orc.cayley_retraction(W, V, lr) - W) / lr
+    assert np.max(np.abs(d + (V - W @ (V.T @ W)))) < 1e-5
+
+
+@pytest.mark.parametrize("shape", [(64, 16), (33, 5), (8, 8)])
+def test_woodbury_form_equals_direct_solve(shape):
+    rng = np.random.default_rng(4)
+    W = _stiefel(rng, *shape)
+    V = orc.project_tangent(W, rng.standard_normal(shape))
+    for lr in (1e-3, 0.3, 2.0):
+        a = orc.cayley_retraction(W, V, lr)
+        b = orc.cayley_retraction_woodbury(W, V, lr)
+        assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_centering_and_momentum_closed_form():
+    rng = np.random.default_rng(5)
+    W = _stiefel(rng, 20, 4)
+    G = rng.standard_normal((20, 4)) + 3.0
+    Gc = orc.center_columns(G)
+    assert np.max(np.abs(Gc.mean(axis=0))) < 1e-15
+    M = np.zeros_like(G)
+    beta = orc.as_f32(0.9)
+    for t in range(1, 6):
+        out = orc.cayley_step(W, G, M, lr=0.0, beta=0.9)
+        M = out["M"]
+        assert np.max(np.abs(M - (1 - beta ** t) * Gc)) < 1e-14
+        assert np.max(np.abs(out["W"] - W)) < 1e-15      # lr = 0 leaves W
+
+
+def test_wide_matrix_uses_the_transposed_problem():
+    rng = np.random.default_rng(6)
+    W = _stiefel(rng, 24, 6).T                      # 6 x 24, orthonormal rows
+    G = rng.standard_normal((6, 24))
+    M = rng.standard_normal((6, 24))
+    out = orc.cayley_step(W, G, M, lr=0.2, beta=0.9)
+    ref = orc.cayley_step(W.T, G.T, M.T, lr=0.2, beta=0.9)
+    assert np.max(np.abs(out["W"] - ref["W"].T)) == 0.0
+    assert np.max(np.abs(out["W"] @ out["W"].T - np.eye(6))) < 1e-13
+
+
+# ----------------------------------------------------------------------------
+# Planted mistakes
+# ----------------------------------------------------------------------------
+
+def _retr(sign=1.0, cfac=0.5):
+    def r(W, V, lr):
+        c = lr * cfac
+        A = sign * (V @ W.T - W @ V.T)
+        eye = np.eye(W.shape[0])
+        return np.linalg.solve(eye + c * A, (eye - c * A) @ W)
+    return r
+
+
+def _pins_fail(monkeypatch, **patches):
+    for name, fn in patches.items():
+        monkeypatch.setattr(co, name, fn)
+        monkeypatch.setattr(orc, name, fn)
+    checks = [test_two_by_one_is_a_plane_rotation, test_projection_is_onto_the_tangent_space,
+              test_first_order_direction, test_centering_and_momentum_closed_form,
+              lambda: test_retraction_keeps_columns_orthonormal(0.1)]
+    failed = 0
+    for chk in checks:
+        try:
+            chk()
+        except AssertionError:
+            failed += 1
+    return failed
+
+
+@pytest.mark.parametrize("kind", ["flipped_A", "c_equals_lr", "projection_without_sym", "centering_rows",
+                                  "plain_momentum"])
+def test_pins_catch_planted_mistake(kind, monkeypatch):
+    if kind == "flipped_A":
+        n = _pins_fail(monkeypatch, cayley_retraction=_retr(sign=-1.0))
+    elif kind == "c_equals_lr":
+        n = _pins_fail(monkeypatch, cayley_retraction=_retr(cfac=1.0))
+    elif kind == "projection_without_sym":
+        n = _pins_fail(monkeypatch, project_tangent=lambda W, X: X - W @ (W.T @ X))
+    elif kind == "centering_rows":
+        n = _pins_fail(monkeypatch, center_columns=lambda G: G - np.asarray(G).mean(axis=1, keepdims=True))
+    else:
+        orig = co.cayley_step
+
+        def plain(W, G, M, *, lr, beta, retraction=co.cayley_retraction):
+            W, G, M = (np.asarray(x, np.float64) for x in (W, G, M))
+            b = orc.as_f32(beta)
+            Mn = b * M + co.center_columns(G)
+            V = co.project_tangent(W, Mn)
+            return {"W": retraction(W, V, lr), "M": Mn, "V": V}
+        n = _pins_fail(monkeypatch, cayley_step=plain)
+        assert co.cayley_step is not orig
+    assert n > 0, kind

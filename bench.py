@@ -201,6 +201,44 @@ def measure_adamw(dev, steps, dtype="bf16"):
             "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_element": 3 * es + 16}
 
 
+def measure_cayley(dev, steps):
+    """The Muon-Cayley row: 32 matrices of 4096 x 128 in fp32, all of its kernels per
+    step, timed with the library's HIP events.  Algorithmic FLOPs per matrix:
+    16 N K^2 (the K x K products W^T G, W^T M, W^T W, W^T V, V^T V over N and the
+    N x K products W S, V Y1, W Y2), against the fp32 vector peak: this path is fp32
+    FMA work, not MFMA."""
+    import torch
+    import matrix_aware_optimizer_amd as mao
+    import workloads as wk
+    shapes = wk.CAYLEY_SET
+    g = torch.Generator(device=dev)
+    g.manual_seed(777)
+    W, G, M = [], [], []
+    for (r, c) in shapes:
+        q, _ = torch.linalg.qr(torch.randn(r, c, generator=g, device=dev))
+        W.append(q.contiguous())
+        G.append(1e-2 * torch.randn(r, c, generator=g, device=dev))
+        M.append(torch.zeros(r, c, device=dev))
+    ws = mao.allocate_workspace(mao.muon_cayley_workspace_bytes(W, G, M), dev)
+    for _ in range(2):
+        mao.muon_cayley_step(W, G, M, lr=1e-3, beta=0.9, workspace=ws)
+    torch.cuda.synchronize()
+    mao.muon_profile_enable(True)
+    mao.muon_profile_read()
+    for _ in range(steps):
+        mao.muon_cayley_step(W, G, M, lr=1e-3, beta=0.9, workspace=ws)
+    torch.cuda.synchronize()
+    prof = mao.muon_profile_read()["cayley"]
+    mao.muon_profile_enable(False)
+    ms = prof["ms"] / steps
+    flops = sum(16.0 * max(r, c) * min(r, c) ** 2 for r, c in shapes)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": f"{len(shapes)} x {shapes[0][0]}x{shapes[0][1]} fp32 on the Stiefel manifold",
+            "ms_per_step": round(ms, 4), "matrices_per_s": round(len(shapes) / (ms * 1e-3), 1),
+            "bound": "alu", "achieved": round(tf, 2), "peak": F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / F32_PEAK_TFLOPS, 4), "flops_per_step": flops}
+
+
 def ns_flops(shapes, steps):
     tot = 0
     for r, c in shapes:
@@ -373,6 +411,7 @@ def main():
     }
     # the other rows of the optimizer step, timed after the headline region
     out["adamw"] = measure_adamw(dev, 10)
+    out["cayley"] = measure_cayley(dev, 5)
 
     if not args.no_cpu_baseline:
         print("# timing the fp64 oracle on a sample", file=sys.stderr, flush=True)

@@ -8,7 +8,8 @@
  *   X  <- a_k X + (b_k A + c_k A A) X,  A = X X^T,  k = 1..ns_steps
  *         (on the smaller side: matrices with rows > cols are transposed)
  *   W' = (1 - lr*wd) W - lr * s_rule(rows, cols) * X
- * It also runs the AdamW step for the other parameters (muon_adamw_step).
+ * It also runs the AdamW step for the other parameters (muon_adamw_step) and
+ * the Muon-Cayley step on the Stiefel manifold (muon_cayley_step).
  * Sources, cited by page title and section:
  *   [Muon优化器] linsight.cn/f25d614e.html -- the industrial Muon class
  *     (momentum, Nesterov, decay and apply), zeropower_via_newtonschulz
@@ -165,6 +166,39 @@ size_t muon_adamw_workspace_bytes(const muon_adamw_tensor* tensors, int32_t n, c
 muon_status muon_adamw_step(const muon_adamw_tensor* tensors, int32_t n, const muon_adamw_hparams* hp,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Muon-Cayley: the closed-form update that keeps a weight on the Stiefel
+ * manifold ([Muon在Stiefel流形上的精确闭式更新解析], sections 1.3, 3.1-3.3, 6.2).
+ * For W with orthonormal columns (W^T W = I; for rows < cols, orthonormal rows,
+ * handled as the transpose):
+ *   M' = beta M + (1 - beta) (G - 1 mean(G)^T)      mean over the rows
+ *   V  = M' - W sym(W^T M'),   sym(S) = (S + S^T) / 2
+ *   W' = (I + c A)^-1 (I - c A) W,  A = V W^T - W V^T,  c = lr / 2
+ * computed through the 2k x 2k Woodbury form (k = min(rows, cols)).  fp32
+ * buffers; the 2k x 2k solve runs in fp64 with partial pivoting.  No weight
+ * decay on this path.
+ * --------------------------------------------------------------------------- */
+typedef struct {
+    float*       weight;    /* in/out rows x cols, fp32, row-major */
+    const float* grad;      /* in; NULL => the matrix is skipped */
+    float*       momentum;  /* in/out, same shape (zero before the first step) */
+    int64_t      rows, cols;
+} muon_cayley_matrix;
+
+#define MUON_CAYLEY_MAX_K 256   /* min(rows, cols) limit of this build */
+
+typedef struct {
+    float lr;      /* finite */
+    float beta;    /* in [0, 1) */
+} muon_cayley_hparams;
+
+size_t muon_cayley_workspace_bytes(const muon_cayley_matrix* mats, int32_t n, const muon_cayley_hparams* hp);
+/* One Muon-Cayley step over `n` matrices (grouped launches).  Same workspace,
+ * stream and validation rules as muon_step; min(rows, cols) above
+ * MUON_CAYLEY_MAX_K is MUON_ERR_UNSUPPORTED. */
+muon_status muon_cayley_step(const muon_cayley_matrix* mats, int32_t n, const muon_cayley_hparams* hp,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* muon_status_string(int32_t status);
 /* Detail of the calling thread's last failure ("" if none). */
@@ -175,8 +209,9 @@ const char* muon_last_error_message(void);
  * events; muon_profile_read synchronizes them and returns, per kernel class,
  * the summed duration in milliseconds and the number of launches, then
  * resets the counters.  Classes: 0 momentum+norm, 1 norm finalize, 2 Gram,
- * 3 polynomial, 4 update, 5 apply, 6 AdamW.  Host-side bookkeeping only. */
-#define MUON_KCLASS_COUNT 7
+ * 3 polynomial, 4 update, 5 apply, 6 AdamW, 7 Muon-Cayley (all its kernels).
+ * Host-side bookkeeping only. */
+#define MUON_KCLASS_COUNT 8
 typedef struct {
     double  ms[MUON_KCLASS_COUNT];
     int64_t launches[MUON_KCLASS_COUNT];

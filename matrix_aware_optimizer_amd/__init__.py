@@ -8,7 +8,8 @@ built, or the device is not gfx950, the calls raise.
 The names mirror the C entry points:
 ``muon_step``, ``muon_ns``, ``muon_workspace_bytes``,
 ``muon_ns_workspace_bytes``, ``muon_adamw_step``,
-``muon_adamw_workspace_bytes``, ``muon_status_string``,
+``muon_adamw_workspace_bytes``, ``muon_cayley_step``,
+``muon_cayley_workspace_bytes``, ``muon_status_string``,
 ``muon_last_error_message``, ``muon_profile_enable``, ``muon_profile_read``,
 ``muon_version``.
 """
@@ -32,8 +33,8 @@ MUON_BF16 = 1
 
 SCALE_RULES = {"naive": 0, "kellerjordan": 1, "mup": 2, "moonlight": 3}
 MUON_FLAG_NESTEROV = 1
-MUON_KCLASS_COUNT = 7
-KERNEL_CLASSES = ("momentum_norm", "norm_finalize", "gram", "poly", "update", "apply", "adamw")
+MUON_KCLASS_COUNT = 8
+KERNEL_CLASSES = ("momentum_norm", "norm_finalize", "gram", "poly", "update", "apply", "adamw", "cayley")
 
 
 class MuonMatrix(ctypes.Structure):
@@ -68,6 +69,15 @@ class MuonAdamwHparams(ctypes.Structure):
                 ("dtype", ctypes.c_int32)]
 
 
+class MuonCayleyMatrix(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("momentum", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class MuonCayleyHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta", ctypes.c_float)]
+
+
 class MuonProfile(ctypes.Structure):
     _fields_ = [("ms", ctypes.c_double * MUON_KCLASS_COUNT), ("launches", ctypes.c_int64 * MUON_KCLASS_COUNT)]
 
@@ -86,6 +96,11 @@ SIGNATURES = {
     "muon_adamw_step": (ctypes.c_int32, [ctypes.POINTER(MuonAdamwTensor), ctypes.c_int32,
                                          ctypes.POINTER(MuonAdamwHparams), ctypes.c_void_p, ctypes.c_size_t,
                                          ctypes.c_void_p]),
+    "muon_cayley_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MuonCayleyMatrix), ctypes.c_int32,
+                                                      ctypes.POINTER(MuonCayleyHparams)]),
+    "muon_cayley_step": (ctypes.c_int32, [ctypes.POINTER(MuonCayleyMatrix), ctypes.c_int32,
+                                          ctypes.POINTER(MuonCayleyHparams), ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_void_p]),
     "muon_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "muon_last_error_message": (ctypes.c_char_p, []),
     "muon_profile_enable": (ctypes.c_int32, [ctypes.c_int32]),
@@ -357,6 +372,53 @@ def muon_adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr, betas=(0.9, 0.9
         raise MuonError(MUON_ERR_WORKSPACE, f"workspace has {workspace.numel()} bytes, {need} needed")
     _check(lib.muon_adamw_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                                workspace.numel() * workspace.element_size(), _stream_handle(stream)))
+    return workspace
+
+
+def _cayley_matrices(weights, grads, moms):
+    import torch
+    weights, grads, moms = list(weights), list(grads), list(moms)
+    if not (len(weights) == len(grads) == len(moms)):
+        raise ValueError("weights, grads and momenta must have equal lengths")
+    arr = (MuonCayleyMatrix * max(1, len(weights)))()
+    for i, (w, g, m) in enumerate(zip(weights, grads, moms)):
+        for t, what in ((w, "weight"), (m, "momentum")) + (((g, "grad"),) if g is not None else ()):
+            _check_matrix(t, f"{what}[{i}]")
+            if t.dtype != torch.float32 or t.shape != w.shape:
+                raise ValueError(f"{what}[{i}] must be float32 with weight[{i}]'s shape")
+        arr[i] = MuonCayleyMatrix(w.data_ptr(), g.data_ptr() if g is not None else None, m.data_ptr(),
+                                  w.shape[0], w.shape[1])
+    return arr, len(weights)
+
+
+def muon_cayley_workspace_bytes(weights, grads, moms, *, lr=1e-3, beta=0.9) -> int:
+    arr, n = _cayley_matrices(weights, grads, moms)
+    hp = MuonCayleyHparams(lr, beta)
+    size = load().muon_cayley_workspace_bytes(arr, n, ctypes.byref(hp))
+    if size == 0:
+        raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error_message())
+    return int(size)
+
+
+def muon_cayley_step(weights, grads, moms, *, lr, beta=0.9, workspace=None, stream=None):
+    """One grouped Muon-Cayley step (fp32), in place on ``weights`` and ``moms``.
+
+    Each weight must have orthonormal columns (orthonormal rows when it is wide);
+    the update keeps it so.  A ``None`` gradient skips its matrix.
+    """
+    weights = list(weights)
+    arr, n = _cayley_matrices(weights, grads, moms)
+    hp = MuonCayleyHparams(lr, beta)
+    lib = load()
+    need = lib.muon_cayley_workspace_bytes(arr, n, ctypes.byref(hp))
+    if need == 0:
+        raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error_message())
+    if workspace is None:
+        workspace = allocate_workspace(need, weights[0].device if weights else None)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise MuonError(MUON_ERR_WORKSPACE, f"workspace has {workspace.numel()} bytes, {need} needed")
+    _check(lib.muon_cayley_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
+                                workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return workspace
 
 

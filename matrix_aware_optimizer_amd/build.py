@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmuon.so")
-SOURCES = ["muon_api.hip", "momentum_apply.hip", "ns_gemm.hip", "adamw.hip"]
+SOURCES = ["muon_api.hip", "momentum_apply.hip", "ns_gemm.hip", "adamw.hip", "cayley.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -1,0 +1,453 @@
+// Muon-Cayley on the Stiefel manifold for gfx950 (fp32, with an fp64 2K x 2K solve).
+//
+// Method ([Muon在Stiefel流形上的精确闭式更新解析] mlqm.cn/news/1339166, sections
+// 1.3, 3.1-3.3 and 6.2), per matrix in its Stiefel frame W (N x K, N >= K,
+// W^T W = I):
+//   M' = beta M + (1 - beta) (G - 1 mean(G)^T)       (column-centered gradient, EMA)
+//   V  = M' - W sym(W^T M')                          (tangent projection)
+//   W' = (I + c A)^-1 (I - c A) W,  A = V W^T - W V^T,  c = lr / 2
+// The retraction goes through the 2K x 2K form: with U = [V, W], B = [W^T; -V^T]
+// (A = U B), C = I + c B U, B W = [W^T W; -V^T W] and Z = C^-1 (B W - c (B U)(B W)),
+// W' = W - c U (B W + Z).  Everything N-sized is then four passes:
+//   reduce1  W^T G, W^T M (K x K partials per row block) and column sums of G, W;
+//   mid      mean(G), S = sym(beta W^T M + (1 - beta)(W^T G - colsum(W) mean^T))
+//            (= sym(W^T M') by linearity, so M' needs no extra pass);
+//   p2       M' (in place) and V = M' - W S;
+//   reduce3  W^T W, W^T V, V^T V;
+//   solve    one workgroup per matrix: C and its right-hand side in fp64, LU with
+//            partial pivoting, Y = B W + Z;
+//   p4       W' = W - c (V Y1 + W Y2) into the workspace, copied out by `out`.
+// Wide matrices (rows < cols) are transposed into frame copies first and back at
+// the end.  Reductions over rows are split into row blocks summed in a fixed
+// order, so results are deterministic.
+#include "muon_internal.h"
+
+namespace muon {
+
+namespace {
+
+__device__ inline const CayleyDesc& cy_locate(const CayleyArgs& a, int t, int& local) {
+    const int mi = find_matrix(a.prefix, a.nmat, t);
+    local = t - a.prefix[mi];
+    return a.descs[mi];
+}
+
+// ---------------------------------------------------------------------------
+// Frame copies for wide matrices: frame (i, j) = caller (j, i)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(CY_THREADS) void cy_transpose_in(CayleyArgs a) {
+    __shared__ float tile[CY_T][CY_T + 1];
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const int i0 = (local / d.tk) * CY_T, j0 = (local % d.tk) * CY_T;
+    const float* src[3] = {d.w, d.g, d.m};
+    float* dst[3] = {d.wf, const_cast<float*>(d.gf), d.mf};
+    for (int x = 0; x < 3; ++x) {
+        for (int q = threadIdx.x; q < CY_T * CY_T; q += CY_THREADS) {
+            const int lr = q / CY_T, lc = q % CY_T;             // caller row j0 + lr, column i0 + lc
+            const int ur = j0 + lr, uc = i0 + lc;
+            tile[lr][lc] = (ur < d.K && uc < d.N) ? G(src[x])[static_cast<size_t>(ur) * d.cols + uc] : 0.0f;
+        }
+        __syncthreads();
+        for (int q = threadIdx.x; q < CY_T * CY_T; q += CY_THREADS) {
+            const int fr = q / CY_T, fc = q % CY_T;
+            const int i = i0 + fr, j = j0 + fc;
+            if (i < d.N && j < d.K) G(dst[x])[static_cast<size_t>(i) * d.K + j] = tile[fc][fr];
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K x K partial products over a row block: out_p[i][j] = sum_r X_p[r][i] Y_p[r][j]
+// 64 x 64 output tile, 256 threads with 4 x 4 outputs each.
+// ---------------------------------------------------------------------------
+template <int NP>
+__device__ void tn_block(const float* const (&X)[NP], const float* const (&Y)[NP], int K, int rs, int re,
+                         int i0, int j0, float* const (&out)[NP]) {
+    __shared__ float xs[NP][16][CY_T], ys[NP][16][CY_T];
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    float acc[NP][4][4];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[p][u][v] = 0.0f;
+    for (int r = rs; r < re; r += 16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int q = tid + CY_THREADS * e;
+            const int rr = q / CY_T, cc = q % CY_T;
+            const bool rok = r + rr < re;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const size_t row = static_cast<size_t>(r + rr) * K;
+                xs[p][rr][cc] = (rok && i0 + cc < K) ? G(X[p])[row + i0 + cc] : 0.0f;
+                ys[p][rr][cc] = (rok && j0 + cc < K) ? G(Y[p])[row + j0 + cc] : 0.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int rr = 0; rr < 16; ++rr) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                float xa[4], yb[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) { xa[u] = xs[p][rr][ty * 4 + u]; yb[u] = ys[p][rr][tx * 4 + u]; }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[p][u][v] = fmaf(xa[u], yb[v], acc[p][u][v]);
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = i0 + ty * 4 + u, j = j0 + tx * 4 + v;
+                if (i < K && j < K) G(out[p])[static_cast<size_t>(i) * K + j] = acc[p][u][v];
+            }
+}
+
+template <int PHASE>
+__global__ __launch_bounds__(CY_THREADS) void cy_reduce(CayleyArgs a) {
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const int per = d.tk * d.tk;
+    const int rb = local / per, t2 = local % per;
+    const int i0 = (t2 / d.tk) * CY_T, j0 = (t2 % d.tk) * CY_T;
+    const int rs = rb * CY_RB, re = min(d.N, rs + CY_RB);
+    const size_t kk = static_cast<size_t>(d.K) * d.K;
+    float* base = d.part + static_cast<size_t>(rb) * 3 * kk;
+    if (PHASE == CY_REDUCE1) {
+        const float* const X[2] = {d.wf, d.wf};
+        const float* const Y[2] = {d.gf, d.mf};
+        float* const out[2] = {base, base + kk};
+        tn_block<2>(X, Y, d.K, rs, re, i0, j0, out);
+    } else {
+        const float* const X[3] = {d.wf, d.wf, d.v};
+        const float* const Y[3] = {d.wf, d.v, d.v};
+        float* const out[3] = {base, base + kk, base + 2 * kk};
+        tn_block<3>(X, Y, d.K, rs, re, i0, j0, out);
+    }
+}
+
+// column sums of G and W over a row block (thread j owns column j)
+__global__ __launch_bounds__(CY_THREADS) void cy_colsum(CayleyArgs a) {
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const int rb = local, j = threadIdx.x;
+    if (j >= d.K) return;
+    const int rs = rb * CY_RB, re = min(d.N, rs + CY_RB);
+    float sg = 0.0f, sw = 0.0f;
+    for (int r = rs; r < re; ++r) {
+        const size_t idx = static_cast<size_t>(r) * d.K + j;
+        sg += G(d.gf)[idx];
+        sw += G(d.wf)[idx];
+    }
+    G(d.colpart)[(static_cast<size_t>(rb) * 2 + 0) * d.K + j] = sg;
+    G(d.colpart)[(static_cast<size_t>(rb) * 2 + 1) * d.K + j] = sw;
+}
+
+// mean(G) and S = sym(beta W^T M + (1 - beta)(W^T G - colsum(W) mean^T)); one block per matrix
+__global__ __launch_bounds__(CY_THREADS) void cy_mid(CayleyArgs a) {
+    __shared__ float mean_s[CAYLEY_MAX_K], colw_s[CAYLEY_MAX_K];
+    const CayleyDesc& d = a.descs[blockIdx.x];
+    const int K = d.K;
+    const size_t kk = static_cast<size_t>(K) * K;
+    for (int j = threadIdx.x; j < K; j += CY_THREADS) {
+        float sg = 0.0f, sw = 0.0f;
+        for (int rb = 0; rb < d.nrb; ++rb) {
+            sg += G(d.colpart)[(static_cast<size_t>(rb) * 2 + 0) * K + j];
+            sw += G(d.colpart)[(static_cast<size_t>(rb) * 2 + 1) * K + j];
+        }
+        const float mean = sg / static_cast<float>(d.N);
+        mean_s[j] = mean;
+        colw_s[j] = sw;
+        G(d.small)[j] = mean;
+    }
+    __syncthreads();
+    const float beta = a.beta, omb = 1.0f - a.beta;
+    for (size_t q = threadIdx.x; q < kk; q += CY_THREADS) {
+        const int i = static_cast<int>(q / K), j = static_cast<int>(q % K);
+        float gij = 0.0f, mij = 0.0f, gji = 0.0f, mji = 0.0f;
+        for (int rb = 0; rb < d.nrb; ++rb) {
+            const float* pr = d.part + static_cast<size_t>(rb) * 3 * kk;
+            gij += G(pr)[static_cast<size_t>(i) * K + j];
+            mij += G(pr)[kk + static_cast<size_t>(i) * K + j];
+            gji += G(pr)[static_cast<size_t>(j) * K + i];
+            mji += G(pr)[kk + static_cast<size_t>(j) * K + i];
+        }
+        const float hij = fmaf(beta, mij, omb * (gij - colw_s[i] * mean_s[j]));
+        const float hji = fmaf(beta, mji, omb * (gji - colw_s[j] * mean_s[i]));
+        G(d.small)[K + q] = 0.5f * (hij + hji);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// N x K output tile (64 x 64) of A[., 0:Kr] B[0:Kr, .] accumulated into acc
+// (A row-major with lda, B row-major K-wide), 4 x 4 outputs per thread.
+// ---------------------------------------------------------------------------
+__device__ void nn_accumulate(const float* A, int lda, int N, const float* B, int K, int Kr, int r0, int c0,
+                              float (&acc)[4][4]) {
+    __shared__ float as[16][CY_T + 1], bs[16][CY_T];
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    for (int k0 = 0; k0 < Kr; k0 += 16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int q = tid + CY_THREADS * e;
+            {   // A tile: 64 rows x 16 columns, stored transposed
+                const int rr = q / 16, kc = q % 16;
+                const int r = r0 + rr, k = k0 + kc;
+                as[kc][rr] = (r < N && k < Kr) ? G(A)[static_cast<size_t>(r) * lda + k] : 0.0f;
+            }
+            {   // B tile: 16 rows x 64 columns
+                const int kr = q / CY_T, cc = q % CY_T;
+                const int k = k0 + kr, c = c0 + cc;
+                bs[kr][cc] = (k < Kr && c < K) ? G(B)[static_cast<size_t>(k) * K + c] : 0.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kc = 0; kc < 16; ++kc) {
+            float xa[4], yb[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) { xa[u] = as[kc][ty * 4 + u]; yb[u] = bs[kc][tx * 4 + u]; }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(xa[u], yb[v], acc[u][v]);
+        }
+        __syncthreads();
+    }
+}
+
+// M' = beta M + (1 - beta)(G - mean), in place; V = M' - W S
+__global__ __launch_bounds__(CY_THREADS) void cy_p2(CayleyArgs a) {
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const int r0 = (local / d.tk) * CY_T, c0 = (local % d.tk) * CY_T;
+    float acc[4][4] = {};
+    const float* S = d.small + d.K;
+    nn_accumulate(d.wf, d.K, d.N, S, d.K, d.K, r0, c0, acc);
+    const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+    const float beta = a.beta, omb = 1.0f - a.beta;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = r0 + ty * 4 + u, j = c0 + tx * 4 + v;
+            if (r < d.N && j < d.K) {
+                const size_t idx = static_cast<size_t>(r) * d.K + j;
+                const float mn = fmaf(beta, G(d.mf)[idx], omb * (G(d.gf)[idx] - G(d.small)[j]));
+                G(d.mf)[idx] = mn;
+                G(d.v)[idx] = mn - acc[u][v];
+            }
+        }
+}
+
+// W' = W - c (V Y1 + W Y2), into the workspace
+__global__ __launch_bounds__(CY_THREADS) void cy_p4(CayleyArgs a) {
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const int r0 = (local / d.tk) * CY_T, c0 = (local % d.tk) * CY_T;
+    const size_t kk = static_cast<size_t>(d.K) * d.K;
+    const float* Y = d.small + d.K + kk;
+    float acc[4][4] = {};
+    nn_accumulate(d.v, d.K, d.N, Y, d.K, d.K, r0, c0, acc);
+    nn_accumulate(d.wf, d.K, d.N, Y + kk, d.K, d.K, r0, c0, acc);
+    const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = r0 + ty * 4 + u, j = c0 + tx * 4 + v;
+            if (r < d.N && j < d.K) {
+                const size_t idx = static_cast<size_t>(r) * d.K + j;
+                G(d.wnew)[idx] = fmaf(-a.c, acc[u][v], G(d.wf)[idx]);
+            }
+        }
+}
+
+// caller's W (and, for wide matrices, M) from the frame
+__global__ __launch_bounds__(CY_THREADS) void cy_out(CayleyArgs a) {
+    __shared__ float tile[CY_T][CY_T + 1];
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const int i0 = (local / d.tk) * CY_T, j0 = (local % d.tk) * CY_T;
+    if (d.tall) {
+        for (int q = threadIdx.x; q < CY_T * CY_T; q += CY_THREADS) {
+            const int i = i0 + q / CY_T, j = j0 + q % CY_T;
+            if (i < d.N && j < d.K) {
+                const size_t idx = static_cast<size_t>(i) * d.K + j;
+                G(d.w)[idx] = G(d.wnew)[idx];
+            }
+        }
+        return;
+    }
+    const float* src[2] = {d.wnew, d.mf};
+    float* dst[2] = {d.w, d.m};
+    for (int x = 0; x < 2; ++x) {
+        for (int q = threadIdx.x; q < CY_T * CY_T; q += CY_THREADS) {
+            const int fr = q / CY_T, fc = q % CY_T;
+            const int i = i0 + fr, j = j0 + fc;
+            tile[fr][fc] = (i < d.N && j < d.K) ? G(src[x])[static_cast<size_t>(i) * d.K + j] : 0.0f;
+        }
+        __syncthreads();
+        for (int q = threadIdx.x; q < CY_T * CY_T; q += CY_THREADS) {
+            const int lr = q / CY_T, lc = q % CY_T;    // caller row j0 + lr, column i0 + lc
+            const int ur = j0 + lr, uc = i0 + lc;
+            if (ur < d.K && uc < d.N) G(dst[x])[static_cast<size_t>(ur) * d.cols + uc] = tile[lc][lr];
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The 2K x 2K solve, one workgroup per matrix, fp64.
+// ---------------------------------------------------------------------------
+__device__ inline void block_argmax(double v, int idx, double* rv, int* ri, double& bv, int& bi) {
+    // v, idx: this thread's candidate; largest |value|, smallest index on ties
+    const int tid = threadIdx.x;
+    rv[tid] = v;
+    ri[tid] = idx;
+    __syncthreads();
+    for (int off = CY_SOLVE_THREADS / 2; off > 0; off >>= 1) {
+        if (tid < off) {
+            const double a = rv[tid], b = rv[tid + off];
+            const int ia = ri[tid], ib = ri[tid + off];
+            if (b > a || (b == a && ib < ia)) { rv[tid] = b; ri[tid] = ib; }
+        }
+        __syncthreads();
+    }
+    bv = rv[0];
+    bi = ri[0];
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
+    __shared__ double rv[CY_SOLVE_THREADS];
+    __shared__ int ri[CY_SOLVE_THREADS];
+    const CayleyDesc& d = a.descs[blockIdx.x];
+    const int K = d.K, K2 = 2 * K, tid = threadIdx.x;
+    const size_t kk = static_cast<size_t>(K) * K;
+    const double c = a.c;
+    double* C = d.cmat;       // 2K x 2K
+    double* R = d.rhs;        // 2K x K
+    double* BW = d.bw;        // 2K x K
+    // 1. K x K products from the partials: W^T W, W^T V, V^T V (fp64 sums in row-block order)
+    for (size_t q = tid; q < kk; q += CY_SOLVE_THREADS) {
+        const int i = static_cast<int>(q / K), j = static_cast<int>(q % K);
+        double ww = 0.0, wv = 0.0, vw = 0.0, vv = 0.0;   // (W^T W)ij, (W^T V)ij, (W^T V)ji, (V^T V)ij
+        for (int rb = 0; rb < d.nrb; ++rb) {
+            const float* pr = d.part + static_cast<size_t>(rb) * 3 * kk;
+            ww += G(pr)[q];
+            wv += G(pr)[kk + q];
+            vw += G(pr)[kk + static_cast<size_t>(j) * K + i];
+            vv += G(pr)[2 * kk + q];
+        }
+        // B U = [[W^T V, W^T W], [-V^T V, -V^T W]], with (V^T W)ij = (W^T V)ji
+        C[static_cast<size_t>(i) * K2 + j] = wv;
+        C[static_cast<size_t>(i) * K2 + K + j] = ww;
+        C[static_cast<size_t>(K + i) * K2 + j] = -vv;
+        C[static_cast<size_t>(K + i) * K2 + K + j] = -vw;
+        BW[static_cast<size_t>(i) * K + j] = ww;
+        BW[static_cast<size_t>(K + i) * K + j] = -vw;
+    }
+    __syncthreads();
+    // 2. right-hand side B (I - c A) W = B W - c (B U)(B W)
+    for (size_t q = tid; q < static_cast<size_t>(K2) * K; q += CY_SOLVE_THREADS) {
+        const int i = static_cast<int>(q / K), j = static_cast<int>(q % K);
+        double s = 0.0;
+        for (int l = 0; l < K2; ++l) s = fma(C[static_cast<size_t>(i) * K2 + l], BW[static_cast<size_t>(l) * K + j], s);
+        R[q] = BW[q] - c * s;
+    }
+    __syncthreads();
+    // 3. C = I + c B U
+    for (size_t q = tid; q < static_cast<size_t>(K2) * K2; q += CY_SOLVE_THREADS) {
+        const int i = static_cast<int>(q / K2), l = static_cast<int>(q % K2);
+        C[q] = (i == l ? 1.0 : 0.0) + c * C[q];
+    }
+    __syncthreads();
+    // 4. LU with partial pivoting, applied to the right-hand side
+    for (int j = 0; j < K2; ++j) {
+        double best = -1.0;
+        int bidx = K2;
+        for (int i = j + tid; i < K2; i += CY_SOLVE_THREADS) {
+            const double v = fabs(C[static_cast<size_t>(i) * K2 + j]);
+            if (v > best) { best = v; bidx = i; }
+        }
+        double bv;
+        int p;
+        block_argmax(best, bidx, rv, ri, bv, p);
+        if (p != j) {
+            for (int col = j + tid; col < K2; col += CY_SOLVE_THREADS) {
+                const double t = C[static_cast<size_t>(j) * K2 + col];
+                C[static_cast<size_t>(j) * K2 + col] = C[static_cast<size_t>(p) * K2 + col];
+                C[static_cast<size_t>(p) * K2 + col] = t;
+            }
+            for (int col = tid; col < K; col += CY_SOLVE_THREADS) {
+                const double t = R[static_cast<size_t>(j) * K + col];
+                R[static_cast<size_t>(j) * K + col] = R[static_cast<size_t>(p) * K + col];
+                R[static_cast<size_t>(p) * K + col] = t;
+            }
+        }
+        __syncthreads();
+        const double piv = C[static_cast<size_t>(j) * K2 + j];
+        const int rows = K2 - j - 1, wc = K2 - j - 1, width = wc + K;
+        for (size_t q = tid; q < static_cast<size_t>(rows) * width; q += CY_SOLVE_THREADS) {
+            const int i = j + 1 + static_cast<int>(q / width), col = static_cast<int>(q % width);
+            const double l = C[static_cast<size_t>(i) * K2 + j] / piv;
+            if (col < wc) {
+                const int cc = j + 1 + col;
+                C[static_cast<size_t>(i) * K2 + cc] -= l * C[static_cast<size_t>(j) * K2 + cc];
+            } else {
+                const int cc = col - wc;
+                R[static_cast<size_t>(i) * K + cc] -= l * R[static_cast<size_t>(j) * K + cc];
+            }
+        }
+        __syncthreads();
+    }
+    // 5. back substitution
+    for (int j = K2 - 1; j >= 0; --j) {
+        const double piv = C[static_cast<size_t>(j) * K2 + j];
+        for (int col = tid; col < K; col += CY_SOLVE_THREADS) R[static_cast<size_t>(j) * K + col] /= piv;
+        __syncthreads();
+        for (size_t q = tid; q < static_cast<size_t>(j) * K; q += CY_SOLVE_THREADS) {
+            const int i = static_cast<int>(q / K), col = static_cast<int>(q % K);
+            R[static_cast<size_t>(i) * K + col] -= C[static_cast<size_t>(i) * K2 + j] * R[static_cast<size_t>(j) * K + col];
+        }
+        __syncthreads();
+    }
+    // 6. Y = B W + Z, fp32 for the final pass
+    float* Y = d.small + K + kk;
+    for (size_t q = tid; q < static_cast<size_t>(K2) * K; q += CY_SOLVE_THREADS)
+        G(Y)[q] = static_cast<float>(BW[q] + R[q]);
+}
+
+}  // namespace
+
+hipError_t launch_cayley(int phase, const CayleyArgs& args, hipStream_t s) {
+    if (args.total <= 0) return hipSuccess;
+    const dim3 grid(args.total), block(CY_THREADS);
+    switch (phase) {
+        case CY_TRANSPOSE_IN: hipLaunchKernelGGL(cy_transpose_in, grid, block, 0, s, args); break;
+        case CY_REDUCE1: hipLaunchKernelGGL(cy_reduce<CY_REDUCE1>, grid, block, 0, s, args); break;
+        case CY_COLSUM: hipLaunchKernelGGL(cy_colsum, grid, block, 0, s, args); break;
+        case CY_MID: hipLaunchKernelGGL(cy_mid, grid, block, 0, s, args); break;
+        case CY_P2: hipLaunchKernelGGL(cy_p2, grid, block, 0, s, args); break;
+        case CY_REDUCE3: hipLaunchKernelGGL(cy_reduce<CY_REDUCE3>, grid, block, 0, s, args); break;
+        case CY_SOLVE: hipLaunchKernelGGL(cy_solve, grid, dim3(CY_SOLVE_THREADS), 0, s, args); break;
+        case CY_P4: hipLaunchKernelGGL(cy_p4, grid, block, 0, s, args); break;
+        case CY_OUT: hipLaunchKernelGGL(cy_out, grid, block, 0, s, args); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace muon

@@ -572,6 +572,123 @@ muon_status collect_adamw(const muon_adamw_tensor* ts, int32_t n, const muon_ada
     return check_overlaps(iv);
 }
 
+// ---------------------------------------------------------------------------
+// Muon-Cayley
+// ---------------------------------------------------------------------------
+
+constexpr int CY_PHASES = 9;
+
+struct CayleyPlan {
+    std::vector<CayleyDesc> descs;
+    std::vector<int32_t> prefix[CY_PHASES];
+    size_t off_prefix = 0, header_bytes = 0, total_bytes = 0;
+};
+
+muon_status collect_cayley(const muon_cayley_matrix* mats, int32_t n, const muon_cayley_hparams* hp,
+                           std::vector<CayleyDesc>& out) {
+    if (n < 0 || n > MUON_MAX_MATRICES) return fail(MUON_ERR_INVALID_ARG, "n = %d outside [0, %d]", n, MUON_MAX_MATRICES);
+    if (n > 0 && !mats) return fail(MUON_ERR_INVALID_ARG, "mats is NULL");
+    if (!hp) return fail(MUON_ERR_INVALID_ARG, "hp is NULL");
+    if (!std::isfinite(hp->lr)) return fail(MUON_ERR_INVALID_ARG, "lr is not finite");
+    if (!(hp->beta >= 0.0f && hp->beta < 1.0f)) return fail(MUON_ERR_INVALID_ARG, "beta must lie in [0, 1)");
+    std::vector<Interval> iv;
+    for (int i = 0; i < n; ++i) {
+        const muon_cayley_matrix& m = mats[i];
+        if (!m.grad) continue;
+        if (m.rows < 1 || m.cols < 1 || m.rows > MUON_MAX_DIM || m.cols > MUON_MAX_DIM)
+            return fail(MUON_ERR_INVALID_ARG, "matrix %d has shape %lld x %lld", i, (long long)m.rows, (long long)m.cols);
+        if (std::min(m.rows, m.cols) > MUON_CAYLEY_MAX_K)
+            return fail(MUON_ERR_UNSUPPORTED, "matrix %d: min(rows, cols) = %lld exceeds %d", i,
+                        (long long)std::min(m.rows, m.cols), MUON_CAYLEY_MAX_K);
+        if (!m.weight || !m.momentum) return fail(MUON_ERR_INVALID_ARG, "matrix %d: weight or momentum is NULL", i);
+        const uintptr_t pw = reinterpret_cast<uintptr_t>(m.weight), pg = reinterpret_cast<uintptr_t>(m.grad),
+                        pm = reinterpret_cast<uintptr_t>(m.momentum);
+        if (pw % 4 || pg % 4 || pm % 4) return fail(MUON_ERR_INVALID_ARG, "matrix %d: misaligned pointer", i);
+        const size_t bytes = static_cast<size_t>(m.rows) * static_cast<size_t>(m.cols) * 4;
+        iv.push_back({pw, pw + bytes, false, i});
+        iv.push_back({pm, pm + bytes, false, i});
+        iv.push_back({pg, pg + bytes, true, i});
+        CayleyDesc d{};
+        d.w = m.weight;
+        d.g = m.grad;
+        d.m = m.momentum;
+        d.rows = static_cast<int32_t>(m.rows);
+        d.cols = static_cast<int32_t>(m.cols);
+        d.tall = m.rows >= m.cols ? 1 : 0;
+        d.N = static_cast<int32_t>(std::max(m.rows, m.cols));
+        d.K = static_cast<int32_t>(std::min(m.rows, m.cols));
+        d.nrb = (d.N + CY_RB - 1) / CY_RB;
+        d.tk = (d.K + CY_T - 1) / CY_T;
+        d.tn = (d.N + CY_T - 1) / CY_T;
+        out.push_back(d);
+    }
+    return check_overlaps(iv);
+}
+
+muon_status build_cayley_plan(std::vector<CayleyDesc>& descs, CayleyPlan& pl) {
+    const size_t nmat = descs.size();
+    size_t off = align_up(sizeof(CayleyDesc) * nmat, ALIGN);
+    pl.off_prefix = off;
+    off = align_up(off + sizeof(int32_t) * CY_PHASES * (nmat + 1), ALIGN);
+    pl.header_bytes = off;
+    for (int ph = 0; ph < CY_PHASES; ++ph) pl.prefix[ph].assign(nmat + 1, 0);
+    int64_t tot[CY_PHASES] = {};
+    for (size_t k = 0; k < nmat; ++k) {
+        CayleyDesc& d = descs[k];
+        const int64_t tiles = static_cast<int64_t>(d.tn) * d.tk, red = static_cast<int64_t>(d.nrb) * d.tk * d.tk;
+        const int64_t per[CY_PHASES] = {d.tall ? 0 : tiles, red, d.nrb, 1, tiles, red, 1, tiles, tiles};
+        for (int ph = 0; ph < CY_PHASES; ++ph) {
+            tot[ph] += per[ph];
+            if (tot[ph] > INT32_MAX) return fail(MUON_ERR_UNSUPPORTED, "too many tiles in one call (split the list)");
+            pl.prefix[ph][k + 1] = static_cast<int32_t>(tot[ph]);
+        }
+        const size_t nk = static_cast<size_t>(d.N) * d.K * 4, kk = static_cast<size_t>(d.K) * d.K;
+        auto take = [&](size_t bytes) { const size_t at = off; off = align_up(off + bytes, ALIGN); return at; };
+        if (d.tall) {
+            d.wf = d.w;
+            d.gf = d.g;
+            d.mf = d.m;
+        } else {
+            d.wf = reinterpret_cast<float*>(take(nk));
+            d.gf = reinterpret_cast<const float*>(take(nk));
+            d.mf = reinterpret_cast<float*>(take(nk));
+        }
+        d.v = reinterpret_cast<float*>(take(nk));
+        d.wnew = reinterpret_cast<float*>(take(nk));
+        d.part = reinterpret_cast<float*>(take(static_cast<size_t>(d.nrb) * 3 * kk * 4));
+        d.colpart = reinterpret_cast<float*>(take(static_cast<size_t>(d.nrb) * 2 * d.K * 4));
+        d.small = reinterpret_cast<float*>(take((d.K + kk + 2 * kk) * 4));
+        d.cmat = reinterpret_cast<double*>(take(4 * kk * 8));
+        d.rhs = reinterpret_cast<double*>(take(2 * kk * 8));
+        d.bw = reinterpret_cast<double*>(take(2 * kk * 8));
+    }
+    pl.total_bytes = off;
+    pl.descs = descs;
+    return MUON_OK;
+}
+
+void rebase_cayley(CayleyPlan& pl, char* base) {
+    auto fix = [base](auto*& p) {
+        using P = std::remove_reference_t<decltype(p)>;
+        p = reinterpret_cast<P>(base + reinterpret_cast<uintptr_t>(p));
+    };
+    for (CayleyDesc& d : pl.descs) {
+        if (!d.tall) {
+            fix(d.wf);
+            fix(d.gf);
+            fix(d.mf);
+        }
+        fix(d.v);
+        fix(d.wnew);
+        fix(d.part);
+        fix(d.colpart);
+        fix(d.small);
+        fix(d.cmat);
+        fix(d.rhs);
+        fix(d.bw);
+    }
+}
+
 size_t adamw_header_bytes(size_t n) {
     return align_up(align_up(sizeof(AdamWDesc) * n, ALIGN) + sizeof(int32_t) * (n + 1), ALIGN);
 }
@@ -579,6 +696,70 @@ size_t adamw_header_bytes(size_t n) {
 }  // namespace
 
 extern "C" {
+
+size_t muon_cayley_workspace_bytes(const muon_cayley_matrix* mats, int32_t n, const muon_cayley_hparams* hp) {
+    std::vector<CayleyDesc> descs;
+    if (collect_cayley(mats, n, hp, descs) != MUON_OK) return 0;
+    if (descs.empty()) return ALIGN;
+    CayleyPlan pl;
+    if (build_cayley_plan(descs, pl) != MUON_OK) return 0;
+    return pl.total_bytes;
+}
+
+muon_status muon_cayley_step(const muon_cayley_matrix* mats, int32_t n, const muon_cayley_hparams* hp,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    std::vector<CayleyDesc> descs;
+    muon_status st = collect_cayley(mats, n, hp, descs);
+    if (st != MUON_OK) return st;
+    if (descs.empty()) { g_last_error.clear(); return MUON_OK; }
+    CayleyPlan pl;
+    st = build_cayley_plan(descs, pl);
+    if (st != MUON_OK) return st;
+    if (!workspace) return fail(MUON_ERR_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) % ALIGN)
+        return fail(MUON_ERR_WORKSPACE, "workspace is not %zu-byte aligned", ALIGN);
+    if (workspace_bytes < pl.total_bytes)
+        return fail(MUON_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, pl.total_bytes);
+    {
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(workspace), hi = lo + pl.total_bytes;
+        for (const CayleyDesc& d : pl.descs) {
+            const size_t bytes = static_cast<size_t>(d.rows) * d.cols * 4;
+            const void* ptrs[3] = {d.w, d.g, d.m};
+            for (int q = 0; q < 3; ++q) {
+                const uintptr_t p = reinterpret_cast<uintptr_t>(ptrs[q]);
+                if (p < hi && p + bytes > lo) return fail(MUON_ERR_INVALID_ARG, "a matrix overlaps the workspace");
+            }
+        }
+    }
+    int dev = 0, cu_count = 0;
+    st = check_device(&dev, &cu_count);
+    if (st != MUON_OK) return st;
+    char* base = static_cast<char*>(workspace);
+    rebase_cayley(pl, base);
+    const size_t nmat = pl.descs.size();
+    std::vector<char> header(pl.header_bytes, 0);
+    std::memcpy(header.data(), pl.descs.data(), sizeof(CayleyDesc) * nmat);
+    for (int ph = 0; ph < CY_PHASES; ++ph)
+        std::memcpy(header.data() + pl.off_prefix + sizeof(int32_t) * ph * (nmat + 1), pl.prefix[ph].data(),
+                    sizeof(int32_t) * (nmat + 1));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = upload(dev, workspace, header.data(), header.size(), s);
+    if (st != MUON_OK) return st;
+    CayleyArgs a{};
+    a.descs = reinterpret_cast<const CayleyDesc*>(base);
+    a.nmat = static_cast<int32_t>(nmat);
+    a.beta = hp->beta;
+    a.c = 0.5f * hp->lr;
+    const int order[CY_PHASES] = {CY_TRANSPOSE_IN, CY_REDUCE1, CY_COLSUM, CY_MID, CY_P2, CY_REDUCE3, CY_SOLVE, CY_P4, CY_OUT};
+    for (int ph : order) {
+        a.prefix = reinterpret_cast<const int32_t*>(base + pl.off_prefix + sizeof(int32_t) * ph * (nmat + 1));
+        a.total = pl.prefix[ph][nmat];
+        st = timed_launch(7, s, "Muon-Cayley kernel", [&] { return launch_cayley(ph, a, s); });
+        if (st != MUON_OK) return st;
+    }
+    g_last_error.clear();
+    return MUON_OK;
+}
 
 size_t muon_adamw_workspace_bytes(const muon_adamw_tensor* tensors, int32_t n, const muon_adamw_hparams* hp) {
     std::vector<AdamWDesc> descs;

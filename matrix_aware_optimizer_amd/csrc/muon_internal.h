@@ -101,7 +101,49 @@ struct AdamWArgs {
     float inv_sqrt_bc2;      // 1 / sqrt(1 - beta2^t)
 };
 
+// Muon-Cayley.  Each matrix is handled in its Stiefel frame N x K (N >= K,
+// row-major fp32): the caller's matrix when rows >= cols, its transpose
+// otherwise.  K x K reductions over N are split into row blocks of CY_RB rows
+// whose partials are summed in a fixed order.
+constexpr int CAYLEY_MAX_K = 256;
+constexpr int CY_T = 64;          // output tile edge of the small GEMMs and K x K products
+constexpr int CY_RB = 512;        // rows per reduction block
+constexpr int CY_THREADS = 256;
+constexpr int CY_SOLVE_THREADS = 1024;
+struct CayleyDesc {
+    float* w;            // caller's weight (rows x cols)
+    const float* g;      // caller's gradient
+    float* m;            // caller's momentum
+    int32_t rows, cols;
+    int32_t N, K;        // Stiefel frame
+    int32_t tall;        // 1: frame = caller's layout; 0: frame = transpose (copies below)
+    int32_t nrb;         // reduction row blocks
+    int32_t tk;          // K tiles per side: ceil(K / CY_T)
+    int32_t tn;          // N tiles: ceil(N / CY_T)
+    float* wf;           // frame W (caller's buffer when tall)
+    const float* gf;     // frame G
+    float* mf;           // frame M, updated in place
+    float* v;            // N x K tangent direction
+    float* wnew;         // N x K updated W (frame)
+    float* part;         // nrb x 3 x K x K partial products
+    float* colpart;      // nrb x 2 x K partial column sums (G, W)
+    float* small;        // K (mean) + K x K (S) + 2K x K (Y)
+    double* cmat;        // 2K x 2K: B U, then the system I + c B U, then its LU factors
+    double* rhs;         // 2K x K right-hand side, then the solution Z
+    double* bw;          // 2K x K: B W = [W^T W; -V^T W]
+};
+struct CayleyArgs {
+    const CayleyDesc* descs;
+    const int32_t* prefix;   // nmat + 1 prefix sums of this phase's tiles
+    int32_t nmat;
+    int32_t total;
+    float beta, c;           // momentum coefficient, c = lr / 2
+};
+
 // Kernel launchers (defined next to the kernels).
+enum CayleyPhase : int32_t { CY_TRANSPOSE_IN = 0, CY_REDUCE1 = 1, CY_COLSUM = 2, CY_MID = 3, CY_P2 = 4,
+                             CY_REDUCE3 = 5, CY_SOLVE = 6, CY_P4 = 7, CY_OUT = 8 };
+hipError_t launch_cayley(int phase, const CayleyArgs& args, hipStream_t s);
 hipError_t launch_adamw(int dtype, const AdamWArgs& args, int grid, hipStream_t s);
 hipError_t launch_momentum_norm(int dtype, bool ns_only, const EwArgs& args, int grid, hipStream_t s);
 hipError_t launch_norm_finalize(const MatDesc* descs, const float* partials, int nmat, float eps,

@@ -256,3 +256,25 @@ def adamw_host_tensors(sizes, dtype="bf16", seed=0, step=1):
             v = np.zeros(n, np.float32)
         out.append({"p": p, "g": g, "m": m, "v": v})
     return out
+
+
+# --------------------------------------------------------------------------
+# Muon-Cayley inputs (points on the Stiefel manifold).
+# --------------------------------------------------------------------------
+
+def cayley_host_matrix(rows, cols, seed=0, grad_std=1e-2, momentum_std=1e-2):
+    """Seeded float32 W with orthonormal columns (orthonormal rows when rows < cols),
+    taken from the QR factor of a Gaussian draw, and Gaussian G and M."""
+    rng = np.random.default_rng([7000 + seed, rows, cols])
+    n, k = max(rows, cols), min(rows, cols)
+    q, r = np.linalg.qr(rng.standard_normal((n, k)))
+    q = q * np.sign(np.diag(r))
+    W = q if rows >= cols else q.T
+    G = grad_std * rng.standard_normal((rows, cols))
+    M = momentum_std * rng.standard_normal((rows, cols))
+    return {"W": np.ascontiguousarray(W, np.float32), "G": G.astype(np.float32), "M": M.astype(np.float32)}
+
+
+CAYLEY_SET = [(4096, 128)] * 32
+"""Timing workload for the Muon-Cayley row: 32 matrices of 4096 x 128 (the Stiefel
+page discusses a hidden size of 4096 with k much smaller than n)."""

@@ -311,28 +311,11 @@ __global__ __launch_bounds__(CY_THREADS) void cy_out(CayleyArgs a) {
 // ---------------------------------------------------------------------------
 // The 2K x 2K solve, one workgroup per matrix, fp64.
 // ---------------------------------------------------------------------------
-__device__ inline void block_argmax(double v, int idx, double* rv, int* ri, double& bv, int& bi) {
-    // v, idx: this thread's candidate; largest |value|, smallest index on ties
-    const int tid = threadIdx.x;
-    rv[tid] = v;
-    ri[tid] = idx;
-    __syncthreads();
-    for (int off = CY_SOLVE_THREADS / 2; off > 0; off >>= 1) {
-        if (tid < off) {
-            const double a = rv[tid], b = rv[tid + off];
-            const int ia = ri[tid], ib = ri[tid + off];
-            if (b > a || (b == a && ib < ia)) { rv[tid] = b; ri[tid] = ib; }
-        }
-        __syncthreads();
-    }
-    bv = rv[0];
-    bi = ri[0];
-    __syncthreads();
-}
-
 __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
-    __shared__ double rv[CY_SOLVE_THREADS];
-    __shared__ int ri[CY_SOLVE_THREADS];
+    __shared__ int perm[2 * CAYLEY_MAX_K];
+    __shared__ double prow[3 * CAYLEY_MAX_K];     // pivot row of C (from column j) and of the right-hand side
+    __shared__ double lmul[2 * CAYLEY_MAX_K];     // multipliers of the rows below the pivot
+    __shared__ double ta[32][33], tb[32][33];     // tiles of the right-hand-side product
     const CayleyDesc& d = a.descs[blockIdx.x];
     const int K = d.K, K2 = 2 * K, tid = threadIdx.x;
     const size_t kk = static_cast<size_t>(K) * K;
@@ -360,12 +343,24 @@ __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
         BW[static_cast<size_t>(K + i) * K + j] = -vw;
     }
     __syncthreads();
-    // 2. right-hand side B (I - c A) W = B W - c (B U)(B W)
-    for (size_t q = tid; q < static_cast<size_t>(K2) * K; q += CY_SOLVE_THREADS) {
-        const int i = static_cast<int>(q / K), j = static_cast<int>(q % K);
-        double s = 0.0;
-        for (int l = 0; l < K2; ++l) s = fma(C[static_cast<size_t>(i) * K2 + l], BW[static_cast<size_t>(l) * K + j], s);
-        R[q] = BW[q] - c * s;
+    // 2. right-hand side B W - c (B U)(B W), 32 x 32 output tiles through LDS
+    {
+        const int ty = tid / 32, tx = tid % 32;
+        for (int r0 = 0; r0 < K2; r0 += 32)
+            for (int c0 = 0; c0 < K; c0 += 32) {
+                double acc = 0.0;
+                for (int l0 = 0; l0 < K2; l0 += 32) {
+                    const int ar = r0 + ty, al = l0 + tx, bl = l0 + ty, bc = c0 + tx;
+                    ta[ty][tx] = (ar < K2 && al < K2) ? C[static_cast<size_t>(ar) * K2 + al] : 0.0;
+                    tb[ty][tx] = (bl < K2 && bc < K) ? BW[static_cast<size_t>(bl) * K + bc] : 0.0;
+                    __syncthreads();
+#pragma unroll 8
+                    for (int l = 0; l < 32; ++l) acc = fma(ta[ty][l], tb[l][tx], acc);
+                    __syncthreads();
+                }
+                const int r = r0 + ty, cc = c0 + tx;
+                if (r < K2 && cc < K) R[static_cast<size_t>(r) * K + cc] = BW[static_cast<size_t>(r) * K + cc] - c * acc;
+            }
     }
     __syncthreads();
     // 3. C = I + c B U
@@ -373,61 +368,74 @@ __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
         const int i = static_cast<int>(q / K2), l = static_cast<int>(q % K2);
         C[q] = (i == l ? 1.0 : 0.0) + c * C[q];
     }
+    for (int i = tid; i < K2; i += CY_SOLVE_THREADS) perm[i] = i;
     __syncthreads();
-    // 4. LU with partial pivoting, applied to the right-hand side
+    // 4. LU with partial pivoting, applied to the right-hand side.  Rows stay in
+    //    place: perm[i] is the stored row that plays the role of row i.  Per
+    //    column: one wave finds the pivot; the pivot row and the multipliers go
+    //    to LDS; every thread then updates its elements with one load and one store.
     for (int j = 0; j < K2; ++j) {
-        double best = -1.0;
-        int bidx = K2;
-        for (int i = j + tid; i < K2; i += CY_SOLVE_THREADS) {
-            const double v = fabs(C[static_cast<size_t>(i) * K2 + j]);
-            if (v > best) { best = v; bidx = i; }
-        }
-        double bv;
-        int p;
-        block_argmax(best, bidx, rv, ri, bv, p);
-        if (p != j) {
-            for (int col = j + tid; col < K2; col += CY_SOLVE_THREADS) {
-                const double t = C[static_cast<size_t>(j) * K2 + col];
-                C[static_cast<size_t>(j) * K2 + col] = C[static_cast<size_t>(p) * K2 + col];
-                C[static_cast<size_t>(p) * K2 + col] = t;
+        if (tid < 64) {
+            double best = -1.0;
+            int bidx = K2;
+            for (int i = j + tid; i < K2; i += 64) {
+                const double v = fabs(C[static_cast<size_t>(perm[i]) * K2 + j]);
+                if (v > best) { best = v; bidx = i; }
             }
-            for (int col = tid; col < K; col += CY_SOLVE_THREADS) {
-                const double t = R[static_cast<size_t>(j) * K + col];
-                R[static_cast<size_t>(j) * K + col] = R[static_cast<size_t>(p) * K + col];
-                R[static_cast<size_t>(p) * K + col] = t;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const double ov = __shfl_xor(best, off, 64);
+                const int oi = __shfl_xor(bidx, off, 64);
+                if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+            }
+            if (tid == 0 && bidx != j) {
+                const int t = perm[j];
+                perm[j] = perm[bidx];
+                perm[bidx] = t;
             }
         }
         __syncthreads();
-        const double piv = C[static_cast<size_t>(j) * K2 + j];
-        const int rows = K2 - j - 1, wc = K2 - j - 1, width = wc + K;
+        const size_t pj = static_cast<size_t>(perm[j]);
+        const int wc = K2 - j - 1, width = wc + K, rows = K2 - j - 1;
+        for (int col = tid; col < width; col += CY_SOLVE_THREADS)
+            prow[col] = col < wc ? C[pj * K2 + j + 1 + col] : R[pj * K + (col - wc)];
+        {
+            const double piv = C[pj * K2 + j];
+            for (int i = tid; i < rows; i += CY_SOLVE_THREADS)
+                lmul[i] = C[static_cast<size_t>(perm[j + 1 + i]) * K2 + j] / piv;
+        }
+        __syncthreads();
         for (size_t q = tid; q < static_cast<size_t>(rows) * width; q += CY_SOLVE_THREADS) {
-            const int i = j + 1 + static_cast<int>(q / width), col = static_cast<int>(q % width);
-            const double l = C[static_cast<size_t>(i) * K2 + j] / piv;
-            if (col < wc) {
-                const int cc = j + 1 + col;
-                C[static_cast<size_t>(i) * K2 + cc] -= l * C[static_cast<size_t>(j) * K2 + cc];
-            } else {
-                const int cc = col - wc;
-                R[static_cast<size_t>(i) * K + cc] -= l * R[static_cast<size_t>(j) * K + cc];
-            }
+            const int ii = static_cast<int>(q / width), col = static_cast<int>(q % width);
+            const size_t pi = static_cast<size_t>(perm[j + 1 + ii]);
+            double* dst = col < wc ? &C[pi * K2 + j + 1 + col] : &R[pi * K + (col - wc)];
+            *dst -= lmul[ii] * prow[col];
         }
         __syncthreads();
     }
-    // 5. back substitution
+    // 5. back substitution by columns of U: the solution for row j goes to row perm[j]
     for (int j = K2 - 1; j >= 0; --j) {
-        const double piv = C[static_cast<size_t>(j) * K2 + j];
-        for (int col = tid; col < K; col += CY_SOLVE_THREADS) R[static_cast<size_t>(j) * K + col] /= piv;
+        const size_t pj = static_cast<size_t>(perm[j]);
+        const double piv = C[pj * K2 + j];
+        for (int col = tid; col < K; col += CY_SOLVE_THREADS) {
+            const double x = R[pj * K + col] / piv;
+            R[pj * K + col] = x;
+            prow[col] = x;
+        }
         __syncthreads();
         for (size_t q = tid; q < static_cast<size_t>(j) * K; q += CY_SOLVE_THREADS) {
             const int i = static_cast<int>(q / K), col = static_cast<int>(q % K);
-            R[static_cast<size_t>(i) * K + col] -= C[static_cast<size_t>(i) * K2 + j] * R[static_cast<size_t>(j) * K + col];
+            const size_t pi = static_cast<size_t>(perm[i]);
+            R[pi * K + col] -= C[pi * K2 + j] * prow[col];
         }
         __syncthreads();
     }
     // 6. Y = B W + Z, fp32 for the final pass
     float* Y = d.small + K + kk;
-    for (size_t q = tid; q < static_cast<size_t>(K2) * K; q += CY_SOLVE_THREADS)
-        G(Y)[q] = static_cast<float>(BW[q] + R[q]);
+    for (size_t q = tid; q < static_cast<size_t>(K2) * K; q += CY_SOLVE_THREADS) {
+        const int j = static_cast<int>(q / K), col = static_cast<int>(q % K);
+        G(Y)[q] = static_cast<float>(BW[q] + R[static_cast<size_t>(perm[j]) * K + col]);
+    }
 }
 
 }  // namespace

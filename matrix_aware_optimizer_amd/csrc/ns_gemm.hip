@@ -130,22 +130,29 @@ struct Engine {
     static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
     static constexpr int SM = WM / 32, SN = WN / 32;
     static constexpr int KS = CHUNKS_PER_ROW * 16 / static_cast<int>(sizeof(T));   // k per k-step
-    static constexpr int P_CHUNKS = BM * CHUNKS_PER_ROW;              // P rows first, then Q
-    static constexpr int STAGE = (BM + BN) * CHUNKS_PER_ROW;          // 16-byte chunks per stage
-    static constexpr int LOADS = STAGE / 64 / NWAVES;                 // loads per wave per k-step
-    static constexpr int SUB = CHUNKS_PER_ROW / 2;                    // MFMA k-slices per k-step
-    static constexpr int GROUPS = SUB * SM;                           // MFMA groups per k-step
-    static_assert(LOADS <= GROUPS, "one load per MFMA group at most");
+    static constexpr int SLAB = BM * CHUNKS_PER_ROW;   // 16-byte chunks of one operand's k-step slab
+    static constexpr int SLOTS = 5;                    // LDS ring of slabs
+    static constexpr int LDS_CHUNKS = SLOTS * SLAB;
+    static constexpr int HL = SLAB / 64 / NWAVES;      // loads per wave per slab
+    static constexpr int SUB = CHUNKS_PER_ROW / 2;     // MFMA k-slices per k-step
+    static constexpr int GROUPS = SUB * SM;            // MFMA groups per k-step
+    static_assert(BM == BN, "P and Q slabs have one size");
+    static_assert(2 * HL <= GROUPS, "one load per MFMA group at most");
     static_assert(SM >= SN, "fragment prefetch pairs A row i with B row i");
-    static_assert((P_CHUNKS / 64) % LOADS == 0, "a wave loads P rows only or Q rows only");
     static_assert(!QK || BN * static_cast<int>(sizeof(T)) == QROW_CHUNKS * 16, "k-major rows are one tile wide");
-    static_assert(!QK || KS * QROW_CHUNKS == BN * CHUNKS_PER_ROW, "k-major region fills the Q part of a stage");
+    static_assert(!QK || KS * QROW_CHUNKS == SLAB, "k-major slab holds KS rows");
 
     // acc[i][j] = init[i][j] + sum_k P[row0 + i][k] * Q(k, col0 + j) over the whole k
     // range, where P points at row row0 (pitch ldp bytes) and Q at row col0
     // (k-contiguous) or at column col0 of k-row 0 (k-major), pitch ldq bytes.
-    // init(acc) fills the accumulators once the first stage's loads are in flight;
-    // hook(kt, Q region of the stage, acc) runs when stage kt is ready.
+    // init(acc) fills the accumulators once the first slabs' loads are in flight;
+    // hook(kt, Q slab of step kt, acc) runs when step kt's slabs are ready.
+    //
+    // Slabs are numbered 2 kt (P) and 2 kt + 1 (Q) and slab s lives in LDS slot s % 5.
+    // During step kt a wave issues Q(kt + 1) and then P(kt + 2): both slots were read
+    // in step kt - 1, which every wave has left at the barrier opening step kt.  Step
+    // kt then waits for all but the newest HL loads (P(kt + 1)), so the loads of the
+    // next-but-one P slab stay in flight across the barrier.
     template <typename Init, typename Hook>
     static __device__ __attribute__((always_inline)) void run(const char* __restrict__ P, size_t ldp, const char* __restrict__ Q,
                                       size_t ldq, int ksteps, u32x4* lds, f32x16_t (&acc)[SM][SN], Init init,
@@ -154,50 +161,63 @@ struct Engine {
         const int lane = tid & 63, wave = tid >> 6;
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
-        // Load j of this wave fills stage chunks [(wave*LOADS + j)*64, +64) in lane order;
+        // Load j of this wave fills slab chunks [(wave*HL + j)*64, +64) in lane order;
         // the source address holds the logical chunk that the swizzle puts there.
-        const char* src[LOADS];
-        const bool wave_q = wave * LOADS * 64 >= P_CHUNKS;
-        const size_t step = (wave_q && QK) ? static_cast<size_t>(KS) * ldq : static_cast<size_t>(CHUNKS_PER_ROW * 16);
+        const char* srcp[HL];
+        const char* srcq[HL];
 #pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            const int chunk = (wave * LOADS + j) * 64 + lane;
-            if (!wave_q) {
-                const int row = chunk / CHUNKS_PER_ROW;
-                const int lc = (chunk % CHUNKS_PER_ROW) ^ ((row >> 1) & 7);
-                src[j] = P + row * ldp + lc * 16;
-            } else if (!QK) {
-                const int row = chunk / CHUNKS_PER_ROW;            // stage row, Q row = row - BM
-                const int lc = (chunk % CHUNKS_PER_ROW) ^ ((row >> 1) & 7);
-                src[j] = Q + (row - BM) * ldq + lc * 16;
+        for (int j = 0; j < HL; ++j) {
+            const int chunk = (wave * HL + j) * 64 + lane;
+            const int row = chunk / CHUNKS_PER_ROW;
+            const int lc = (chunk % CHUNKS_PER_ROW) ^ ((row >> 1) & 7);
+            srcp[j] = P + row * ldp + lc * 16;
+            if (!QK) {
+                srcq[j] = Q + row * ldq + lc * 16;
             } else {
-                const int qc = chunk - P_CHUNKS;
-                const int kr = qc / QROW_CHUNKS;
-                const int lc = (qc % QROW_CHUNKS) ^ ((kr & 3) << 2);
-                src[j] = Q + kr * ldq + lc * 16;
+                const int kr = chunk / QROW_CHUNKS;
+                const int lq = (chunk % QROW_CHUNKS) ^ ((kr & 3) << 2);
+                srcq[j] = Q + kr * ldq + lq * 16;
             }
         }
-        auto issue = [&](int kt, int j) {
-            lds_ptr_t d = (lds_ptr_t)(lds + (kt & 1) * STAGE + (wave * LOADS + j) * 64);
-            __builtin_amdgcn_global_load_lds((const void*)(src[j] + static_cast<size_t>(kt) * step), d, 16, 0, 0);
+        const size_t pstep = CHUNKS_PER_ROW * 16;
+        const size_t qstep = QK ? static_cast<size_t>(KS) * ldq : static_cast<size_t>(CHUNKS_PER_ROW * 16);
+        auto issue = [&](int kt, bool q, int slot, int j) {
+            lds_ptr_t d = (lds_ptr_t)(lds + slot * SLAB + (wave * HL + j) * 64);
+            const char* s = q ? srcq[j] + static_cast<size_t>(kt) * qstep : srcp[j] + static_cast<size_t>(kt) * pstep;
+            __builtin_amdgcn_global_load_lds((const void*)s, d, 16, 0, 0);
         };
 #pragma unroll
-        for (int j = 0; j < LOADS; ++j) issue(0, j);
+        for (int j = 0; j < HL; ++j) issue(0, false, 0, j);
+#pragma unroll
+        for (int j = 0; j < HL; ++j) issue(0, true, 1, j);
+        if (ksteps > 1) {
+#pragma unroll
+            for (int j = 0; j < HL; ++j) issue(1, false, 2, j);
+        }
         init(acc);
 
         const int half = lane >> 5;
-        const int arow = wm * WM + (lane & 31), brow = BM + wn * WN + (lane & 31);
+        const int arow = wm * WM + (lane & 31), brow = wn * WN + (lane & 31);
+        int sp = 0;   // slot of P(kt); Q(kt) sits in the next one
         for (int kt = 0; kt < ksteps; ++kt) {
-            // this wave's loads of stage kt are done; the barrier makes every wave's visible
-            // and guarantees stage (kt + 1) & 1 is no longer being read
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            // this wave's loads of step kt's slabs are done (P(kt + 1) may still be in
+            // flight); the barrier makes every wave's visible and guarantees that the
+            // slots of step kt - 1 are no longer being read
+            if (kt + 1 < ksteps)
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(HL) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             asm volatile("s_barrier" ::: "memory");
-            const u32x4* L = lds + (kt & 1) * STAGE;
-            const lds_byte_t* Lq = (const lds_byte_t*)(L + P_CHUNKS);
+            const int sq = sp + 1 == SLOTS ? 0 : sp + 1;
+            const int s3 = sp >= 2 ? sp - 2 : sp + 3;   // slot of Q(kt + 1)
+            const int s4 = sp >= 1 ? sp - 1 : sp + 4;   // slot of P(kt + 2)
+            const u32x4* L = lds + sp * SLAB;
+            const u32x4* LQ = lds + sq * SLAB;
+            const lds_byte_t* Lq = (const lds_byte_t*)LQ;
             hook(kt, Lq, acc);
             // B operand of k-slice s (16 bf16 or 8 fp32 of k) for 32-column block j
             auto read_b = [&](int j, int s) -> u32x4 {
-                if (!QK) return L[swz(brow + j * 32, 2 * s + half)];
+                if (!QK) return LQ[swz(brow + j * 32, 2 * s + half)];
                 if (sizeof(T) == 2) {
                     const int i16 = lane & 15, g16 = lane >> 4;
                     const int col = wn * WN + j * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
@@ -222,7 +242,7 @@ struct Engine {
                     return v;
                 }
             };
-            const bool more = kt + 1 < ksteps;
+            const bool more1 = kt + 1 < ksteps, more2 = kt + 2 < ksteps;
             u32x4 fa[2][SM], fb[2][SN];
 #pragma unroll
             for (int i = 0; i < SM; ++i) fa[0][i] = L[swz(arow + i * 32, half)];
@@ -241,10 +261,12 @@ struct Engine {
                         if (i < SN) fb[(s + 1) & 1][i] = read_b(i, s + 1);
                     }
                     const int g = s * SM + i;
-                    if (g < LOADS && more) issue(kt + 1, g);
+                    if (g < HL && more1) issue(kt + 1, true, s3, g);
+                    if (g >= HL && g < 2 * HL && more2) issue(kt + 2, false, s4, g - HL);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+            sp = sp >= 3 ? sp - 3 : sp + 2;
         }
     }
 };
@@ -323,6 +345,16 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4]) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) v[p] = ((p ^ t) & 2) ? s[p ^ 2] : x[p];
 }
+
+// Lanes c and c ^ 4 of each 32-lane half hold the same rows (8 g + 4 h + t) and
+// adjacent column quads after quad_transpose.  Swapping one quad of a pair of g
+// values gives each lane 8 consecutive columns of one row: the lane of the even
+// quad (bit 2 of the lane clear) takes row g0 = 2 gg, the other row g1 = 2 gg + 1,
+// both starting at column (lane & 24) of the 32-column block.  16-byte accesses.
+__device__ __forceinline__ unsigned swap_xor4(unsigned v) {
+    return static_cast<unsigned>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x101F));   // lane ^ 4
+}
+__device__ __forceinline__ bool odd_quad() { return (threadIdx.x >> 2) & 1; }
 
 // Per-lane coordinates inside a wave's sub-tile.
 template <typename E>
@@ -419,6 +451,41 @@ struct UpdateInit {
     float a;
     template <typename A> __device__ __forceinline__ void operator()(A& acc) const {
         const Coords<E> q(row0, col0);
+        if (sizeof(T) == 2) {
+            // 16 bytes of one row per lane, then the quad swap back to the pair's rows
+            const bool odd = odd_quad();
+#pragma unroll
+            for (int i = 0; i < E::SM; ++i)
+#pragma unroll
+                for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+                    for (int gg = 0; gg < 2; ++gg) {
+                        const size_t idx = static_cast<size_t>(q.tr_row + 32 * i + 8 * (2 * gg + odd)) * np +
+                                           q.tr_col + 32 * j - (odd ? 4 : 0);
+                        const u32x4 w = G(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + idx))[0];
+                        // words 0-1: the even lane's columns, words 2-3: the odd lane's
+                        const unsigned k0 = odd ? w.z : w.x, k1 = odd ? w.w : w.y;
+                        const unsigned r0 = swap_xor4(odd ? w.x : w.z), r1 = swap_xor4(odd ? w.y : w.w);
+                        const unsigned g0w[2] = {odd ? r0 : k0, odd ? r1 : k1};   // row g0, own columns
+                        const unsigned g1w[2] = {odd ? k0 : r0, odd ? k1 : r1};   // row g1, own columns
+                        float v0[4], v1[4];
+#pragma unroll
+                        for (int p = 0; p < 2; ++p) {
+                            v0[2 * p] = a * __uint_as_float(g0w[p] << 16);
+                            v0[2 * p + 1] = a * __uint_as_float(g0w[p] & 0xffff0000u);
+                            v1[2 * p] = a * __uint_as_float(g1w[p] << 16);
+                            v1[2 * p + 1] = a * __uint_as_float(g1w[p] & 0xffff0000u);
+                        }
+                        quad_transpose(v0);   // row layout -> accumulator layout (an involution)
+                        quad_transpose(v1);
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) {
+                            acc[i][j][8 * gg + p] = v0[p];
+                            acc[i][j][8 * gg + 4 + p] = v1[p];
+                        }
+                    }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < E::SM; ++i)
 #pragma unroll
@@ -483,28 +550,57 @@ template <typename E, typename T>
 __device__ __attribute__((always_inline)) void update_epilogue(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
                                                                void* hi_out, uint16_t* lo_out, size_t np, float u) {
     const Coords<E> q(row0, col0);
+    if (sizeof(T) == 4) {
+#pragma unroll
+        for (int i = 0; i < E::SM; ++i)
+#pragma unroll
+            for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) v[p] = acc[i][j][4 * g + p];
+                    quad_transpose(v);
+                    const size_t idx = static_cast<size_t>(q.tr_row + 32 * i + 8 * g) * np + q.tr_col + 32 * j;
+                    st_f4(static_cast<float*>(hi_out) + idx, make_float4(u * v[0], u * v[1], u * v[2], u * v[3]));
+                }
+        return;
+    }
+    // bf16: 8 consecutive columns of one row per lane after the quad swap
+    const bool odd = odd_quad();
 #pragma unroll
     for (int i = 0; i < E::SM; ++i)
 #pragma unroll
         for (int j = 0; j < E::SN; ++j)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float v[4];
+            for (int gg = 0; gg < 2; ++gg) {
+                float v0[4], v1[4];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) v[p] = acc[i][j][4 * g + p];
-                quad_transpose(v);
-                const float4 o = make_float4(u * v[0], u * v[1], u * v[2], u * v[3]);
-                const size_t idx = static_cast<size_t>(q.tr_row + 32 * i + 8 * g) * np + q.tr_col + 32 * j;
-                if (sizeof(T) == 4) {
-                    st_f4(static_cast<float*>(hi_out) + idx, o);
-                } else {
-                    const u32x2_t h = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
-                    const float4 hf = make_float4(__uint_as_float(h.x << 16), __uint_as_float(h.x & 0xffff0000u),
-                                                  __uint_as_float(h.y << 16), __uint_as_float(h.y & 0xffff0000u));
-                    const u32x2_t l = {pack_bf16x2(o.x - hf.x, o.y - hf.y), pack_bf16x2(o.z - hf.z, o.w - hf.w)};
-                    st_u2(static_cast<uint16_t*>(hi_out) + idx, h);
-                    st_u2(lo_out + idx, l);
+                for (int p = 0; p < 4; ++p) {
+                    v0[p] = acc[i][j][8 * gg + p];
+                    v1[p] = acc[i][j][8 * gg + 4 + p];
                 }
+                quad_transpose(v0);
+                quad_transpose(v1);
+                float x[8];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float keep = odd ? v1[p] : v0[p];
+                    const float recv = __uint_as_float(swap_xor4(__float_as_uint(odd ? v0[p] : v1[p])));
+                    x[p] = odd ? recv : keep;
+                    x[4 + p] = odd ? keep : recv;
+                }
+                unsigned h[4], l[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float o0 = u * x[2 * p], o1 = u * x[2 * p + 1];
+                    h[p] = pack_bf16x2(o0, o1);
+                    l[p] = pack_bf16x2(o0 - __uint_as_float(h[p] << 16), o1 - __uint_as_float(h[p] & 0xffff0000u));
+                }
+                const size_t idx = static_cast<size_t>(q.tr_row + 32 * i + 8 * (2 * gg + odd)) * np +
+                                   q.tr_col + 32 * j - (odd ? 4 : 0);
+                G(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(hi_out) + idx))[0] = u32x4{h[0], h[1], h[2], h[3]};
+                G(reinterpret_cast<u32x4*>(lo_out + idx))[0] = u32x4{l[0], l[1], l[2], l[3]};
             }
 }
 
@@ -558,7 +654,7 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
 template <typename T, int PHASE>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void ns_gemm_kernel(NsArgs args) {
     using E = Engine<T, PHASE == PH_UPDATE>;
-    __shared__ u32x4 lds[2 * E::STAGE];
+    __shared__ u32x4 lds[E::LDS_CHUNKS];
     const int t = xcd_run_remap(blockIdx.x, gridDim.x);
     if (t < args.total) process_tile<T, PHASE>(args, t, lds);
 }

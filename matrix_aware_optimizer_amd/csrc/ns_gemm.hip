@@ -355,6 +355,10 @@ __device__ __forceinline__ unsigned swap_xor4(unsigned v) {
     return static_cast<unsigned>(__builtin_amdgcn_ds_swizzle(static_cast<int>(v), 0x101F));   // lane ^ 4
 }
 __device__ __forceinline__ bool odd_quad() { return (threadIdx.x >> 2) & 1; }
+// Lanes l and l ^ 32 hold the same column and rows 4 apart (8 g + 4 h + (0..3)).
+__device__ __forceinline__ unsigned swap_xor32(unsigned v) {
+    return static_cast<unsigned>(__builtin_amdgcn_ds_bpermute(((threadIdx.x & 63) ^ 32) << 2, static_cast<int>(v)));
+}
 
 // Per-lane coordinates inside a wave's sub-tile.
 template <typename E>
@@ -380,7 +384,7 @@ struct Coords {
 //   polynomial:  value = b * A + c * acc   (A read at the mirrored position,
 //                                            equal to the direct one by symmetry)
 template <typename E, typename T, bool POLY>
-__device__ __attribute__((always_inline)) void sym_epilogue(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
+__device__ __attribute__((always_inline)) void sym_epilogue_quad(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
                                                             bool diag, void* dst, size_t ld, float scale,
                                                             const void* amat, float b, float c) {
     const Coords<E> q(row0, col0);
@@ -431,6 +435,136 @@ __device__ __attribute__((always_inline)) void sym_epilogue(f32x16_t (&acc)[E::S
             for (int k = 0; k < E::SN * 4; ++k) cur[k] = nxt[k];
         }
     }
+}
+
+// bf16 symmetric output with 16-byte accesses.  For each pair of 8-row groups
+// (g0 = 2 gg, g1 = 2 gg + 1) of a 32 x 32 block:
+//   mirrored: lanes l and l ^ 32 swap one quad, so lane half h owns rows
+//             8 g_h + (0..7) of its column and stores them as 8 consecutive
+//             columns of the mirrored row;
+//   direct:   after quad_transpose, lanes c and c ^ 4 swap one quad (as in the
+//             update epilogue), giving 8 consecutive columns of one row.
+// The polynomial's A is read the same way as the mirrored store (A[cc][8 g_h ..])
+// and swapped back to the accumulator rows.  Diagonal tiles mask per element,
+// exactly as the 4-element version does.
+__device__ __forceinline__ void st_bf16x8_masked(uint16_t* p, const float (&v)[8], unsigned mask) {
+    if (mask == 0xFFu) {
+        G(reinterpret_cast<u32x4*>(p))[0] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    } else if (mask) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (mask & (1u << e)) G(p)[e] = f32_to_bf16(v[e]);
+    }
+}
+
+template <typename E, bool POLY>
+__device__ __attribute__((always_inline)) void sym_epilogue_bf16(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
+                                                                 bool diag, uint16_t* dst, size_t ld, float scale,
+                                                                 const uint16_t* amat, float b, float c) {
+    const Coords<E> q(row0, col0);
+    const bool hh = (threadIdx.x >> 5) & 1;
+    const bool odd = odd_quad();
+    const int mbase = q.raw_row - (hh ? 4 : 0);   // first row of the wave's sub-tile
+    u32x4 cur[E::SN * 2], nxt[E::SN * 2];
+    auto fetch = [&](u32x4 (&buf)[E::SN * 2], int i) {
+#pragma unroll
+        for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+            for (int gg = 0; gg < 2; ++gg)
+                buf[j * 2 + gg] = G(reinterpret_cast<const u32x4*>(
+                    amat + static_cast<size_t>(q.raw_col + 32 * j) * ld + mbase + 32 * i + 8 * (2 * gg + hh)))[0];
+    };
+    if (POLY) fetch(cur, 0);
+#pragma unroll
+    for (int i = 0; i < E::SM; ++i) {
+        if (POLY && i + 1 < E::SM) fetch(nxt, i + 1);
+#pragma unroll
+        for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+            for (int gg = 0; gg < 2; ++gg) {
+                float r0[4], r1[4];   // raw layout: rows 8 g + 4 h + p of column cc
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    r0[p] = acc[i][j][8 * gg + p];
+                    r1[p] = acc[i][j][8 * gg + 4 + p];
+                }
+                if (POLY) {
+                    // this lane read rows 8 g_h + (0..7); words 0-1 hold rows +0..3, words 2-3 rows +4..7
+                    const u32x4 w = cur[j * 2 + gg];
+                    const unsigned k0 = hh ? w.z : w.x, k1 = hh ? w.w : w.y;
+                    const unsigned s0 = swap_xor32(hh ? w.x : w.z), s1 = swap_xor32(hh ? w.y : w.w);
+                    const unsigned a0w[2] = {hh ? s0 : k0, hh ? s1 : k1};   // rows 8 g0 + 4 h + (0..3)
+                    const unsigned a1w[2] = {hh ? k0 : s0, hh ? k1 : s1};   // rows 8 g1 + 4 h + (0..3)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        r0[2 * p] = fmaf(c, r0[2 * p], b * __uint_as_float(a0w[p] << 16));
+                        r0[2 * p + 1] = fmaf(c, r0[2 * p + 1], b * __uint_as_float(a0w[p] & 0xffff0000u));
+                        r1[2 * p] = fmaf(c, r1[2 * p], b * __uint_as_float(a1w[p] << 16));
+                        r1[2 * p + 1] = fmaf(c, r1[2 * p + 1], b * __uint_as_float(a1w[p] & 0xffff0000u));
+                    }
+                } else {
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        r0[p] *= scale;
+                        r1[p] *= scale;
+                    }
+                }
+                const int cc = q.raw_col + 32 * j;
+                // mirrored: h = 0 stores rows 8 g0 + (0..7), h = 1 rows 8 g1 + (0..7), at row cc
+                {
+                    float m[8];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float rcv = __uint_as_float(swap_xor32(__float_as_uint(hh ? r0[p] : r1[p])));
+                        m[p] = hh ? rcv : r0[p];
+                        m[4 + p] = hh ? r1[p] : rcv;
+                    }
+                    const int mc = mbase + 32 * i + 8 * (2 * gg + hh);
+                    unsigned mm = 0xFFu;
+                    if (diag) {
+                        mm = 0;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) mm |= (mc + e < cc) ? (1u << e) : 0u;
+                    }
+                    st_bf16x8_masked(dst + static_cast<size_t>(cc) * ld + mc, m, mm);
+                }
+                // direct: row tr, columns tc .. tc + 7
+                quad_transpose(r0);
+                quad_transpose(r1);
+                float x[8];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float keep = odd ? r1[p] : r0[p];
+                    const float recv = __uint_as_float(swap_xor4(__float_as_uint(odd ? r0[p] : r1[p])));
+                    x[p] = odd ? recv : keep;
+                    x[4 + p] = odd ? keep : recv;
+                }
+                const int tr = q.tr_row + 32 * i + 8 * (2 * gg + odd);
+                const int tc = q.tr_col + 32 * j - (odd ? 4 : 0);
+                unsigned md = 0xFFu;
+                if (diag) {
+                    md = 0;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) md |= (tr <= tc + e) ? (1u << e) : 0u;
+                }
+                st_bf16x8_masked(dst + static_cast<size_t>(tr) * ld + tc, x, md);
+            }
+        if (POLY) {
+#pragma unroll
+            for (int k = 0; k < E::SN * 2; ++k) cur[k] = nxt[k];
+        }
+    }
+}
+
+template <typename E, typename T, bool POLY>
+__device__ __forceinline__ void sym_epilogue(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0, bool diag, void* dst,
+                                             size_t ld, float scale, const void* amat, float b, float c) {
+    if (sizeof(T) == 2)
+        sym_epilogue_bf16<E, POLY>(acc, row0, col0, diag, static_cast<uint16_t*>(dst), ld, scale,
+                                   static_cast<const uint16_t*>(amat), b, c);
+    else
+        sym_epilogue_quad<E, T, POLY>(acc, row0, col0, diag, dst, ld, scale, amat, b, c);
 }
 
 // X' = u (a X + B X).  a X enters the accumulators before or during the

@@ -42,6 +42,8 @@
 // matrices first), one workgroup per tile.  The hardware deals workgroups
 // round-robin over the 8 XCDs; block ids are remapped so that each XCD works
 // on runs of 32 consecutive tiles, whose operand blocks then share its L2.
+#include <cmath>
+
 #include "muon_internal.h"
 
 namespace muon {
@@ -306,7 +308,9 @@ template <typename T> __device__ inline void st_quad_masked(void* p, size_t i, c
     }
 }
 
-enum Phase { PH_GRAM = 0, PH_POLY = 1, PH_UPDATE = 2 };
+// PH_POLY_LDS is the polynomial with b A added from the staged operand (c != 0);
+// PH_POLY reads A again in the epilogue and serves any c.
+enum Phase { PH_GRAM = 0, PH_POLY = 1, PH_UPDATE = 2, PH_POLY_LDS = 3 };
 
 struct NoHook {
     template <typename A> __device__ __forceinline__ void operator()(int, const lds_byte_t*, A&) const {}
@@ -680,6 +684,58 @@ struct HiAddend {
     }
 };
 
+// Polynomial B = b A + c A A with c != 0, accumulated as c (A A + (b / c) A): the
+// Q slab of k-step kt holds A[col0 + r][kt KS + (0..KS-1)], which by symmetry is
+// A[kt KS + (0..KS-1)][col0 + r]; when those k are output rows of this tile the
+// waves owning them add f A = (b / c) A for those rows.  A lane's 4 accumulator
+// rows of one column are 4 consecutive k of one slab row: one 8-byte (bf16) or
+// 16-byte (fp32) LDS read.
+template <typename E, typename T>
+struct PolyAddend {
+    int kt0;    // row0 / KS
+    float f;    // b / c
+    template <typename A> __device__ __forceinline__ void operator()(int kt, const lds_byte_t* Lq, A& acc) const {
+        const int rel = kt - kt0;
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+        if (rel < 0 || rel >= E::BM / E::KS || (rel * E::KS) / E::WM != wm) return;
+        const int ifirst = (rel * E::KS - wm * E::WM) / 32;
+        constexpr int EPC = 16 / static_cast<int>(sizeof(T));   // elements per 16-byte chunk
+        const int h = lane >> 5;
+#pragma unroll
+        for (int i = 0; i < E::SM; ++i) {
+            if (i >= ifirst && i < ifirst + E::KS / 32) {
+#pragma unroll
+                for (int j = 0; j < E::SN; ++j) {
+                    const int sr = wn * E::WN + 32 * j + (lane & 31);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int kk = 32 * (i - ifirst) + 8 * g + 4 * h;
+                        const lds_byte_t* a = Lq + swz(sr, kk / EPC) * 16 + (kk % EPC) * static_cast<int>(sizeof(T));
+                        float v[4];
+                        if (sizeof(T) == 2) {
+                            const u32x2_t w = *(const __attribute__((address_space(3))) u32x2_t*)a;
+                            v[0] = __uint_as_float(w.x << 16);
+                            v[1] = __uint_as_float(w.x & 0xffff0000u);
+                            v[2] = __uint_as_float(w.y << 16);
+                            v[3] = __uint_as_float(w.y & 0xffff0000u);
+                        } else {
+                            const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)a;
+                            v[0] = __uint_as_float(w.x);
+                            v[1] = __uint_as_float(w.y);
+                            v[2] = __uint_as_float(w.z);
+                            v[3] = __uint_as_float(w.w);
+                        }
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) acc[i][j][4 * g + p] = fmaf(f, v[p], acc[i][j][4 * g + p]);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+};
+
 template <typename E, typename T>
 __device__ __attribute__((always_inline)) void update_epilogue(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
                                                                void* hi_out, uint16_t* lo_out, size_t np, float u) {
@@ -768,6 +824,12 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         const size_t ld = static_cast<size_t>(mp) * sizeof(T);
         E::run(A + row0 * ld, ld, A + col0 * ld, ld, mp * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc, ZeroInit{}, NoHook{});
         sym_epilogue<E, T, true>(acc, row0, col0, ti == tj, d.bmat, mp, 1.0f, d.amat, args.b, args.c);
+    } else if (PHASE == PH_POLY_LDS) {
+        const char* A = static_cast<const char*>(d.amat);
+        const size_t ld = static_cast<size_t>(mp) * sizeof(T);
+        E::run(A + row0 * ld, ld, A + col0 * ld, ld, mp * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc, ZeroInit{},
+               PolyAddend<E, T>{row0 / E::KS, args.b / args.c});
+        sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.bmat, mp, args.c, nullptr, 0.0f, 0.0f);
     } else {
         const char* B = static_cast<const char*>(d.bmat);
         const char* X = static_cast<const char*>(d.xop[ping]);
@@ -806,7 +868,12 @@ hipError_t launch_phase(int dtype, const NsArgs& args, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gram(int dtype, const NsArgs& args, hipStream_t s) { return launch_phase<PH_GRAM>(dtype, args, s); }
-hipError_t launch_poly(int dtype, const NsArgs& args, hipStream_t s) { return launch_phase<PH_POLY>(dtype, args, s); }
+hipError_t launch_poly(int dtype, const NsArgs& args, hipStream_t s) {
+    // the kernel forms b / c in fp32; it must be finite for the staged-operand form
+    const float f = args.b / args.c;
+    if (args.c != 0.0f && std::isfinite(f)) return launch_phase<PH_POLY_LDS>(dtype, args, s);
+    return launch_phase<PH_POLY>(dtype, args, s);
+}
 hipError_t launch_update(int dtype, const NsArgs& args, hipStream_t s) { return launch_phase<PH_UPDATE>(dtype, args, s); }
 
 }  // namespace muon

@@ -32,27 +32,39 @@ template <> struct Elem<uint16_t> {
     }
 };
 
-// Store 4 consecutive values of the operand dtype (8-byte or 16-byte store).
-template <typename T> __device__ inline void store4(void* base, size_t idx, float v0, float v1, float v2, float v3);
-template <> __device__ inline void store4<float>(void* base, size_t idx, float v0, float v1, float v2, float v3) {
-    st_f4(static_cast<float*>(base) + idx, make_float4(v0, v1, v2, v3));
+// 8 consecutive elements of the caller's dtype as fp32 (one 16-byte bf16 or two
+// 16-byte fp32 accesses), and the matching store.
+template <typename T> __device__ inline void load8(const void* base, size_t idx, float (&v)[8]);
+template <> __device__ inline void load8<float>(const void* base, size_t idx, float (&v)[8]) {
+    const float4 a = ld_f4(static_cast<const float*>(base) + idx), b = ld_f4(static_cast<const float*>(base) + idx + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
-template <> __device__ inline void store4<uint16_t>(void* base, size_t idx, float v0, float v1, float v2, float v3) {
-    const u32x2_t p = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-    st_u2(static_cast<uint16_t*>(base) + idx, p);
+template <> __device__ inline void load8<uint16_t>(const void* base, size_t idx, float (&v)[8]) {
+    const u32x4_t q = G(reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(base) + idx))[0];
+    const unsigned w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        v[2 * k] = __uint_as_float(w[k] << 16);
+        v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+    }
+}
+template <typename T> __device__ inline void store8(void* base, size_t idx, const float (&v)[8]);
+template <> __device__ inline void store8<float>(void* base, size_t idx, const float (&v)[8]) {
+    st_f4(static_cast<float*>(base) + idx, make_float4(v[0], v[1], v[2], v[3]));
+    st_f4(static_cast<float*>(base) + idx + 4, make_float4(v[4], v[5], v[6], v[7]));
+}
+template <> __device__ inline void store8<uint16_t>(void* base, size_t idx, const float (&v)[8]) {
+    G(reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(base) + idx))[0] =
+        u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
 }
 
-// 4 consecutive elements of the caller's dtype as fp32 (8-byte or 16-byte load).
-template <typename T> __device__ inline float4 load4(const void* base, size_t idx);
-template <> __device__ inline float4 load4<float>(const void* base, size_t idx) {
-    return ld_f4(static_cast<const float*>(base) + idx);
-}
-template <> __device__ inline float4 load4<uint16_t>(const void* base, size_t idx) {
-    const u32x2_t q = ld_u2(static_cast<const uint16_t*>(base) + idx);
-    return make_float4(__uint_as_float(q.x << 16), __uint_as_float(q.x & 0xffff0000u),
-                       __uint_as_float(q.y << 16), __uint_as_float(q.y & 0xffff0000u));
-}
-__device__ inline float f4at(const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; }
+// Element ownership inside a 64 x 64 tile: thread t covers rows (t >> 3) + 32 p,
+// p = 0, 1, and 8 consecutive columns starting at (t & 7) * 8.
+constexpr int EW_GROUP = 8;
+constexpr int EW_PASSES = EW_TILE * EW_TILE / (EW_GROUP * EW_THREADS);
+static_assert(EW_PASSES == 2, "two 8-element groups per thread and tile");
+__device__ __forceinline__ int ew_row(int p) { return (threadIdx.x >> 3) + (EW_THREADS / 8) * p; }
+__device__ __forceinline__ int ew_col() { return (threadIdx.x & 7) * EW_GROUP; }
 
 // Deterministic block sum (fixed shuffle pattern, fixed wave order).
 __device__ inline float block_sum_256(float v, float* red) {
@@ -75,103 +87,114 @@ __device__ inline void ew_tile_origin(const MatDesc& d, int local, int& i0, int&
 
 // ----------------------------------------------------------------------------
 // Momentum + norm partials + operand copies.
-//   user-frame load (coalesced) -> fp32 M' (state store) -> U into LDS in the
-//   NS frame -> rows of the iterate (fp32, or the bf16 pair hi + lo whose hi
-//   is the MFMA operand), coalesced, with the sum of squares taken in NS-frame
-//   order so the result does not depend on the caller's orientation.
+//   Each thread owns two 8-element row groups of an NS-frame tile.  For a
+//   matrix stored untransposed the caller's layout is the NS frame and the
+//   groups are read and written in place; a tall matrix is read along the
+//   caller's rows (coalesced) and turned through LDS.  Then: rows of the
+//   iterate (fp32, or the bf16 pair hi + lo whose hi is the MFMA operand) and
+//   the sum of squares, taken in NS-frame order so the result does not depend
+//   on the caller's orientation.
 // ----------------------------------------------------------------------------
+template <typename T, bool NS_ONLY>
+__device__ __forceinline__ void momentum_group(const MatDesc& d, float beta, int nesterov, int ur, int uc,
+                                               float (&u)[EW_GROUP]) {
+#pragma unroll
+    for (int e = 0; e < EW_GROUP; ++e) u[e] = 0.0f;
+    if (ur >= d.rows || uc >= d.cols) return;
+    const size_t idx = static_cast<size_t>(ur) * d.cols + uc;
+    if (d.uvec) {   // cols % 8 == 0: the whole group is inside the row
+        float g[EW_GROUP];
+        load8<T>(d.g, idx, g);
+        if (NS_ONLY) {
+#pragma unroll
+            for (int e = 0; e < EW_GROUP; ++e) u[e] = g[e];
+        } else {
+            float m[EW_GROUP], mn[EW_GROUP];
+            load8<T>(d.mom, idx, m);
+#pragma unroll
+            for (int e = 0; e < EW_GROUP; ++e) {
+                mn[e] = fmaf(beta, m[e], g[e]);
+                u[e] = nesterov ? fmaf(beta, mn[e], g[e]) : mn[e];
+            }
+            store8<T>(d.mom, idx, mn);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EW_GROUP; ++e) {
+            if (uc + e >= d.cols) break;
+            const float g = Elem<T>::load(d.g, idx + e);
+            if (NS_ONLY) {
+                u[e] = g;
+            } else {
+                const float m = Elem<T>::load(d.mom, idx + e);
+                const float mn = fmaf(beta, m, g);
+                Elem<T>::store(d.mom, idx + e, mn);
+                u[e] = nesterov ? fmaf(beta, mn, g) : mn;
+            }
+        }
+    }
+}
+
 template <typename T, bool NS_ONLY>
 __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) {
     __shared__ float tile[EW_TILE][EW_TILE + 1];
     __shared__ float red[4];
-    const int tid = threadIdx.x;
     const int t0 = blockIdx.x * args.tiles_per_block;
     const int t1 = min(args.total, t0 + args.tiles_per_block);
     if (t0 >= t1) return;
     int mi = find_matrix(args.prefix, args.nmat, t0);
-    const float beta = args.beta;
+    const int jl = ew_col();
 
     for (int t = t0; t < t1; ++t) {
         while (t >= args.prefix[mi + 1]) ++mi;
         const MatDesc& d = args.descs[mi];
         int i0, j0;
         ew_tile_origin(d, t - args.prefix[mi], i0, j0);
-        const int ur0 = d.tall ? j0 : i0;   // user-frame block origin
-        const int uc0 = d.tall ? i0 : j0;
-        const int rows = d.rows, cols = d.cols;
-
-        // ---- load phase: 4 consecutive user columns per thread, 16 threads per 64-element row
+        float u[EW_PASSES][EW_GROUP];
+        if (!d.tall) {
 #pragma unroll
-        for (int p = 0; p < EW_TILE * EW_TILE / (4 * EW_THREADS); ++p) {
-            const int q = tid + EW_THREADS * p;
-            const int lr = q >> 4, lc = (q & 15) * 4;
-            const int ur = ur0 + lr, uc = uc0 + lc;
-            float u[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if (ur < rows && uc < cols) {
-                const size_t idx = static_cast<size_t>(ur) * cols + uc;
-                if (d.uvec) {   // uc + 3 < cols: cols and uc are multiples of 4
-                    const float4 g = load4<T>(d.g, idx);
-                    if (NS_ONLY) {
-                        u[0] = g.x; u[1] = g.y; u[2] = g.z; u[3] = g.w;
-                    } else {
-                        const float4 m = load4<T>(d.mom, idx);
-                        float mn[4];
+            for (int p = 0; p < EW_PASSES; ++p)
+                momentum_group<T, NS_ONLY>(d, args.beta, args.nesterov, i0 + ew_row(p), j0 + jl, u[p]);
+        } else {
+            // caller rows are NS columns: load caller row (j0 + r), columns i0 + jl + e
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            mn[e] = fmaf(beta, f4at(m, e), f4at(g, e));
-                            u[e] = args.nesterov ? fmaf(beta, mn[e], f4at(g, e)) : mn[e];
-                        }
-                        store4<T>(d.mom, idx, mn[0], mn[1], mn[2], mn[3]);
-                    }
-                } else {
+            for (int p = 0; p < EW_PASSES; ++p) {
+                float v[EW_GROUP];
+                momentum_group<T, NS_ONLY>(d, args.beta, args.nesterov, j0 + ew_row(p), i0 + jl, v);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (uc + e >= cols) break;
-                        const float g = Elem<T>::load(d.g, idx + e);
-                        if (NS_ONLY) {
-                            u[e] = g;
-                        } else {
-                            const float m = Elem<T>::load(d.mom, idx + e);
-                            const float mn = fmaf(beta, m, g);
-                            Elem<T>::store(d.mom, idx + e, mn);
-                            u[e] = args.nesterov ? fmaf(beta, mn, g) : mn;
-                        }
-                    }
-                }
+                for (int e = 0; e < EW_GROUP; ++e) tile[jl + e][ew_row(p)] = v[e];
             }
+            __syncthreads();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (d.tall) tile[lc + e][lr] = u[e]; else tile[lr][lc + e] = u[e];
-            }
+            for (int p = 0; p < EW_PASSES; ++p)
+#pragma unroll
+                for (int e = 0; e < EW_GROUP; ++e) u[p][e] = tile[ew_row(p)][jl + e];
         }
-        __syncthreads();
 
         // ---- NS-frame rows: X32 (and the bf16 operand copy)
         float sq = 0.0f;
-        {
-            const int jl = (tid & 15) * 4;
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int il = (tid >> 4) + 16 * p;
-                const float v0 = tile[il][jl], v1 = tile[il][jl + 1];
-                const float v2 = tile[il][jl + 2], v3 = tile[il][jl + 3];
-                sq = fmaf(v0, v0, sq); sq = fmaf(v1, v1, sq);
-                sq = fmaf(v2, v2, sq); sq = fmaf(v3, v3, sq);
-                const size_t idx = static_cast<size_t>(i0 + il) * d.np + (j0 + jl);
-                if (sizeof(T) == 2) {
-                    // the iterate as the pair hi + lo: hi = bf16(U), lo = bf16(U - hi)
-                    const uint32_t h01 = pack_bf16x2(v0, v1), h23 = pack_bf16x2(v2, v3);
-                    const float r0 = v0 - __uint_as_float(h01 << 16), r1 = v1 - __uint_as_float(h01 & 0xffff0000u);
-                    const float r2 = v2 - __uint_as_float(h23 << 16), r3 = v3 - __uint_as_float(h23 & 0xffff0000u);
-                    st_u2(static_cast<uint16_t*>(d.xop[0]) + idx, u32x2_t{h01, h23});
-                    store4<T>(d.xlo, idx, r0, r1, r2, r3);
-                } else {
-                    st_f4(d.x32[0] + idx, make_float4(v0, v1, v2, v3));
+        for (int p = 0; p < EW_PASSES; ++p) {
+#pragma unroll
+            for (int e = 0; e < EW_GROUP; ++e) sq = fmaf(u[p][e], u[p][e], sq);
+            const size_t idx = static_cast<size_t>(i0 + ew_row(p)) * d.np + (j0 + jl);
+            if (sizeof(T) == 2) {
+                // the iterate as the pair hi + lo: hi = bf16(U), lo = bf16(U - hi)
+                unsigned h[4], l[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float a = u[p][2 * k], b = u[p][2 * k + 1];
+                    h[k] = pack_bf16x2(a, b);
+                    l[k] = pack_bf16x2(a - __uint_as_float(h[k] << 16), b - __uint_as_float(h[k] & 0xffff0000u));
                 }
+                G(reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(d.xop[0]) + idx))[0] = u32x4_t{h[0], h[1], h[2], h[3]};
+                G(reinterpret_cast<u32x4_t*>(d.xlo + idx))[0] = u32x4_t{l[0], l[1], l[2], l[3]};
+            } else {
+                store8<float>(d.x32[0], idx, u[p]);
             }
         }
         const float total = block_sum_256(sq, red);   // also orders LDS reuse
-        if (tid == 0) G(args.partials)[t] = total;
+        if (threadIdx.x == 0) G(args.partials)[t] = total;
     }
 }
 
@@ -200,67 +223,91 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* descs
 
 // ----------------------------------------------------------------------------
 // Apply: W' = (1 - lr*wd) W - lr*s_rule*X  (muon_step), or out = X (muon_ns).
-// X is read in the NS frame and written back in the caller's frame.
+// X is read in the NS frame; an untransposed matrix is written in place, a
+// tall one is turned through LDS and written along the caller's rows.
 // ----------------------------------------------------------------------------
+template <typename T, bool NS_ONLY>
+__device__ __forceinline__ void apply_group(const MatDesc& d, float coef, float oscale, int ur, int uc,
+                                            const float (&o)[EW_GROUP]) {
+    if (ur >= d.rows || uc >= d.cols) return;
+    const size_t idx = static_cast<size_t>(ur) * d.cols + uc;
+    if (d.uvec) {
+        float r[EW_GROUP];
+        if (NS_ONLY) {
+#pragma unroll
+            for (int e = 0; e < EW_GROUP; ++e) r[e] = o[e] * oscale;
+            store8<float>(d.out, idx, r);
+        } else {
+            float w[EW_GROUP];
+            load8<T>(d.w, idx, w);
+#pragma unroll
+            for (int e = 0; e < EW_GROUP; ++e) r[e] = fmaf(-coef, o[e], d.decay * w[e]);
+            store8<T>(d.w, idx, r);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EW_GROUP; ++e) {
+            if (uc + e >= d.cols) break;
+            if (NS_ONLY) {
+                G(d.out)[idx + e] = o[e] * oscale;
+            } else {
+                const float w = Elem<T>::load(d.w, idx + e);
+                Elem<T>::store(d.w, idx + e, fmaf(-coef, o[e], d.decay * w));
+            }
+        }
+    }
+}
+
 template <typename T, bool NS_ONLY>
 __global__ __launch_bounds__(EW_THREADS) void apply_kernel(EwArgs args) {
     __shared__ float tile[EW_TILE][EW_TILE + 1];
-    const int tid = threadIdx.x;
     const int t0 = blockIdx.x * args.tiles_per_block;
     const int t1 = min(args.total, t0 + args.tiles_per_block);
     if (t0 >= t1) return;
     int mi = find_matrix(args.prefix, args.nmat, t0);
+    const int jl = ew_col();
 
     for (int t = t0; t < t1; ++t) {
         while (t >= args.prefix[mi + 1]) ++mi;
         const MatDesc& d = args.descs[mi];
         int i0, j0;
         ew_tile_origin(d, t - args.prefix[mi], i0, j0);
-        {
-            const int jl = (tid & 15) * 4;
+        float x[EW_PASSES][EW_GROUP];
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                const int il = (tid >> 4) + 16 * p;
-                const size_t idx = static_cast<size_t>(i0 + il) * d.np + (j0 + jl);
-                float4 v;
-                if (sizeof(T) == 2) {   // X = hi + lo (exact in fp32)
-                    const u32x2_t h = ld_u2(static_cast<const uint16_t*>(d.xop[args.fin]) + idx);
-                    const u32x2_t l = ld_u2(d.xlo + idx);
-                    v = make_float4(__uint_as_float(h.x << 16) + __uint_as_float(l.x << 16),
-                                    __uint_as_float(h.x & 0xffff0000u) + __uint_as_float(l.x & 0xffff0000u),
-                                    __uint_as_float(h.y << 16) + __uint_as_float(l.y << 16),
-                                    __uint_as_float(h.y & 0xffff0000u) + __uint_as_float(l.y & 0xffff0000u));
-                } else {
-                    v = ld_f4(d.x32[args.fin] + idx);
-                }
-                tile[il][jl] = v.x; tile[il][jl + 1] = v.y; tile[il][jl + 2] = v.z; tile[il][jl + 3] = v.w;
+        for (int p = 0; p < EW_PASSES; ++p) {
+            const size_t idx = static_cast<size_t>(i0 + ew_row(p)) * d.np + (j0 + jl);
+            if (sizeof(T) == 2) {   // X = hi + lo (exact in fp32)
+                float h[EW_GROUP], l[EW_GROUP];
+                load8<uint16_t>(d.xop[args.fin], idx, h);
+                load8<uint16_t>(d.xlo, idx, l);
+#pragma unroll
+                for (int e = 0; e < EW_GROUP; ++e) x[p][e] = h[e] + l[e];
+            } else {
+                load8<float>(d.x32[args.fin], idx, x[p]);
             }
         }
-        __syncthreads();
         // with no Newton-Schulz step the output is the normalized input
         const float oscale = args.ns_zero ? G(d.scal)[0] : 1.0f;
-        const int ur0 = d.tall ? j0 : i0;
-        const int uc0 = d.tall ? i0 : j0;
         const float coef = d.apply_coef * oscale;
-        const float decay = d.decay;
-        // one element per thread and pass: a wave writes one 64-element user row
-#pragma unroll 4
-        for (int p = 0; p < EW_TILE * EW_TILE / EW_THREADS; ++p) {
-            const int q = tid + EW_THREADS * p;
-            const int lr = q >> 6, lc = q & 63;
-            const int ur = ur0 + lr, uc = uc0 + lc;
-            if (ur < d.rows && uc < d.cols) {
-                const float o = d.tall ? tile[lc][lr] : tile[lr][lc];
-                const size_t idx = static_cast<size_t>(ur) * d.cols + uc;
-                if (NS_ONLY) {
-                    G(d.out)[idx] = o * oscale;
-                } else {
-                    const float w = Elem<T>::load(d.w, idx);
-                    Elem<T>::store(d.w, idx, fmaf(-coef, o, decay * w));
-                }
+        if (!d.tall) {
+#pragma unroll
+            for (int p = 0; p < EW_PASSES; ++p) apply_group<T, NS_ONLY>(d, coef, oscale, i0 + ew_row(p), j0 + jl, x[p]);
+        } else {
+#pragma unroll
+            for (int p = 0; p < EW_PASSES; ++p)
+#pragma unroll
+                for (int e = 0; e < EW_GROUP; ++e) tile[ew_row(p)][jl + e] = x[p][e];
+            __syncthreads();
+            // caller row j0 + r holds NS column j0 + r: columns i0 + jl + e are NS rows
+#pragma unroll
+            for (int p = 0; p < EW_PASSES; ++p) {
+                float o[EW_GROUP];
+#pragma unroll
+                for (int e = 0; e < EW_GROUP; ++e) o[e] = tile[jl + e][ew_row(p)];
+                apply_group<T, NS_ONLY>(d, coef, oscale, j0 + ew_row(p), i0 + jl, o);
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 

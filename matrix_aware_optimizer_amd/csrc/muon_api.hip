@@ -178,10 +178,9 @@ muon_status build_plan(std::vector<Item>& items, const muon_hparams* hp, bool ns
         d.np = static_cast<int32_t>(s.np);
         d.tall = it.rows > it.cols ? 1 : 0;
         {
-            const uintptr_t va = 4 * es;   // bytes of 4 elements
-            auto ok = [va](const void* ptr) { return ptr == nullptr || reinterpret_cast<uintptr_t>(ptr) % va == 0; };
-            d.uvec = (it.cols % 4 == 0 && ok(it.w) && ok(it.g) && ok(it.mom) &&
-                      (it.out == nullptr || reinterpret_cast<uintptr_t>(it.out) % 16 == 0)) ? 1 : 0;
+            // 8-element groups with 16-byte accesses
+            auto ok = [](const void* ptr) { return ptr == nullptr || reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
+            d.uvec = (it.cols % 8 == 0 && ok(it.w) && ok(it.g) && ok(it.mom) && ok(it.out)) ? 1 : 0;
         }
         const int64_t ewt = (s.mp / EW_TILE) * (s.np / EW_TILE);
         const int64_t tm = s.mp / pad, tn = s.np / pad;

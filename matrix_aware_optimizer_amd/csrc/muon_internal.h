@@ -34,7 +34,7 @@ struct MatDesc {
     int32_t m, n;       // NS frame
     int32_t mp, np;     // NS frame padded to the GEMM tile
     int32_t tall;       // 1 if rows > cols
-    int32_t uvec;       // 1 if cols % 4 == 0 and every caller pointer is 4-element aligned
+    int32_t uvec;       // 1 if cols % 8 == 0 and every caller pointer is 16-byte aligned
     // workspace buffers (NS frame, mp x np, zero-padded).  Step k reads index
     // k & 1 and writes index (k & 1) ^ 1.
     //   fp32: the iterate is x32[k & 1], which is also the MFMA operand.
@@ -183,6 +183,7 @@ __device__ __forceinline__ MUON_GLOBAL T* G(T* p) { return (MUON_GLOBAL T*)p; }
 // assigned across address spaces).
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float4 ld_f4(const float* p) {
     const f32x4_t v = G(reinterpret_cast<const f32x4_t*>(p))[0];
     return make_float4(v.x, v.y, v.z, v.w);

@@ -48,6 +48,8 @@ PROFILE_COMMANDS = [
     "-- python3 $R/bench.py --calibrate-copy",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/cwrite -o copy "
     "-- python3 $R/bench.py --calibrate-copy",
+    "rocprofv3 --kernel-trace --pmc GRBM_COUNT GRBM_GUI_ACTIVE --kernel-include-regex \"ns_gemm_kernel\" "
+    "--output-format csv -d $R/gpurun_out/prof/clock -o clk -- python3 $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline",
     "python3 bench.py --summarize-profiles gpurun_out/prof",
 ]
 
@@ -104,6 +106,29 @@ def _counter_rows(path, name_part=None):
 UPDATE_KERNEL = "ns_gemm_kernel<unsigned short, 2>"
 
 
+def _engine_clock(path):
+    """Average engine clock per kernel from a --kernel-trace --pmc GRBM_COUNT run."""
+    import csv
+    import glob
+    traces = sorted(glob.glob(os.path.join(path, "*kernel_trace.csv")))
+    if not traces:
+        return {}
+    dur = {}
+    with open(traces[0]) as fh:
+        for r in csv.DictReader(fh):
+            dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    acc = {}
+    for r in _counter_rows(path):
+        if r["Counter_Name"] != "GRBM_COUNT" or r["Dispatch_Id"] not in dur:
+            continue
+        ghz = float(r["Counter_Value"]) / 8.0 / dur[r["Dispatch_Id"]]
+        n, tot = acc.get(r["Kernel_Name"], (0, 0.0))
+        acc[r["Kernel_Name"]] = (n + 1, tot + ghz)
+    def short(k):
+        return k.replace("void ", "").replace("muon::(anonymous namespace)::", "").split("(")[0]
+    return {short(k): (n, tot / n) for k, (n, tot) in acc.items()}
+
+
 def summarize_profiles(prof_dir, workload_id, commands):
     """Turn one rocprofv3 session (kernel trace, FETCH_SIZE and WRITE_SIZE runs of
     the update kernel, and the same two counters on a 1 GiB device copy) into
@@ -138,7 +163,7 @@ def summarize_profiles(prof_dir, workload_id, commands):
         "read_bytes_per_launch": int(read_b),
         "write_bytes_per_launch": int(write_b),
         "bytes_per_launch": int(read_b + write_b),
-        "note": f"average over all update launches, {T} per step (the last writes only the fp32 iterate)",
+        "note": f"average over all update launches, {T} per step",
         "commands": commands,
     }
     with open(TRAFFIC_FILE, "w") as fh:
@@ -158,6 +183,13 @@ def summarize_profiles(prof_dir, workload_id, commands):
     lines += ["", f"Update kernel HBM traffic per launch (FETCH_SIZE x {fetch_factor:.3f}, WRITE_SIZE x "
               f"{write_factor:.3f}, factors from a 1 GiB device copy): read {read_b / 1e9:.3f} GB, "
               f"write {write_b / 1e9:.3f} GB.", ""]
+    clock = _engine_clock(os.path.join(prof_dir, "clock"))
+    if clock:
+        lines += ["Engine clock during the Newton-Schulz GEMMs: GRBM_COUNT (summed over the 8 XCDs) / 8 / dispatch",
+                  "duration, averaged over the dispatches of one step.", "",
+                  "| kernel | dispatches | avg GHz |", "|---|---|---|"]
+        lines += [f"| `{k}` | {n} | {ghz:.3f} |" for k, (n, ghz) in sorted(clock.items())]
+        lines += [""]
     out = os.path.join(ROOT, "profiles", f"kernels_{wk.short_name(workload_id)}.md")
     with open(out, "w") as fh:
         fh.write("\n".join(lines))

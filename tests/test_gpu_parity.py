@@ -10,9 +10,12 @@ Tolerances (from the method's arithmetic and the stated bounds):
     the rounded oracle value, plus the share of O's own error that
     lr * s * |dO| can carry into an element.
 Small cases run the oracle in full; the full-size workloads compare sampled
-matrices of the grouped call.
+matrices of the grouped call (the 28672x8192 set through sampled elements and
+the singular-value map, which the oracle computes at any size).
 """
 from __future__ import annotations
+
+import time
 
 import numpy as np
 import pytest
@@ -383,6 +386,97 @@ def test_full_moe_expert_set(gpu_lib):
     _say("full MoE set, 192 matrices")
     # expert 0 gate, expert 7 down, expert 63 up (different per-expert scales)
     _full_workload_check(gpu_lib, wl, [0, 23, 190])
+
+
+def _gram_eigs(x):
+    """Eigenvalues (ascending, fp64) of x^T x for a tall device matrix x."""
+    xd = x.to(torch.float64)
+    g = (xd.T @ xd).cpu().numpy()
+    del xd
+    return np.linalg.eigvalsh(g)
+
+
+def test_full_large_mlp_set(gpu_lib):
+    """16 x 28672x8192 in one grouped call.  The oracle cannot run the iteration
+    at this size inside a test, so it checks what it computes at any size:
+      * M' at sampled positions, to 1 ulp of the once-rounded oracle value;
+      * W' at sampled positions against the oracle's apply with the observed O;
+      * the singular values of O: in exact arithmetic the iteration maps each
+        singular value x of M' / (||M'||_F + eps) through the schedule's odd
+        polynomials (oracle ``phi_schedule``), so sigma(O) must lie inside
+        [min - 0.05, max + 0.05] of that map, and the sorted spectra must agree
+        to 0.05 (the bf16 band).
+    The two 8192 x 8192 Gram matrices are formed in fp64 with torch on the
+    device; their eigenvalues are taken on the host in fp64."""
+    wl = wk.WORKLOADS[5]
+    hp = wl.hp
+    sample = 0
+    t0 = time.time()
+    _say("full large MLP set, 16 x 28672x8192: drawing inputs")
+    W, G, M = [], [], []
+    for i in range(wl.n):
+        d = wk.device_matrix(wl, i, DEV)
+        W.append(d["W"]); G.append(d["G"]); M.append(d["M"])
+    W0 = W[sample].clone()
+    M0 = M[sample].clone()
+    kw = dict(beta=hp["beta"], weight_decay=hp["weight_decay"], schedule=hp["schedule"],
+              scale_rule=hp["scale_rule"], eps=hp["eps"])
+    _say("step 1 (real weights)")
+    ws = gpu_lib.muon_step(W, G, M, lr=hp["lr"], **kw)
+    torch.cuda.synchronize()
+    rows, cols = wl.shapes[sample]
+    rng = np.random.default_rng(5)
+    pos = rng.choice(rows * cols, size=8192, replace=False)
+
+    def at(t):
+        return to_numpy_f32(t.reshape(-1)[torch.from_numpy(pos).to(DEV)]).astype(np.float64)
+
+    Wp, Mp = at(W[sample]), at(M[sample])
+    # second call from the same state: W = 0, lr = 1 gives W' = -s O
+    for i in range(wl.n):
+        W[i].zero_()
+    M[sample].copy_(M0)
+    _say("step 2 (W = 0, lr = 1)")
+    gpu_lib.muon_step(W, G, M, lr=1.0, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    del ws
+    s = orc.scale_factor(rows, cols, hp["scale_rule"])
+    O = W[sample].to(torch.float32) / (-s)
+    Gs = G[sample]
+    for i in range(wl.n):
+        if i != sample:
+            W[i] = G[i] = M[i] = None
+    torch.cuda.empty_cache()
+
+    # M' at sampled positions
+    g_at, m0_at = at(Gs), at(M0)
+    m_ref = orc.rne(orc.momentum_update(m0_at, g_at, orc.as_f32(hp["beta"])), "bf16")
+    assert ulp_distance(Mp.astype(np.float32), m_ref, "bf16").max() <= 1
+
+    # W' at sampled positions: the oracle's apply with the observed O (itself
+    # rounded once to bf16 in the second call, hence the 2^-8 |O| slack)
+    o_at, w0_at = at(O), at(W0)
+    lr32, wd32 = orc.as_f32(hp["lr"]), orc.as_f32(hp["weight_decay"])
+    w_ref = orc.apply_update(w0_at, o_at, lr32, wd32, s)
+    ulp = np.abs(orc.rne(w_ref, "bf16").astype(np.float64)) * 2.0 ** -7 + 2.0 ** -133
+    slack = lr32 * s * np.abs(o_at) * 2.0 ** -8
+    assert np.all(np.abs(Wp - w_ref) <= ulp + slack)
+
+    # singular values: input through the oracle's scalar map vs the GPU's O
+    _say("spectra", f"{time.time() - t0:.1f}s")
+    # the iteration starts from the unrounded M' = beta M + G (exact in fp64 here)
+    M1 = orc.as_f32(hp["beta"]) * M0.to(torch.float64) + Gs.to(torch.float64)
+    ev_in = np.clip(_gram_eigs(M1), 0.0, None)
+    del M1
+    x = np.sqrt(ev_in) / (np.sqrt(ev_in.sum()) + hp["eps"])
+    s_exp = orc.phi_schedule(x, hp["schedule"])
+    s_gpu = np.sqrt(np.clip(_gram_eigs(O), 0.0, None))
+    lo, hi = s_exp.min() - 0.05, s_exp.max() + 0.05
+    dev = np.abs(np.sort(s_gpu) - np.sort(s_exp)).max()
+    _say(f"sigma(O) in [{s_gpu.min():.4f}, {s_gpu.max():.4f}], band [{lo:.4f}, {hi:.4f}], "
+         f"max sorted deviation {dev:.4f}, {time.time() - t0:.1f}s")
+    assert s_gpu.min() >= lo and s_gpu.max() <= hi
+    assert dev <= 0.05
 
 
 def test_bf16_state_rounding_is_round_to_nearest_even(gpu_lib):

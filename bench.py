@@ -398,7 +398,9 @@ def main():
     elem = sum(r * c for r, c in wl.shapes)
     es = 2 if bf16 else 4
     k1_ms = prof["momentum_norm"]["ms"] / max(1, prof["momentum_norm"]["launches"])
-    k5_ms = prof["apply"]["ms"] / max(1, prof["apply"]["launches"])
+    # muon_step's apply runs inside its last update launch; a separate apply launch
+    # only happens for muon_ns and for ns_steps = 0
+    k5_ms = prof["apply"]["ms"] / prof["apply"]["launches"] if prof["apply"]["launches"] else None
 
     out = {
         "metric": "Muon step matrices/s and NS TFLOP/s as % of MI355X bf16 MFMA peak",
@@ -427,7 +429,7 @@ def main():
         "kernel_ms_per_step": {k: round(v["ms"] / args.steps, 4) for k, v in prof.items()},
         "elementwise_gbs": {
             "momentum_norm": round(3 * es * elem / (k1_ms * 1e-3) / 1e9, 1),
-            "apply": round((2 * es + 4) * elem / (k5_ms * 1e-3) / 1e9, 1),
+            "apply": round((2 * es + 4) * elem / (k5_ms * 1e-3) / 1e9, 1) if k5_ms else "fused into the last update",
         },
         "roofline": {
             "kernel": "update (X <- aX + BX)",

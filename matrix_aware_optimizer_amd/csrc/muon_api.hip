@@ -460,7 +460,8 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
         na.b = hp->schedule[k].b;
         na.c = hp->schedule[k].c;
         na.first = k == 0;
-        na.last = k == hp->ns_steps - 1;
+        // muon_step's last update writes W' itself (no apply launch)
+        na.apply = (!ns_only && k == hp->ns_steps - 1) ? 1 : 0;
         na.ping = k & 1;
         na.prefix = d_pre + (nmat + 1);
         na.total = static_cast<int32_t>(pl.total_sym);
@@ -473,8 +474,10 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
         st = timed_launch(4, stream, "update kernel", [&] { return launch_update(dtype, na, stream); });
         if (st != MUON_OK) return st;
     }
-    st = timed_launch(5, stream, "apply kernel", [&] { return launch_apply(dtype, ns_only, ew, ew_grid, stream); });
-    if (st != MUON_OK) return st;
+    if (ns_only || hp->ns_steps == 0) {
+        st = timed_launch(5, stream, "apply kernel", [&] { return launch_apply(dtype, ns_only, ew, ew_grid, stream); });
+        if (st != MUON_OK) return st;
+    }
     g_last_error.clear();
     return MUON_OK;
 }

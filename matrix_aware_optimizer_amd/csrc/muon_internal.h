@@ -74,7 +74,7 @@ struct NsArgs {
     int32_t total;
     float a, b, c;           // this step's coefficients
     int32_t first;           // first step: fold the normalization scale in
-    int32_t last;            // last step: only the fp32 iterate is needed
+    int32_t apply;           // last step of muon_step: write W' = decay W - coef X' instead of X'
     int32_t ping;            // x32 / xop index read by this step; ping ^ 1 is written
 };
 

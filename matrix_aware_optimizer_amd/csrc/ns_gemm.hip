@@ -310,7 +310,8 @@ template <typename T> __device__ inline void st_quad_masked(void* p, size_t i, c
 
 // PH_POLY_LDS is the polynomial with b A added from the staged operand (c != 0);
 // PH_POLY reads A again in the epilogue and serves any c.
-enum Phase { PH_GRAM = 0, PH_POLY = 1, PH_UPDATE = 2, PH_POLY_LDS = 3 };
+// PH_UPDATE_APPLY is the last update of muon_step, writing W' instead of X'.
+enum Phase { PH_GRAM = 0, PH_POLY = 1, PH_UPDATE = 2, PH_POLY_LDS = 3, PH_UPDATE_APPLY = 4 };
 
 struct NoHook {
     template <typename A> __device__ __forceinline__ void operator()(int, const lds_byte_t*, A&) const {}
@@ -794,9 +795,138 @@ __device__ __attribute__((always_inline)) void update_epilogue(f32x16_t (&acc)[E
             }
 }
 
+// Last update of muon_step: W' = decay W - coef X' goes straight from the
+// accumulators into the caller's weight (user frame), in place of storing the
+// iterate and running the apply kernel.  X' = u acc in fp32, W' rounded once.
+//   untransposed matrix: the direct layout after the quad swap gives 8
+//     consecutive NS columns of one row = 8 consecutive user columns;
+//   tall matrix (NS frame = user transposed): lanes l and l ^ 32 swap one quad
+//     so each owns 8 consecutive NS rows of one NS column = 8 consecutive user
+//     columns of one user row.
+// With the 16-byte flag (cols % 8 == 0, aligned pointers) a group is inside or
+// outside the matrix as a whole; otherwise each element is bounds-checked.
+template <typename T> struct WeightIO;
+template <> struct WeightIO<uint16_t> {
+    static __device__ inline void load8(const void* p, float (&v)[8]) {
+        const u32x4 q = G(static_cast<const u32x4*>(p))[0];
+        const unsigned w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = __uint_as_float(w[k] << 16);
+            v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+    }
+    static __device__ inline void store8(void* p, const float (&v)[8]) {
+        G(static_cast<u32x4*>(p))[0] = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                             pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    }
+    static __device__ inline float load1(const void* p) { return bf16_to_f32(G(static_cast<const uint16_t*>(p))[0]); }
+    static __device__ inline void store1(void* p, float v) { G(static_cast<uint16_t*>(p))[0] = f32_to_bf16(v); }
+};
+template <> struct WeightIO<float> {
+    static __device__ inline void load8(const void* p, float (&v)[8]) {
+        const float4 a = ld_f4(static_cast<const float*>(p)), b = ld_f4(static_cast<const float*>(p) + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    static __device__ inline void store8(void* p, const float (&v)[8]) {
+        st_f4(static_cast<float*>(p), make_float4(v[0], v[1], v[2], v[3]));
+        st_f4(static_cast<float*>(p) + 4, make_float4(v[4], v[5], v[6], v[7]));
+    }
+    static __device__ inline float load1(const void* p) { return G(static_cast<const float*>(p))[0]; }
+    static __device__ inline void store1(void* p, float v) { G(static_cast<float*>(p))[0] = v; }
+};
+
+template <typename E, typename T>
+__device__ __attribute__((always_inline)) void apply_epilogue(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
+                                                              const MatDesc& d, float u) {
+    using IO = WeightIO<T>;
+    const Coords<E> q(row0, col0);
+    const bool hh = (threadIdx.x >> 5) & 1;
+    const bool odd = odd_quad();
+    const int mbase = q.raw_row - (hh ? 4 : 0);
+    const float coef = d.apply_coef, decay = d.decay;
+    const bool tall = d.tall != 0, vec = d.uvec != 0;
+    char* const w = static_cast<char*>(d.w);
+#pragma unroll
+    for (int i = 0; i < E::SM; ++i) {
+        // user-frame origin of each 8-element group of this row block
+        int ur[E::SN * 2], uc[E::SN * 2];
+#pragma unroll
+        for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+            for (int gg = 0; gg < 2; ++gg) {
+                if (tall) {
+                    ur[j * 2 + gg] = q.raw_col + 32 * j;
+                    uc[j * 2 + gg] = mbase + 32 * i + 8 * (2 * gg + hh);
+                } else {
+                    ur[j * 2 + gg] = q.tr_row + 32 * i + 8 * (2 * gg + odd);
+                    uc[j * 2 + gg] = q.tr_col + 32 * j - (odd ? 4 : 0);
+                }
+            }
+        // read the weight groups of this row block first
+        float wv[E::SN * 2][8];
+#pragma unroll
+        for (int k = 0; k < E::SN * 2; ++k) {
+            const bool in = ur[k] < d.rows && uc[k] < d.cols;
+            const size_t idx = static_cast<size_t>(ur[k]) * d.cols + uc[k];
+            if (vec) {
+                if (in) IO::load8(w + idx * sizeof(T), wv[k]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    wv[k][e] = (in && uc[k] + e < d.cols) ? IO::load1(w + (idx + e) * sizeof(T)) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+            for (int gg = 0; gg < 2; ++gg) {
+                const int k = j * 2 + gg;
+                float r0[4], r1[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    r0[p] = u * acc[i][j][8 * gg + p];
+                    r1[p] = u * acc[i][j][8 * gg + 4 + p];
+                }
+                float x[8];
+                if (tall) {
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float rcv = __uint_as_float(swap_xor32(__float_as_uint(hh ? r0[p] : r1[p])));
+                        x[p] = hh ? rcv : r0[p];
+                        x[4 + p] = hh ? r1[p] : rcv;
+                    }
+                } else {
+                    quad_transpose(r0);
+                    quad_transpose(r1);
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const float keep = odd ? r1[p] : r0[p];
+                        const float recv = __uint_as_float(swap_xor4(__float_as_uint(odd ? r0[p] : r1[p])));
+                        x[p] = odd ? recv : keep;
+                        x[4 + p] = odd ? keep : recv;
+                    }
+                }
+                if (ur[k] >= d.rows || uc[k] >= d.cols) continue;
+                float o[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] = fmaf(-coef, x[e], decay * wv[k][e]);
+                const size_t idx = static_cast<size_t>(ur[k]) * d.cols + uc[k];
+                if (vec) {
+                    IO::store8(w + idx * sizeof(T), o);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (uc[k] + e < d.cols) IO::store1(w + (idx + e) * sizeof(T), o[e]);
+                }
+            }
+    }
+}
+
 template <typename T, int PHASE>
 __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, int t, u32x4* lds) {
-    using E = Engine<T, PHASE == PH_UPDATE>;
+    constexpr bool UPD = PHASE == PH_UPDATE || PHASE == PH_UPDATE_APPLY;
+    using E = Engine<T, UPD>;
     const int mi = find_matrix(args.prefix, args.nmat, t);
     const MatDesc& d = args.descs[mi];
     const int local = t - args.prefix[mi];
@@ -804,7 +934,7 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
     const int ping = args.ping;
 
     int ti, tj;
-    if (PHASE == PH_UPDATE) {
+    if (UPD) {
         grouped_decode(local, mp / E::BM, np / E::BN, ti, tj);
     } else {
         sym_decode(local, mp / E::BM, ti, tj);
@@ -843,13 +973,16 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
             E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, mp / E::KS, lds, acc, init, NoHook{});
         // first step: X1 = s (a M' + B0 M') with M' unscaled in the iterate and operand copy
         const float u = args.first ? G(d.scal)[0] : 1.0f;
-        update_epilogue<E, T>(acc, row0, col0, d.xop[ping ^ 1], d.xlo, np, u);
+        if (PHASE == PH_UPDATE_APPLY)
+            apply_epilogue<E, T>(acc, row0, col0, d, u);
+        else
+            update_epilogue<E, T>(acc, row0, col0, d.xop[ping ^ 1], d.xlo, np, u);
     }
 }
 
 template <typename T, int PHASE>
 __global__ __launch_bounds__(GEMM_THREADS, 1) void ns_gemm_kernel(NsArgs args) {
-    using E = Engine<T, PHASE == PH_UPDATE>;
+    using E = Engine<T, PHASE == PH_UPDATE || PHASE == PH_UPDATE_APPLY>;
     __shared__ u32x4 lds[E::LDS_CHUNKS];
     const int t = xcd_run_remap(blockIdx.x, gridDim.x);
     if (t < args.total) process_tile<T, PHASE>(args, t, lds);
@@ -874,6 +1007,9 @@ hipError_t launch_poly(int dtype, const NsArgs& args, hipStream_t s) {
     if (args.c != 0.0f && std::isfinite(f)) return launch_phase<PH_POLY_LDS>(dtype, args, s);
     return launch_phase<PH_POLY>(dtype, args, s);
 }
-hipError_t launch_update(int dtype, const NsArgs& args, hipStream_t s) { return launch_phase<PH_UPDATE>(dtype, args, s); }
+hipError_t launch_update(int dtype, const NsArgs& args, hipStream_t s) {
+    if (args.apply) return launch_phase<PH_UPDATE_APPLY>(dtype, args, s);
+    return launch_phase<PH_UPDATE>(dtype, args, s);
+}
 
 }  // namespace muon

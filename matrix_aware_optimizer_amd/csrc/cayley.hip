@@ -311,15 +311,16 @@ __global__ __launch_bounds__(CY_THREADS) void cy_out(CayleyArgs a) {
 // ---------------------------------------------------------------------------
 // The 2K x 2K solve, one workgroup per matrix, fp64.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
-    __shared__ int perm[2 * CAYLEY_MAX_K];
-    __shared__ double prow[3 * CAYLEY_MAX_K];     // pivot row of C (from column j) and of the right-hand side
-    __shared__ double lmul[2 * CAYLEY_MAX_K];     // multipliers of the rows below the pivot
-    __shared__ double ta[32][33], tb[32][33];     // tiles of the right-hand-side product
-    const CayleyDesc& d = a.descs[blockIdx.x];
+// The 2K x 2K system in global memory: LU with partial pivoting (any K).
+__device__ void solve_global(const CayleyDesc& d, double cc, double* arena) {
+    int* perm = reinterpret_cast<int*>(arena);                          // 2K
+    double* prow = arena + CAYLEY_MAX_K;                                // 3K: pivot row of C and of the right-hand side
+    double* lmul = prow + 3 * CAYLEY_MAX_K;                             // 2K: multipliers of the rows below the pivot
+    double (*ta)[33] = reinterpret_cast<double (*)[33]>(lmul + 2 * CAYLEY_MAX_K);   // 32 x 33 product tiles
+    double (*tb)[33] = ta + 32;
     const int K = d.K, K2 = 2 * K, tid = threadIdx.x;
     const size_t kk = static_cast<size_t>(K) * K;
-    const double c = a.c;
+    const double c = cc;
     double* C = d.cmat;       // 2K x 2K
     double* R = d.rhs;        // 2K x K
     double* BW = d.bw;        // 2K x K
@@ -436,6 +437,202 @@ __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
         const int j = static_cast<int>(q / K), col = static_cast<int>(q % K);
         G(Y)[q] = static_cast<float>(BW[q] + R[static_cast<size_t>(perm[j]) * K + col]);
     }
+}
+
+
+// ---------------------------------------------------------------------------
+// K <= 128: block elimination.  With WW = W^T W, WV = W^T V, VV = V^T V and
+// VW = WV^T, the system C [z1; z2] = [r1; r2] has the K x K blocks
+//   C11 = I + c WV,  C12 = c WW,  C21 = -c VV,  C22 = I - c VW,
+// and B W = [WW; -VW].  Eliminating z1:
+//   X = C11^-1 C12,  y = C11^-1 r1,  S = C22 - C21 X,  r' = r2 - C21 y,
+//   z2 = S^-1 r',  z1 = y - X z2.
+// C11 and S are inverted by Gauss-Jordan with partial pivoting in LDS (a K x K
+// fp64 matrix fits); the products are K x K GEMMs through LDS tiles.  Every
+// block is nonsingular: det C = det(I + c A) != 0 for skew A, C11 = I + c WV
+// with WV skew up to rounding, and det C = det C11 det S.
+// ---------------------------------------------------------------------------
+constexpr int CY_LDS_K = 128;
+
+// out = base_scale * base + (identity ? I : 0) + alpha * A B   (K x K, pitch K, fp64, global).
+// out may be base (each element is read and written by one thread) but not A or B.
+// Thread t owns the 4 x 4 block at rows 4 (t / 32), columns 4 (t % 32).
+__device__ void kk_gemm(int K, double* out, const double* A, const double* B, double alpha, const double* base,
+                        double base_scale, bool identity, double* lds) {
+    constexpr int KC = 16;
+    double (*As)[KC + 1] = reinterpret_cast<double (*)[KC + 1]>(lds);                     // 128 x 17
+    double (*Bs)[CY_LDS_K + 4] = reinterpret_cast<double (*)[CY_LDS_K + 4]>(lds + CY_LDS_K * (KC + 1));   // 16 x 132
+    const int tid = threadIdx.x, r0 = 4 * (tid / 32), c0 = 4 * (tid % 32);
+    double acc[4][4] = {};
+    for (int l0 = 0; l0 < K; l0 += KC) {
+        for (int q = tid; q < CY_LDS_K * KC; q += CY_SOLVE_THREADS) {
+            const int i = q / KC, l = q % KC;
+            As[i][l] = (i < K && l0 + l < K) ? A[static_cast<size_t>(i) * K + l0 + l] : 0.0;
+            const int bl = q / CY_LDS_K, bj = q % CY_LDS_K;
+            Bs[bl][bj] = (l0 + bl < K && bj < K) ? B[static_cast<size_t>(l0 + bl) * K + bj] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int l = 0; l < KC; ++l) {
+            double av[4], bv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) av[r] = As[r0 + r][l];
+#pragma unroll
+            for (int cI = 0; cI < 4; ++cI) bv[cI] = Bs[l][c0 + cI];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int cI = 0; cI < 4; ++cI) acc[r][cI] = fma(av[r], bv[cI], acc[r][cI]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int cI = 0; cI < 4; ++cI) {
+            const int i = r0 + r, j = c0 + cI;
+            if (i >= K || j >= K) continue;
+            const size_t q = static_cast<size_t>(i) * K + j;
+            double v = alpha * acc[r][cI];
+            if (base) v += base_scale * base[q];
+            if (identity && i == j) v += 1.0;
+            out[q] = v;
+        }
+    __syncthreads();
+}
+
+// out = ((identity ? I : 0) + scale * src)^-1 by Gauss-Jordan with partial pivoting,
+// in LDS.  Rows are swapped in place; the columns are unscrambled in reverse order
+// at the end.  out may be src.
+__device__ void kk_gj_inverse(int K, double* out, const double* src, double scale, bool identity, double* lds) {
+    double* M = lds;                       // K x K, pitch K
+    double* prow = M + CY_LDS_K * CY_LDS_K;
+    double* colf = prow + CY_LDS_K;
+    int* piv = reinterpret_cast<int*>(colf + CY_LDS_K);
+    const int tid = threadIdx.x;
+    for (int q = tid; q < K * K; q += CY_SOLVE_THREADS) {
+        const int i = q / K, j = q % K;
+        M[q] = (identity && i == j ? 1.0 : 0.0) + scale * src[q];
+    }
+    __syncthreads();
+    for (int j = 0; j < K; ++j) {
+        if (tid < 64) {   // one wave: largest |M[i][j]|, i >= j (ties to the smaller i)
+            double best = -1.0;
+            int bidx = K;
+            for (int i = j + tid; i < K; i += 64) {
+                const double v = fabs(M[i * K + j]);
+                if (v > best) { best = v; bidx = i; }
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const double ov = __shfl_xor(best, off, 64);
+                const int oi = __shfl_xor(bidx, off, 64);
+                if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+            }
+            if (tid == 0) piv[j] = bidx;
+        }
+        __syncthreads();
+        const int p = piv[j];
+        if (p != j && tid < K) {
+            const double t = M[j * K + tid];
+            M[j * K + tid] = M[p * K + tid];
+            M[p * K + tid] = t;
+        }
+        __syncthreads();
+        const double inv = 1.0 / M[j * K + j];
+        if (tid < K) {
+            prow[tid] = tid == j ? inv : M[j * K + tid] * inv;
+            colf[tid] = tid == j ? 0.0 : M[tid * K + j];
+        }
+        __syncthreads();
+        for (int q = tid; q < K * K; q += CY_SOLVE_THREADS) {
+            const int i = q / K, k = q % K;
+            if (i == j) M[q] = prow[k];
+            else if (k == j) M[q] = -colf[i] * inv;
+            else M[q] -= colf[i] * prow[k];
+        }
+        __syncthreads();
+    }
+    for (int j = K - 1; j >= 0; --j) {
+        const int p = piv[j];
+        if (p != j && tid < K) {
+            const double t = M[tid * K + j];
+            M[tid * K + j] = M[tid * K + p];
+            M[tid * K + p] = t;
+        }
+        __syncthreads();
+    }
+    for (int q = tid; q < K * K; q += CY_SOLVE_THREADS) out[q] = M[q];
+    __syncthreads();
+}
+
+__device__ void solve_blocked(const CayleyDesc& d, double c, double* lds) {
+    const int K = d.K, tid = threadIdx.x;
+    const size_t kk = static_cast<size_t>(K) * K;
+    // K x K fp64 blocks in the workspace (pitch K)
+    double* WV = d.cmat;            // then y
+    double* VV = d.cmat + kk;
+    double* C11i = d.cmat + 2 * kk; // then r'
+    double* Xm = d.cmat + 3 * kk;
+    double* R1 = d.rhs;             // then S, then S^-1
+    double* R2 = d.rhs + kk;        // then z1
+    double* WW = d.bw;              // B W = [WW; bwb], bwb = -VW
+    double* bwb = d.bw + kk;
+    // 1. WW, WV, VV and B W from the partials (fp64 sums in row-block order)
+    for (size_t q = tid; q < kk; q += CY_SOLVE_THREADS) {
+        const int i = static_cast<int>(q / K), j = static_cast<int>(q % K);
+        double ww = 0.0, wv = 0.0, vw = 0.0, vv = 0.0;   // (W^T W)ij, (W^T V)ij, (W^T V)ji, (V^T V)ij
+        for (int rb = 0; rb < d.nrb; ++rb) {
+            const float* pr = d.part + static_cast<size_t>(rb) * 3 * kk;
+            ww += G(pr)[q];
+            wv += G(pr)[kk + q];
+            vw += G(pr)[kk + static_cast<size_t>(j) * K + i];
+            vv += G(pr)[2 * kk + q];
+        }
+        WV[q] = wv;
+        VV[q] = vv;
+        WW[q] = ww;
+        bwb[q] = -vw;
+    }
+    __syncthreads();
+    // 2. right-hand side r = B W - c (B U)(B W):
+    //    r1 = WW - c (WV WW - WW VW),  r2 = -VW - c (VW VW - VV WW)
+    kk_gemm(K, R1, WV, WW, -c, WW, 1.0, false, lds);
+    kk_gemm(K, R1, WW, bwb, -c, R1, 1.0, false, lds);      // + c WW VW = - c WW bwb
+    kk_gemm(K, R2, bwb, bwb, -c, bwb, 1.0, false, lds);    // VW VW = bwb bwb
+    kk_gemm(K, R2, VV, WW, c, R2, 1.0, false, lds);
+    // 3. C11^-1 = (I + c WV)^-1
+    kk_gj_inverse(K, C11i, WV, c, true, lds);
+    // 4. X = C11^-1 (c WW), y = C11^-1 r1 (into WV's block, no longer needed)
+    kk_gemm(K, Xm, C11i, WW, c, nullptr, 0.0, false, lds);
+    double* y = WV;
+    kk_gemm(K, y, C11i, R1, 1.0, nullptr, 0.0, false, lds);
+    // 5. S = C22 - C21 X = I + c bwb + c VV X;  r' = r2 + c VV y
+    double* S = R1;
+    kk_gemm(K, S, VV, Xm, c, bwb, c, true, lds);
+    double* rp = C11i;
+    kk_gemm(K, rp, VV, y, c, R2, 1.0, false, lds);
+    // 6. z2 = S^-1 r',  z1 = y - X z2
+    kk_gj_inverse(K, S, S, 1.0, false, lds);
+    double* z2 = VV;
+    kk_gemm(K, z2, S, rp, 1.0, nullptr, 0.0, false, lds);
+    double* z1 = R2;
+    kk_gemm(K, z1, Xm, z2, -1.0, y, 1.0, false, lds);
+    // 7. Y = B W + Z, fp32 for the final pass (rows 0..K-1: top, K..2K-1: bottom)
+    float* Y = d.small + K + kk;
+    for (size_t q = tid; q < kk; q += CY_SOLVE_THREADS) {
+        G(Y)[q] = static_cast<float>(WW[q] + z1[q]);
+        G(Y)[kk + q] = static_cast<float>(bwb[q] + z2[q]);
+    }
+}
+
+__global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
+    __shared__ double arena[CY_LDS_K * CY_LDS_K + 3 * CY_LDS_K];
+    const CayleyDesc& d = a.descs[blockIdx.x];
+    if (d.K <= CY_LDS_K)
+        solve_blocked(d, a.c, arena);
+    else
+        solve_global(d, a.c, arena);
 }
 
 }  // namespace

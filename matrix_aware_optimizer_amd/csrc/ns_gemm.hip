@@ -795,6 +795,87 @@ __device__ __attribute__((always_inline)) void update_epilogue(f32x16_t (&acc)[E
             }
 }
 
+// bf16 update epilogue staged through LDS.  Stores whose lanes each hold 16 bytes
+// of a different row (the register layout) reach about a third of the per-CU
+// store rate of row-contiguous ones, so the tile goes through LDS: hi' is written
+// there in the register layout, read back as whole 512-byte tile rows (two per
+// wave instruction) and stored; then the same for lo', kept in registers
+// meanwhile.  Staged row r of the tile sits at r * 512 bytes with its 16-byte
+// chunk c at position c ^ (r & 31).
+__device__ __forceinline__ int stage_off(int r, int chunk) { return r * 512 + ((chunk ^ (r & 31)) << 4); }
+
+template <typename E>
+__device__ __forceinline__ void stage_copy_out(const lds_byte_t* L, uint16_t* dst, int row0, int col0, size_t np) {
+    constexpr int CHUNKS = E::BM * E::BN / 8;   // 16-byte chunks of the tile
+#pragma unroll 4
+    for (int q = threadIdx.x; q < CHUNKS; q += GEMM_THREADS) {
+        const int r = q >> 5, c = q & 31;
+        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(L + stage_off(r, c));
+        G(reinterpret_cast<u32x4*>(dst + static_cast<size_t>(row0 + r) * np + col0 + 8 * c))[0] = v;
+    }
+}
+
+template <typename E>
+__device__ __attribute__((always_inline)) void update_epilogue_staged(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
+                                                                      uint16_t* hi_out, uint16_t* lo_out, size_t np,
+                                                                      float u, u32x4* lds) {
+    static_assert(E::BN * 2 == 512 && E::BM * 512 <= E::LDS_CHUNKS * 16, "a staged tile row is 512 bytes");
+    const Coords<E> q(row0, col0);
+    const bool odd = odd_quad();
+    lds_byte_t* L = (lds_byte_t*)lds;
+    u32x4 lo[E::SM][E::SN][2];
+    __syncthreads();   // every wave is done reading the operand slabs
+#pragma unroll
+    for (int i = 0; i < E::SM; ++i)
+#pragma unroll
+        for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+            for (int gg = 0; gg < 2; ++gg) {
+                float v0[4], v1[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    v0[p] = acc[i][j][8 * gg + p];
+                    v1[p] = acc[i][j][8 * gg + 4 + p];
+                }
+                quad_transpose(v0);
+                quad_transpose(v1);
+                float x[8];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float keep = odd ? v1[p] : v0[p];
+                    const float recv = __uint_as_float(swap_xor4(__float_as_uint(odd ? v0[p] : v1[p])));
+                    x[p] = odd ? recv : keep;
+                    x[4 + p] = odd ? keep : recv;
+                }
+                unsigned h[4], l[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const float o0 = u * x[2 * p], o1 = u * x[2 * p + 1];
+                    h[p] = pack_bf16x2(o0, o1);
+                    l[p] = pack_bf16x2(o0 - __uint_as_float(h[p] << 16), o1 - __uint_as_float(h[p] & 0xffff0000u));
+                }
+                const int r = q.tr_row - row0 + 32 * i + 8 * (2 * gg + odd);
+                const int c = (q.tr_col - col0 + 32 * j - (odd ? 4 : 0)) >> 3;
+                *(__attribute__((address_space(3))) u32x4*)(L + stage_off(r, c)) = u32x4{h[0], h[1], h[2], h[3]};
+                lo[i][j][gg] = u32x4{l[0], l[1], l[2], l[3]};
+            }
+    __syncthreads();
+    stage_copy_out<E>(L, hi_out, row0, col0, np);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < E::SM; ++i)
+#pragma unroll
+        for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+            for (int gg = 0; gg < 2; ++gg) {
+                const int r = q.tr_row - row0 + 32 * i + 8 * (2 * gg + odd);
+                const int c = (q.tr_col - col0 + 32 * j - (odd ? 4 : 0)) >> 3;
+                *(__attribute__((address_space(3))) u32x4*)(L + stage_off(r, c)) = lo[i][j][gg];
+            }
+    __syncthreads();
+    stage_copy_out<E>(L, lo_out, row0, col0, np);
+}
+
 // Last update of muon_step: W' = decay W - coef X' goes straight from the
 // accumulators into the caller's weight (user frame), in place of storing the
 // iterate and running the apply kernel.  X' = u acc in fp32, W' rounded once.
@@ -973,8 +1054,10 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
             E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, mp / E::KS, lds, acc, init, NoHook{});
         // first step: X1 = s (a M' + B0 M') with M' unscaled in the iterate and operand copy
         const float u = args.first ? G(d.scal)[0] : 1.0f;
-        if (PHASE == PH_UPDATE_APPLY)
+        if constexpr (PHASE == PH_UPDATE_APPLY)
             apply_epilogue<E, T>(acc, row0, col0, d, u);
+        else if constexpr (sizeof(T) == 2)
+            update_epilogue_staged<E>(acc, row0, col0, static_cast<uint16_t*>(d.xop[ping ^ 1]), d.xlo, np, u, lds);
         else
             update_epilogue<E, T>(acc, row0, col0, d.xop[ping ^ 1], d.xlo, np, u);
     }

@@ -13,7 +13,8 @@
 // writes p, m, v.  The work is split into ADAMW_CHUNK-element chunks
 // (concatenated over tensors, per-tensor prefix sums); each block walks chunks
 // with a grid stride, each thread handles 4 quads of 4 consecutive elements,
-// with 8- or 16-byte accesses when the tensor is aligned for them.
+// with 8- or 16-byte accesses when the tensor is aligned for them.  In a whole,
+// aligned chunk all of a thread's loads are issued before its first store.
 #include "muon_internal.h"
 
 namespace muon {
@@ -67,8 +68,34 @@ __global__ __launch_bounds__(ADAMW_THREADS) void adamw_kernel(AdamWArgs args) {
         float* __restrict__ mp = d.m;
         float* __restrict__ vp = d.v;
         const int64_t numel = d.numel;
+        constexpr int QUADS = ADAMW_CHUNK / (4 * ADAMW_THREADS);
+        if (d.vec && base + ADAMW_CHUNK <= numel) {
+            // whole chunk: every load of the thread's quads is issued before any store
+            float4 p[QUADS], g[QUADS], m[QUADS], v[QUADS];
 #pragma unroll
-        for (int k = 0; k < ADAMW_CHUNK / (4 * ADAMW_THREADS); ++k) {
+            for (int k = 0; k < QUADS; ++k) {
+                const int64_t e0 = base + 4 * (tid + k * ADAMW_THREADS);
+                p[k] = PElem<T>::load4(pp, e0);
+                g[k] = PElem<T>::load4(gp, e0);
+                m[k] = ld_f4(mp + e0);
+                v[k] = ld_f4(vp + e0);
+            }
+#pragma unroll
+            for (int k = 0; k < QUADS; ++k) {
+                const int64_t e0 = base + 4 * (tid + k * ADAMW_THREADS);
+                float4 o;
+                o.x = f(p[k].x, g[k].x, m[k].x, v[k].x);
+                o.y = f(p[k].y, g[k].y, m[k].y, v[k].y);
+                o.z = f(p[k].z, g[k].z, m[k].z, v[k].z);
+                o.w = f(p[k].w, g[k].w, m[k].w, v[k].w);
+                PElem<T>::store4(pp, e0, o);
+                st_f4(mp + e0, m[k]);
+                st_f4(vp + e0, v[k]);
+            }
+            continue;
+        }
+#pragma unroll
+        for (int k = 0; k < QUADS; ++k) {
             const int64_t e0 = base + 4 * (tid + k * ADAMW_THREADS);
             if (e0 >= numel) break;
             if (d.vec && e0 + 3 < numel) {

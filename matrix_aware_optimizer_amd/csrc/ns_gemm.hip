@@ -1022,23 +1022,26 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
     }
     const int row0 = ti * E::BM, col0 = tj * E::BN;
 
+    // k runs over the real extent rounded up to a k-step, not the tile padding: the
+    // padding of X, A and B is zero, so the skipped k-steps would add nothing
+    const int ks_m = (d.m + E::KS - 1) / E::KS, ks_n = (d.n + E::KS - 1) / E::KS;
     f32x16_t acc[E::SM][E::SN];
     if (PHASE == PH_GRAM) {
         const char* X = static_cast<const char*>(d.xop[ping]);
         const size_t ld = static_cast<size_t>(np) * sizeof(T);
-        E::run(X + row0 * ld, ld, X + col0 * ld, ld, np * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc, ZeroInit{}, NoHook{});
+        E::run(X + row0 * ld, ld, X + col0 * ld, ld, ks_n, lds, acc, ZeroInit{}, NoHook{});
         // first step: X0 = s * M' is folded in as A0 = s^2 M' M'^T
         const float scale = args.first ? G(d.scal)[0] * G(d.scal)[0] : 1.0f;
         sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.amat, mp, scale, nullptr, 0.0f, 0.0f);
     } else if (PHASE == PH_POLY) {
         const char* A = static_cast<const char*>(d.amat);
         const size_t ld = static_cast<size_t>(mp) * sizeof(T);
-        E::run(A + row0 * ld, ld, A + col0 * ld, ld, mp * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc, ZeroInit{}, NoHook{});
+        E::run(A + row0 * ld, ld, A + col0 * ld, ld, ks_m, lds, acc, ZeroInit{}, NoHook{});
         sym_epilogue<E, T, true>(acc, row0, col0, ti == tj, d.bmat, mp, 1.0f, d.amat, args.b, args.c);
     } else if (PHASE == PH_POLY_LDS) {
         const char* A = static_cast<const char*>(d.amat);
         const size_t ld = static_cast<size_t>(mp) * sizeof(T);
-        E::run(A + row0 * ld, ld, A + col0 * ld, ld, mp * (int)sizeof(T) / (CHUNKS_PER_ROW * 16), lds, acc, ZeroInit{},
+        E::run(A + row0 * ld, ld, A + col0 * ld, ld, ks_m, lds, acc, ZeroInit{},
                PolyAddend<E, T>{row0 / E::KS, args.b / args.c});
         sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.bmat, mp, args.c, nullptr, 0.0f, 0.0f);
     } else {
@@ -1048,10 +1051,10 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         const UpdateInit<E, T> init{sizeof(T) == 2 ? static_cast<const void*>(d.xlo) : static_cast<const void*>(d.x32[ping]),
                                     static_cast<size_t>(np), row0, col0, args.a};
         if (sizeof(T) == 2)
-            E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, mp / E::KS, lds, acc, init,
+            E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, ks_m, lds, acc, init,
                    HiAddend<E>{row0 / E::KS, args.a});
         else
-            E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, mp / E::KS, lds, acc, init, NoHook{});
+            E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, ks_m, lds, acc, init, NoHook{});
         // first step: X1 = s (a M' + B0 M') with M' unscaled in the iterate and operand copy
         const float u = args.first ? G(d.scal)[0] : 1.0f;
         if constexpr (PHASE == PH_UPDATE_APPLY)

@@ -17,8 +17,9 @@
 // v_mfma_f32_32x32x2_f32, fp32 accumulation).  A k-step stages 128 bytes of
 // every k-contiguous operand row (or 64 / 32 k-rows of a k-major operand, one
 // 512-byte tile row each) in LDS with direct global->LDS loads
-// (global_load_lds_dwordx4, no VGPR staging), double-buffered; the next
-// k-step's loads are spread between the current one's MFMA groups, and MFMA
+// (global_load_lds_dwordx4, no VGPR staging) into a ring of five slabs (one
+// slab = one operand's k-step); the loads of the next Q slab and of the P slab
+// after it are spread between the current k-step's MFMA groups, and MFMA
 // fragments are double-buffered in registers.
 //
 // LDS layouts.  k-contiguous rows: 16-byte chunks XOR-swizzled with bits 1..3
@@ -33,9 +34,12 @@
 //
 // Epilogues work from registers: a 4 x 4 transpose inside each lane quad
 // (DPP) turns a lane's 4 rows x 1 column of a 32 x 32 block into 1 row x 4
-// columns, for 16-byte (fp32) and 8-byte (bf16) row-contiguous accesses.  The
-// mirrored half of a symmetric output is stored from the untransposed layout.
-// Buffers are zero-padded to the block tile, so there are no edge masks.
+// columns (16-byte fp32 accesses); for bf16 a swap between lanes c and c ^ 4
+// then gives each lane 8 columns (16 bytes).  The mirrored half of a symmetric
+// output is stored from the untransposed layout.  The bf16 update stages its
+// output through LDS and stores whole tile rows.  Buffers are zero-padded to
+// the block tile, so there are no edge masks, and k-loops run over the real
+// extent rounded up to a k-step.
 //
 // Grouping: one launch covers every matrix of the call.  The tile space is the
 // concatenation of all matrices' tiles (per-matrix prefix sums, largest
@@ -575,7 +579,7 @@ __device__ __forceinline__ void sym_epilogue(f32x16_t (&acc)[E::SM][E::SN], int 
 // X' = u (a X + B X).  a X enters the accumulators before or during the
 // k-loop, so the epilogue only scales and stores.
 //   fp32: the iterate is x32[ping] (also the operand); a X is read into the
-//         accumulators while the first operand stage loads (UpdateInit), and
+//         accumulators while the first operand slabs load (UpdateInit), and
 //         X' goes to x32[ping ^ 1].
 //   bf16: the iterate is the pair hi + lo (hi = xop[ping], the operand copy,
 //         lo = xlo).  a lo is read into the accumulators at the start; a hi is

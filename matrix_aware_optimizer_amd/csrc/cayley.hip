@@ -139,27 +139,46 @@ __global__ __launch_bounds__(CY_THREADS) void cy_reduce(CayleyArgs a) {
 
 // column sums of G and W over a row block (thread j owns column j)
 __global__ __launch_bounds__(CY_THREADS) void cy_colsum(CayleyArgs a) {
+    __shared__ float part[2][CY_THREADS];
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
-    const int rb = local, j = threadIdx.x;
-    if (j >= d.K) return;
+    const int rb = local, K = d.K, tid = threadIdx.x;
+    // column j = tid % K; the CY_THREADS / K row subsets of the block are summed
+    // separately (rows s, s + S, ...) and combined in a fixed order
+    const int S = max(1, CY_THREADS / K), j = tid % K, sub = tid / K;
     const int rs = rb * CY_RB, re = min(d.N, rs + CY_RB);
     float sg = 0.0f, sw = 0.0f;
-    for (int r = rs; r < re; ++r) {
-        const size_t idx = static_cast<size_t>(r) * d.K + j;
-        sg += G(d.gf)[idx];
-        sw += G(d.wf)[idx];
+    if (sub < S) {
+#pragma unroll 8
+        for (int r = rs + sub; r < re; r += S) {
+            const size_t idx = static_cast<size_t>(r) * K + j;
+            sg += G(d.gf)[idx];
+            sw += G(d.wf)[idx];
+        }
     }
-    G(d.colpart)[(static_cast<size_t>(rb) * 2 + 0) * d.K + j] = sg;
-    G(d.colpart)[(static_cast<size_t>(rb) * 2 + 1) * d.K + j] = sw;
+    part[0][tid] = sg;
+    part[1][tid] = sw;
+    __syncthreads();
+    if (tid < K) {
+        float tg = 0.0f, tw = 0.0f;
+        for (int k = 0; k < S; ++k) {
+            tg += part[0][k * K + tid];
+            tw += part[1][k * K + tid];
+        }
+        G(d.colpart)[(static_cast<size_t>(rb) * 2 + 0) * K + tid] = tg;
+        G(d.colpart)[(static_cast<size_t>(rb) * 2 + 1) * K + tid] = tw;
+    }
 }
 
-// mean(G) and S = sym(beta W^T M + (1 - beta)(W^T G - colsum(W) mean^T)); one block per matrix
+// mean(G) and S = sym(beta W^T M + (1 - beta)(W^T G - colsum(W) mean^T)); CY_MID_SPLIT
+// blocks per matrix, each taking a slice of S (and recomputing the K column sums)
 __global__ __launch_bounds__(CY_THREADS) void cy_mid(CayleyArgs a) {
     __shared__ float mean_s[CAYLEY_MAX_K], colw_s[CAYLEY_MAX_K];
-    const CayleyDesc& d = a.descs[blockIdx.x];
+    int slice;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, slice);
     const int K = d.K;
     const size_t kk = static_cast<size_t>(K) * K;
+    const size_t q0 = kk * slice / CY_MID_SPLIT, q1 = kk * (slice + 1) / CY_MID_SPLIT;
     for (int j = threadIdx.x; j < K; j += CY_THREADS) {
         float sg = 0.0f, sw = 0.0f;
         for (int rb = 0; rb < d.nrb; ++rb) {
@@ -169,11 +188,11 @@ __global__ __launch_bounds__(CY_THREADS) void cy_mid(CayleyArgs a) {
         const float mean = sg / static_cast<float>(d.N);
         mean_s[j] = mean;
         colw_s[j] = sw;
-        G(d.small)[j] = mean;
+        if (slice == 0) G(d.small)[j] = mean;
     }
     __syncthreads();
     const float beta = a.beta, omb = 1.0f - a.beta;
-    for (size_t q = threadIdx.x; q < kk; q += CY_THREADS) {
+    for (size_t q = q0 + threadIdx.x; q < q1; q += CY_THREADS) {
         const int i = static_cast<int>(q / K), j = static_cast<int>(q % K);
         float gij = 0.0f, mij = 0.0f, gji = 0.0f, mji = 0.0f;
         for (int rb = 0; rb < d.nrb; ++rb) {

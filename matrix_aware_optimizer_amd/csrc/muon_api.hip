@@ -638,7 +638,7 @@ muon_status build_cayley_plan(std::vector<CayleyDesc>& descs, CayleyPlan& pl) {
     for (size_t k = 0; k < nmat; ++k) {
         CayleyDesc& d = descs[k];
         const int64_t tiles = static_cast<int64_t>(d.tn) * d.tk, red = static_cast<int64_t>(d.nrb) * d.tk * d.tk;
-        const int64_t per[CY_PHASES] = {d.tall ? 0 : tiles, red, d.nrb, 1, tiles, red, 1, tiles, tiles};
+        const int64_t per[CY_PHASES] = {d.tall ? 0 : tiles, red, d.nrb, CY_MID_SPLIT, tiles, red, 1, tiles, tiles};
         for (int ph = 0; ph < CY_PHASES; ++ph) {
             tot[ph] += per[ph];
             if (tot[ph] > INT32_MAX) return fail(MUON_ERR_UNSUPPORTED, "too many tiles in one call (split the list)");

@@ -110,6 +110,7 @@ constexpr int CY_T = 64;          // output tile edge of the small GEMMs and K x
 constexpr int CY_RB = 512;        // rows per reduction block
 constexpr int CY_THREADS = 256;
 constexpr int CY_SOLVE_THREADS = 1024;
+constexpr int CY_MID_SPLIT = 16;         // workgroups per matrix for the K x K middle step
 struct CayleyDesc {
     float* w;            // caller's weight (rows x cols)
     const float* g;      // caller's gradient

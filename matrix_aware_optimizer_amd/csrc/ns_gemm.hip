@@ -741,61 +741,23 @@ struct PolyAddend {
     }
 };
 
-template <typename E, typename T>
-__device__ __attribute__((always_inline)) void update_epilogue(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
-                                                               void* hi_out, uint16_t* lo_out, size_t np, float u) {
+// fp32 update epilogue: X' = u acc to x32[ping ^ 1], one row of 4 columns per lane.
+template <typename E>
+__device__ __attribute__((always_inline)) void update_epilogue_f32(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
+                                                                   float* out, size_t np, float u) {
     const Coords<E> q(row0, col0);
-    if (sizeof(T) == 4) {
-#pragma unroll
-        for (int i = 0; i < E::SM; ++i)
-#pragma unroll
-            for (int j = 0; j < E::SN; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float v[4];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) v[p] = acc[i][j][4 * g + p];
-                    quad_transpose(v);
-                    const size_t idx = static_cast<size_t>(q.tr_row + 32 * i + 8 * g) * np + q.tr_col + 32 * j;
-                    st_f4(static_cast<float*>(hi_out) + idx, make_float4(u * v[0], u * v[1], u * v[2], u * v[3]));
-                }
-        return;
-    }
-    // bf16: 8 consecutive columns of one row per lane after the quad swap
-    const bool odd = odd_quad();
 #pragma unroll
     for (int i = 0; i < E::SM; ++i)
 #pragma unroll
         for (int j = 0; j < E::SN; ++j)
 #pragma unroll
-            for (int gg = 0; gg < 2; ++gg) {
-                float v0[4], v1[4];
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    v0[p] = acc[i][j][8 * gg + p];
-                    v1[p] = acc[i][j][8 * gg + 4 + p];
-                }
-                quad_transpose(v0);
-                quad_transpose(v1);
-                float x[8];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float keep = odd ? v1[p] : v0[p];
-                    const float recv = __uint_as_float(swap_xor4(__float_as_uint(odd ? v0[p] : v1[p])));
-                    x[p] = odd ? recv : keep;
-                    x[4 + p] = odd ? keep : recv;
-                }
-                unsigned h[4], l[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float o0 = u * x[2 * p], o1 = u * x[2 * p + 1];
-                    h[p] = pack_bf16x2(o0, o1);
-                    l[p] = pack_bf16x2(o0 - __uint_as_float(h[p] << 16), o1 - __uint_as_float(h[p] & 0xffff0000u));
-                }
-                const size_t idx = static_cast<size_t>(q.tr_row + 32 * i + 8 * (2 * gg + odd)) * np +
-                                   q.tr_col + 32 * j - (odd ? 4 : 0);
-                G(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(hi_out) + idx))[0] = u32x4{h[0], h[1], h[2], h[3]};
-                G(reinterpret_cast<u32x4*>(lo_out + idx))[0] = u32x4{l[0], l[1], l[2], l[3]};
+                for (int p = 0; p < 4; ++p) v[p] = acc[i][j][4 * g + p];
+                quad_transpose(v);
+                const size_t idx = static_cast<size_t>(q.tr_row + 32 * i + 8 * g) * np + q.tr_col + 32 * j;
+                st_f4(out + idx, make_float4(u * v[0], u * v[1], u * v[2], u * v[3]));
             }
 }
 
@@ -1066,7 +1028,7 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         else if constexpr (sizeof(T) == 2)
             update_epilogue_staged<E>(acc, row0, col0, static_cast<uint16_t*>(d.xop[ping ^ 1]), d.xlo, np, u, lds);
         else
-            update_epilogue<E, T>(acc, row0, col0, d.xop[ping ^ 1], d.xlo, np, u);
+            update_epilogue_f32<E>(acc, row0, col0, d.x32[ping ^ 1], np, u);
     }
 }
 

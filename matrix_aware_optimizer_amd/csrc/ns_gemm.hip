@@ -765,7 +765,8 @@ __device__ __attribute__((always_inline)) void update_epilogue_f32(f32x16_t (&ac
 // of a different row (the register layout) reach about a third of the per-CU
 // store rate of row-contiguous ones, so the tile goes through LDS: hi' is written
 // there in the register layout, read back as whole 512-byte tile rows (two per
-// wave instruction) and stored; then the same for lo', kept in registers
+// wave instruction) and stored (non-temporal: the next reader is the next
+// step, after the whole launch); then the same for lo', kept in registers
 // meanwhile.  Staged row r of the tile sits at r * 512 bytes with its 16-byte
 // chunk c at position c ^ (r & 31).
 __device__ __forceinline__ int stage_off(int r, int chunk) { return r * 512 + ((chunk ^ (r & 31)) << 4); }
@@ -777,7 +778,7 @@ __device__ __forceinline__ void stage_copy_out(const lds_byte_t* L, uint16_t* ds
     for (int q = threadIdx.x; q < CHUNKS; q += GEMM_THREADS) {
         const int r = q >> 5, c = q & 31;
         const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(L + stage_off(r, c));
-        G(reinterpret_cast<u32x4*>(dst + static_cast<size_t>(row0 + r) * np + col0 + 8 * c))[0] = v;
+        __builtin_nontemporal_store(v, G(reinterpret_cast<u32x4*>(dst + static_cast<size_t>(row0 + r) * np + col0 + 8 * c)));
     }
 }
 

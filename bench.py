@@ -145,7 +145,8 @@ def summarize_profiles(prof_dir, workload_id, commands):
     write_factor = copy_bytes / (sum(cw) / len(cw) * 1024.0)
     uf = [float(r["Counter_Value"]) for r in _counter_rows(os.path.join(prof_dir, "fetch"), UPDATE_KERNEL)]
     uw = [float(r["Counter_Value"]) for r in _counter_rows(os.path.join(prof_dir, "write"), UPDATE_KERNEL)]
-    # launches per step: ns_steps; the last one writes only the fp32 iterate
+    # the counted kernel runs ns_steps - 1 times per step: the last update of a
+    # step is the kernel that also applies the step to W
     import workloads as wk
     wl = wk.WORKLOADS[workload_id]
     T = len(wl.hp["schedule"])
@@ -163,7 +164,7 @@ def summarize_profiles(prof_dir, workload_id, commands):
         "read_bytes_per_launch": int(read_b),
         "write_bytes_per_launch": int(write_b),
         "bytes_per_launch": int(read_b + write_b),
-        "note": f"average over all update launches, {T} per step",
+        "note": f"average over the update launches that write the iterate, {T - 1} per step",
         "commands": commands,
     }
     with open(TRAFFIC_FILE, "w") as fh:
@@ -388,8 +389,10 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     steps_ns = len(hp["schedule"])
     flops_ns = ns_flops(wl.shapes, steps_ns)
-    ns_ms = (prof["gram"]["ms"] + prof["poly"]["ms"] + prof["update"]["ms"]) / args.steps
-    upd = prof["update"]
+    ns_ms = (prof["gram"]["ms"] + prof["poly"]["ms"] + prof["update"]["ms"] + prof["update_apply"]["ms"]) / args.steps
+    # the roofline kernel: the update launches that write the iterate (all but the
+    # last of a step, whose kernel also applies the step to W and is timed apart)
+    upd = prof["update"] if prof["update"]["launches"] else prof["update_apply"]
     upd_ms = upd["ms"] / max(1, upd["launches"])
     upd_tflops = update_flops_per_launch(wl.shapes) / (upd_ms * 1e-3) / 1e12
     bf16 = wl.dtype == "bf16"
@@ -440,6 +443,7 @@ def main():
             "frac": round(upd_tflops / peak, 4),
             "traffic": measured_traffic(args.workload),
             "avg_launch_ms": round(upd_ms, 4),
+            "launches_per_step": round(upd["launches"] / args.steps, 2),
             "flops_per_launch": update_flops_per_launch(wl.shapes),
         },
     }

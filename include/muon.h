@@ -209,9 +209,10 @@ const char* muon_last_error_message(void);
  * events; muon_profile_read synchronizes them and returns, per kernel class,
  * the summed duration in milliseconds and the number of launches, then
  * resets the counters.  Classes: 0 momentum+norm, 1 norm finalize, 2 Gram,
- * 3 polynomial, 4 update, 5 apply, 6 AdamW, 7 Muon-Cayley (all its kernels).
+ * 3 polynomial, 4 update, 5 apply, 6 AdamW, 7 Muon-Cayley (all its kernels),
+ * 8 the last update of muon_step, which also applies decay and the step to W.
  * Host-side bookkeeping only. */
-#define MUON_KCLASS_COUNT 8
+#define MUON_KCLASS_COUNT 9
 typedef struct {
     double  ms[MUON_KCLASS_COUNT];
     int64_t launches[MUON_KCLASS_COUNT];

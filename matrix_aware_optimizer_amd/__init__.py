@@ -33,8 +33,9 @@ MUON_BF16 = 1
 
 SCALE_RULES = {"naive": 0, "kellerjordan": 1, "mup": 2, "moonlight": 3}
 MUON_FLAG_NESTEROV = 1
-MUON_KCLASS_COUNT = 8
-KERNEL_CLASSES = ("momentum_norm", "norm_finalize", "gram", "poly", "update", "apply", "adamw", "cayley")
+MUON_KCLASS_COUNT = 9
+KERNEL_CLASSES = ("momentum_norm", "norm_finalize", "gram", "poly", "update", "apply", "adamw", "cayley",
+                  "update_apply")
 
 
 class MuonMatrix(ctypes.Structure):

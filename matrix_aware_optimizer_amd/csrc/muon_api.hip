@@ -471,7 +471,7 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
         if (st != MUON_OK) return st;
         na.prefix = d_pre + 2 * (nmat + 1);
         na.total = static_cast<int32_t>(pl.total_upd);
-        st = timed_launch(4, stream, "update kernel", [&] { return launch_update(dtype, na, stream); });
+        st = timed_launch(na.apply ? 8 : 4, stream, "update kernel", [&] { return launch_update(dtype, na, stream); });
         if (st != MUON_OK) return st;
     }
     if (ns_only || hp->ns_steps == 0) {

@@ -144,6 +144,12 @@ struct Engine {
     static constexpr int GROUPS = SUB * SM;            // MFMA groups per k-step
     static_assert(BM == BN, "P and Q slabs have one size");
     static_assert(2 * HL <= GROUPS, "one load per MFMA group at most");
+    // The rotated k-loop (below) for k-contiguous Q; the k-major update keeps one
+    // barrier per step at its top, where its per-step hook needs the registers.
+    static constexpr bool ROTATE = !QK;
+    // loads of P(kt + 2) issued before the barrier that opens step kt + 1 (the last slice's)
+    static constexpr int PB = ((SUB - 1) * SM < 2 * HL ? (SUB - 1) * SM : 2 * HL) - HL;
+    static_assert(PB >= 0 && PB <= HL, "the loads of Q(kt + 1) precede the last slice");
     static_assert(SM >= SN, "fragment prefetch pairs A row i with B row i");
     static_assert(!QK || BN * static_cast<int>(sizeof(T)) == QROW_CHUNKS * 16, "k-major rows are one tile wide");
     static_assert(!QK || KS * QROW_CHUNKS == SLAB, "k-major slab holds KS rows");
@@ -155,10 +161,13 @@ struct Engine {
     // hook(kt, Q slab of step kt, acc) runs when step kt's slabs are ready.
     //
     // Slabs are numbered 2 kt (P) and 2 kt + 1 (Q) and slab s lives in LDS slot s % 5.
-    // During step kt a wave issues Q(kt + 1) and then P(kt + 2): both slots were read
-    // in step kt - 1, which every wave has left at the barrier opening step kt.  Step
-    // kt then waits for all but the newest HL loads (P(kt + 1)), so the loads of the
-    // next-but-one P slab stay in flight across the barrier.
+    // A barrier opens step kt once each wave's loads of P(kt) and Q(kt) are done, so
+    // only P(kt + 1) stays in flight across it; after it no wave reads the slots of
+    // step kt - 1 again, and step kt refills them with Q(kt + 1) and P(kt + 2).
+    // Rotated (ROTATE), that barrier sits before the last k-slice of step kt - 1 (after
+    // the prologue for step 0), whose MFMAs then cover the first fragment reads of
+    // step kt; each wave also waits for its LDS reads before it.  Otherwise it sits at
+    // the top of step kt.
     template <typename Init, typename Hook>
     static __device__ __attribute__((always_inline)) void run(const char* __restrict__ P, size_t ldp, const char* __restrict__ Q,
                                       size_t ldq, int ksteps, u32x4* lds, f32x16_t (&acc)[SM][SN], Init init,
@@ -204,59 +213,92 @@ struct Engine {
 
         const int half = lane >> 5;
         const int arow = wm * WM + (lane & 31), brow = wn * WN + (lane & 31);
-        int sp = 0;   // slot of P(kt); Q(kt) sits in the next one
-        for (int kt = 0; kt < ksteps; ++kt) {
-            // this wave's loads of step kt's slabs are done (P(kt + 1) may still be in
-            // flight); the barrier makes every wave's visible and guarantees that the
-            // slots of step kt - 1 are no longer being read
-            if (kt + 1 < ksteps)
+        // B operand of k-slice s (16 bf16 or 8 fp32 of k) for 32-column block j of the Q slab at LQ
+        auto read_b = [&](const u32x4* LQ, int j, int s) -> u32x4 {
+            if (!QK) return LQ[swz(brow + j * 32, 2 * s + half)];
+            const lds_byte_t* Lq = (const lds_byte_t*)LQ;
+            if (sizeof(T) == 2) {
+                const int i16 = lane & 15, g16 = lane >> 4;
+                const int col = wn * WN + j * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
+                const int kr = 16 * s + 8 * (g16 >> 1) + (i16 >> 2);
+                const int cb = (col & 7) * 2;
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t*)(Lq + qswz(kr, col >> 3) * 16 + cb));
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4_t*)(Lq + qswz(kr + 4, col >> 3) * 16 + cb));
+                const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+                return u32x4{l2.x, l2.y, h2.x, h2.y};
+            } else {
+                // MFMA e of the chunk pair uses k = 8 s + 4 half + e
+                const int col = wn * WN + j * 32 + (lane & 31);
+                const int kr = 8 * s + 4 * half;
+                const int cb = (col & 3) * 4;
+                u32x4 v;
+                v.x = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 0, col >> 2) * 16 + cb));
+                v.y = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 1, col >> 2) * 16 + cb));
+                v.z = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 2, col >> 2) * 16 + cb));
+                v.w = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 3, col >> 2) * 16 + cb));
+                return v;
+            }
+        };
+
+        u32x4 fa[2][SM], fb[2][SN];
+        if constexpr (ROTATE) {
+            // step 0's slabs (P(1) may still be in flight), then its first fragments
+            if (ksteps > 1)
                 asm volatile("s_waitcnt vmcnt(%0)" ::"n"(HL) : "memory");
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+            for (int i = 0; i < SM; ++i) fa[0][i] = lds[swz(arow + i * 32, half)];
+#pragma unroll
+            for (int j = 0; j < SN; ++j) fb[0][j] = read_b(lds + SLAB, j, 0);
+        }
+
+        int sp = 0;   // slot of P(kt); Q(kt) sits in the next one
+        for (int kt = 0; kt < ksteps; ++kt) {
             const int sq = sp + 1 == SLOTS ? 0 : sp + 1;
             const int s3 = sp >= 2 ? sp - 2 : sp + 3;   // slot of Q(kt + 1)
             const int s4 = sp >= 1 ? sp - 1 : sp + 4;   // slot of P(kt + 2)
+            const int np = sp >= 3 ? sp - 3 : sp + 2;   // slot of P(kt + 1)
             const u32x4* L = lds + sp * SLAB;
             const u32x4* LQ = lds + sq * SLAB;
-            const lds_byte_t* Lq = (const lds_byte_t*)LQ;
-            hook(kt, Lq, acc);
-            // B operand of k-slice s (16 bf16 or 8 fp32 of k) for 32-column block j
-            auto read_b = [&](int j, int s) -> u32x4 {
-                if (!QK) return LQ[swz(brow + j * 32, 2 * s + half)];
-                if (sizeof(T) == 2) {
-                    const int i16 = lane & 15, g16 = lane >> 4;
-                    const int col = wn * WN + j * 32 + 16 * (g16 & 1) + 4 * (i16 & 3);
-                    const int kr = 16 * s + 8 * (g16 >> 1) + (i16 >> 2);
-                    const int cb = (col & 7) * 2;
-                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4_t*)(Lq + qswz(kr, col >> 3) * 16 + cb));
-                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4_t*)(Lq + qswz(kr + 4, col >> 3) * 16 + cb));
-                    const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
-                    return u32x4{l2.x, l2.y, h2.x, h2.y};
-                } else {
-                    // MFMA e of the chunk pair uses k = 8 s + 4 half + e
-                    const int col = wn * WN + j * 32 + (lane & 31);
-                    const int kr = 8 * s + 4 * half;
-                    const int cb = (col & 3) * 4;
-                    u32x4 v;
-                    v.x = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 0, col >> 2) * 16 + cb));
-                    v.y = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 1, col >> 2) * 16 + cb));
-                    v.z = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 2, col >> 2) * 16 + cb));
-                    v.w = __float_as_uint(*(const lds_float_t*)(Lq + qswz(kr + 3, col >> 2) * 16 + cb));
-                    return v;
-                }
-            };
+            if constexpr (!ROTATE) {
+                // this wave's loads of step kt's slabs are done (P(kt + 1) may still be
+                // in flight); the barrier publishes every wave's and ends all reads of
+                // the slots of step kt - 1
+                if (kt + 1 < ksteps)
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(HL) : "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                asm volatile("s_barrier" ::: "memory");
+            }
+            hook(kt, (const lds_byte_t*)LQ, acc);
+            if constexpr (!ROTATE) {
+#pragma unroll
+                for (int i = 0; i < SM; ++i) fa[0][i] = L[swz(arow + i * 32, half)];
+#pragma unroll
+                for (int j = 0; j < SN; ++j) fb[0][j] = read_b(LQ, j, 0);
+            }
             const bool more1 = kt + 1 < ksteps, more2 = kt + 2 < ksteps;
-            u32x4 fa[2][SM], fb[2][SN];
-#pragma unroll
-            for (int i = 0; i < SM; ++i) fa[0][i] = L[swz(arow + i * 32, half)];
-#pragma unroll
-            for (int j = 0; j < SN; ++j) fb[0][j] = read_b(j, 0);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < SUB; ++s) {
+                if (ROTATE && s == SUB - 1 && more1) {
+                    // Open step kt + 1 before this step's last slice, whose MFMAs then
+                    // cover the first fragment reads of the next step.  Every read of
+                    // step kt's slabs (fragments and hook) has completed; this wave's
+                    // loads of Q(kt + 1) and P(kt + 1) are done, only P(kt + 2) may be
+                    // in flight.  After the barrier the slots of step kt are free.
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    if (more2)
+                        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PB) : "memory");
+                    else
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    asm volatile("s_barrier" ::: "memory");
+                    __builtin_amdgcn_sched_barrier(0);
+                }
                 const int cn = 2 * (s + 1) + half;
 #pragma unroll
                 for (int i = 0; i < SM; ++i) {
@@ -264,7 +306,10 @@ struct Engine {
                     for (int j = 0; j < SN; ++j) mfma_chunk(acc[i][j], fa[s & 1][i], fb[s & 1][j], T{});
                     if (s + 1 < SUB) {
                         fa[(s + 1) & 1][i] = L[swz(arow + i * 32, cn)];
-                        if (i < SN) fb[(s + 1) & 1][i] = read_b(i, s + 1);
+                        if (i < SN) fb[(s + 1) & 1][i] = read_b(LQ, i, s + 1);
+                    } else if (ROTATE && more1) {
+                        fa[0][i] = lds[np * SLAB + swz(arow + i * 32, half)];
+                        if (i < SN) fb[0][i] = read_b(lds + s3 * SLAB, i, 0);
                     }
                     const int g = s * SM + i;
                     if (g < HL && more1) issue(kt + 1, true, s3, g);
@@ -272,7 +317,7 @@ struct Engine {
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            sp = sp >= 3 ? sp - 3 : sp + 2;
+            sp = np;
         }
     }
 };

@@ -67,14 +67,15 @@ __device__ __forceinline__ int ew_row(int p) { return (threadIdx.x >> 3) + (EW_T
 __device__ __forceinline__ int ew_col() { return (threadIdx.x & 7) * EW_GROUP; }
 
 // Deterministic block sum (fixed shuffle pattern, fixed wave order).
+// LDS barriers only: the tile's global stores stay in flight across them.
 __device__ inline float block_sum_256(float v, float* red) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[wave] = v;
-    __syncthreads();
+    lds_barrier();
     float total = ((red[0] + red[1]) + (red[2] + red[3]));
-    __syncthreads();
+    lds_barrier();
     return total;
 }
 
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
 #pragma unroll
                 for (int e = 0; e < EW_GROUP; ++e) tile[jl + e][ew_row(p)] = v[e];
             }
-            __syncthreads();
+            lds_barrier();
 #pragma unroll
             for (int p = 0; p < EW_PASSES; ++p)
 #pragma unroll
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(EwArgs args) {
             for (int p = 0; p < EW_PASSES; ++p)
 #pragma unroll
                 for (int e = 0; e < EW_GROUP; ++e) tile[ew_row(p)][jl + e] = x[p][e];
-            __syncthreads();
+            lds_barrier();
             // caller row j0 + r holds NS column j0 + r: columns i0 + jl + e are NS rows
 #pragma unroll
             for (int p = 0; p < EW_PASSES; ++p) {
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(EW_THREADS) void apply_kernel(EwArgs args) {
                 for (int e = 0; e < EW_GROUP; ++e) o[e] = tile[jl + e][ew_row(p)];
                 apply_group<T, NS_ONLY>(d, coef, oscale, j0 + ew_row(p), i0 + jl, o);
             }
-            __syncthreads();
+            lds_barrier();   // the tile is reused; the stores stay in flight
         }
     }
 }

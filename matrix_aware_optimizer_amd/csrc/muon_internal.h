@@ -156,8 +156,8 @@ hipError_t launch_update(int dtype, const NsArgs& args, hipStream_t s);
 
 // Workgroup barrier for LDS hand-offs only.  __syncthreads() also fences
 // global memory, i.e. waits until every store the wave has issued is
-// acknowledged; in the store-heavy epilogues that wait dominated.  Here only
-// LDS operations are waited for, so global stores stay in flight.
+// acknowledged.  Here only LDS operations are waited for, so global stores
+// stay in flight across the barrier.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

@@ -836,7 +836,7 @@ __device__ __attribute__((always_inline)) void update_epilogue_staged(f32x16_t (
     const bool odd = odd_quad();
     lds_byte_t* L = (lds_byte_t*)lds;
     u32x4 lo[E::SM][E::SN][2];
-    __syncthreads();   // every wave is done reading the operand slabs
+    lds_barrier();   // every wave is done reading the operand slabs
 #pragma unroll
     for (int i = 0; i < E::SM; ++i)
 #pragma unroll
@@ -871,9 +871,9 @@ __device__ __attribute__((always_inline)) void update_epilogue_staged(f32x16_t (
                 *(__attribute__((address_space(3))) u32x4*)(L + stage_off(r, c)) = u32x4{h[0], h[1], h[2], h[3]};
                 lo[i][j][gg] = u32x4{l[0], l[1], l[2], l[3]};
             }
-    __syncthreads();
+    lds_barrier();
     stage_copy_out<E>(L, hi_out, row0, col0, np);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < E::SM; ++i)
 #pragma unroll
@@ -884,7 +884,7 @@ __device__ __attribute__((always_inline)) void update_epilogue_staged(f32x16_t (
                 const int c = (q.tr_col - col0 + 32 * j - (odd ? 4 : 0)) >> 3;
                 *(__attribute__((address_space(3))) u32x4*)(L + stage_off(r, c)) = lo[i][j][gg];
             }
-    __syncthreads();
+    lds_barrier();
     stage_copy_out<E>(L, lo_out, row0, col0, np);
 }
 

@@ -154,6 +154,24 @@ struct Engine {
     static_assert(!QK || BN * static_cast<int>(sizeof(T)) == QROW_CHUNKS * 16, "k-major rows are one tile wide");
     static_assert(!QK || KS * QROW_CHUNKS == SLAB, "k-major slab holds KS rows");
 
+    // Source of DMA load j of this wave for a k-major slab whose first k-row is at Q
+    // (pitch ldq bytes): the load fills slab chunks [(wave*HL + j)*64, +64) in lane
+    // order, and each lane fetches the logical chunk that the swizzle puts there.
+    static __device__ __forceinline__ const char* kmajor_src(const char* Q, size_t ldq, int j) {
+        const int chunk = (static_cast<int>(threadIdx.x >> 6) * HL + j) * 64 + static_cast<int>(threadIdx.x & 63);
+        const int kr = chunk / QROW_CHUNKS;
+        const int lq = (chunk % QROW_CHUNKS) ^ ((kr & 3) << 2);
+        return Q + kr * ldq + lq * 16;
+    }
+    // Issue this wave's share of the DMA of one k-major slab into LDS slot `slot`.
+    static __device__ __forceinline__ void load_kmajor_slab(const char* Q, size_t ldq, u32x4* lds, int slot) {
+        const int wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int j = 0; j < HL; ++j)
+            __builtin_amdgcn_global_load_lds((const void*)kmajor_src(Q, ldq, j),
+                                             (lds_ptr_t)(lds + slot * SLAB + (wave * HL + j) * 64), 16, 0, 0);
+    }
+
     // acc[i][j] = init[i][j] + sum_k P[row0 + i][k] * Q(k, col0 + j) over the whole k
     // range, where P points at row row0 (pitch ldp bytes) and Q at row col0
     // (k-contiguous) or at column col0 of k-row 0 (k-major), pitch ldq bytes.
@@ -186,13 +204,7 @@ struct Engine {
             const int row = chunk / CHUNKS_PER_ROW;
             const int lc = (chunk % CHUNKS_PER_ROW) ^ ((row >> 1) & 7);
             srcp[j] = P + row * ldp + lc * 16;
-            if (!QK) {
-                srcq[j] = Q + row * ldq + lc * 16;
-            } else {
-                const int kr = chunk / QROW_CHUNKS;
-                const int lq = (chunk % QROW_CHUNKS) ^ ((kr & 3) << 2);
-                srcq[j] = Q + kr * ldq + lq * 16;
-            }
+            srcq[j] = QK ? kmajor_src(Q, ldq, j) : Q + row * ldq + lc * 16;
         }
         const size_t pstep = CHUNKS_PER_ROW * 16;
         const size_t qstep = QK ? static_cast<size_t>(KS) * ldq : static_cast<size_t>(CHUNKS_PER_ROW * 16);
@@ -627,53 +639,19 @@ __device__ __forceinline__ void sym_epilogue(f32x16_t (&acc)[E::SM][E::SN], int 
 //         accumulators while the first operand slabs load (UpdateInit), and
 //         X' goes to x32[ping ^ 1].
 //   bf16: the iterate is the pair hi + lo (hi = xop[ping], the operand copy,
-//         lo = xlo).  a lo is read into the accumulators at the start; a hi is
-//         added from LDS during the k-steps that stage the tile's own rows of
-//         X as operand k-rows (HiAddend).  X' is stored as hi' = bf16(X') to
-//         xop[ping ^ 1] and lo' = bf16(X' - hi') to xlo, in place.
+//         lo = xlo).  a hi is added from LDS during the k-steps that stage the
+//         tile's own rows of X as operand k-rows (HiAddend); a lo after the
+//         k-loop, from the tile's lo rows loaded into the idle ring as k-major
+//         slabs (add_lo_tile).  X' is stored as hi' = bf16(X') to xop[ping ^ 1]
+//         and lo' = bf16(X' - hi') to xlo, in place.
 template <typename E, typename T>
-struct UpdateInit {
-    const void* src;    // x32[ping] (fp32) or xlo (bf16)
+struct UpdateInit {   // fp32 iterate
+    const void* src;    // x32[ping]
     size_t np;
     int row0, col0;
     float a;
     template <typename A> __device__ __forceinline__ void operator()(A& acc) const {
         const Coords<E> q(row0, col0);
-        if (sizeof(T) == 2) {
-            // 16 bytes of one row per lane, then the quad swap back to the pair's rows
-            const bool odd = odd_quad();
-#pragma unroll
-            for (int i = 0; i < E::SM; ++i)
-#pragma unroll
-                for (int j = 0; j < E::SN; ++j)
-#pragma unroll
-                    for (int gg = 0; gg < 2; ++gg) {
-                        const size_t idx = static_cast<size_t>(q.tr_row + 32 * i + 8 * (2 * gg + odd)) * np +
-                                           q.tr_col + 32 * j - (odd ? 4 : 0);
-                        const u32x4 w = G(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(src) + idx))[0];
-                        // words 0-1: the even lane's columns, words 2-3: the odd lane's
-                        const unsigned k0 = odd ? w.z : w.x, k1 = odd ? w.w : w.y;
-                        const unsigned r0 = swap_xor4(odd ? w.x : w.z), r1 = swap_xor4(odd ? w.y : w.w);
-                        const unsigned g0w[2] = {odd ? r0 : k0, odd ? r1 : k1};   // row g0, own columns
-                        const unsigned g1w[2] = {odd ? k0 : r0, odd ? k1 : r1};   // row g1, own columns
-                        float v0[4], v1[4];
-#pragma unroll
-                        for (int p = 0; p < 2; ++p) {
-                            v0[2 * p] = a * __uint_as_float(g0w[p] << 16);
-                            v0[2 * p + 1] = a * __uint_as_float(g0w[p] & 0xffff0000u);
-                            v1[2 * p] = a * __uint_as_float(g1w[p] << 16);
-                            v1[2 * p + 1] = a * __uint_as_float(g1w[p] & 0xffff0000u);
-                        }
-                        quad_transpose(v0);   // row layout -> accumulator layout (an involution)
-                        quad_transpose(v1);
-#pragma unroll
-                        for (int p = 0; p < 4; ++p) {
-                            acc[i][j][8 * gg + p] = v0[p];
-                            acc[i][j][8 * gg + 4 + p] = v1[p];
-                        }
-                    }
-            return;
-        }
 #pragma unroll
         for (int i = 0; i < E::SM; ++i)
 #pragma unroll
@@ -733,6 +711,25 @@ struct HiAddend {
         }
     }
 };
+
+// a lo for the bf16 update, after the k-loop: the tile's lo rows arrive as
+// BM / KS k-major slabs in the idle ring (coalesced 512-byte rows) and are
+// added with the same transpose reads as a hi.
+template <typename E>
+__device__ __forceinline__ void add_lo_tile(f32x16_t (&acc)[E::SM][E::SN], const uint16_t* xlo, size_t np, int row0,
+                                            int col0, float a, u32x4* lds) {
+    constexpr int NSLAB = E::BM / E::KS;
+    static_assert(NSLAB * E::SLAB <= E::LDS_CHUNKS, "the lo tile fits the ring");
+    const size_t ld = np * sizeof(uint16_t);
+    const char* base = reinterpret_cast<const char*>(xlo + static_cast<size_t>(row0) * np + col0);
+    lds_barrier();   // every wave is done reading the operand slabs
+#pragma unroll
+    for (int c = 0; c < NSLAB; ++c) E::load_kmajor_slab(base + static_cast<size_t>(c) * E::KS * ld, ld, lds, c);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    const HiAddend<E> add{row0 / E::KS, a};
+#pragma unroll
+    for (int c = 0; c < NSLAB; ++c) add(row0 / E::KS + c, (const lds_byte_t*)(lds + c * E::SLAB), acc);
+}
 
 // Polynomial B = b A + c A A with c != 0, accumulated as c (A A + (b / c) A): the
 // Q slab of k-step kt holds A[col0 + r][kt KS + (0..KS-1)], which by symmetry is
@@ -1060,13 +1057,14 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         const char* B = static_cast<const char*>(d.bmat);
         const char* X = static_cast<const char*>(d.xop[ping]);
         const size_t ldb = static_cast<size_t>(mp) * sizeof(T), ldx = static_cast<size_t>(np) * sizeof(T);
-        const UpdateInit<E, T> init{sizeof(T) == 2 ? static_cast<const void*>(d.xlo) : static_cast<const void*>(d.x32[ping]),
-                                    static_cast<size_t>(np), row0, col0, args.a};
-        if (sizeof(T) == 2)
-            E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, ks_m, lds, acc, init,
+        if constexpr (sizeof(T) == 2) {
+            E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, ks_m, lds, acc, ZeroInit{},
                    HiAddend<E>{row0 / E::KS, args.a});
-        else
+            add_lo_tile<E>(acc, d.xlo, static_cast<size_t>(np), row0, col0, args.a, lds);
+        } else {
+            const UpdateInit<E, T> init{d.x32[ping], static_cast<size_t>(np), row0, col0, args.a};
             E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, ks_m, lds, acc, init, NoHook{});
+        }
         // first step: X1 = s (a M' + B0 M') with M' unscaled in the iterate and operand copy
         const float u = args.first ? G(d.scal)[0] : 1.0f;
         if constexpr (PHASE == PH_UPDATE_APPLY)

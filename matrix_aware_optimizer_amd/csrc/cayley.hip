@@ -520,69 +520,104 @@ __device__ void kk_gemm(int K, double* out, const double* A, const double* B, do
     __syncthreads();
 }
 
-// out = ((identity ? I : 0) + scale * src)^-1 by Gauss-Jordan with partial pivoting,
-// in LDS.  Rows are swapped in place; the columns are unscrambled in reverse order
-// at the end.  out may be src.
+// out = ((identity ? I : 0) + scale * src)^-1 by Gauss-Jordan with partial pivoting.
+// The working matrix, 128 x 128 with the identity beyond K, lives in registers:
+// thread t holds row t / 8, columns 16 (t % 8) .. 16 (t % 8) + 15.  Rows are not
+// swapped: step j pivots on the unused row p_j with the largest |M[p][j]| (ties to
+// the smaller row) and eliminates column j in place, so the final matrix E holds
+// the inverse permuted, inv[a][p_b] = E[p_a][b].  Per step only the pivot search
+// and the scaled pivot row pass through LDS.  out may be src.
 __device__ void kk_gj_inverse(int K, double* out, const double* src, double scale, bool identity, double* lds) {
-    double* M = lds;                       // K x K, pitch K
-    double* prow = M + CY_LDS_K * CY_LDS_K;
-    double* colf = prow + CY_LDS_K;
-    int* piv = reinterpret_cast<int*>(colf + CY_LDS_K);
-    const int tid = threadIdx.x;
-    for (int q = tid; q < K * K; q += CY_SOLVE_THREADS) {
-        const int i = q / K, j = q % K;
-        M[q] = (identity && i == j ? 1.0 : 0.0) + scale * src[q];
-    }
-    __syncthreads();
-    for (int j = 0; j < K; ++j) {
-        if (tid < 64) {   // one wave: largest |M[i][j]|, i >= j (ties to the smaller i)
-            double best = -1.0;
-            int bidx = K;
-            for (int i = j + tid; i < K; i += 64) {
-                const double v = fabs(M[i * K + j]);
-                if (v > best) { best = v; bidx = i; }
-            }
+    static_assert(CY_SOLVE_THREADS == 8 * CY_LDS_K, "eight threads per row of the 128 x 128 matrix");
+    constexpr int CB = 16;   // columns per thread
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int i = tid >> 3, cb = tid & 7;
+    double* red_abs = lds;                                  // [2][16] per-wave best |M[i][j]|
+    double* red_val = lds + 32;                             // [2][16] its signed value
+    int* red_row = reinterpret_cast<int*>(lds + 64);        // [2][16] its row
+    double* prow = lds + 80;                                // [2][128] scaled pivot row
+    int* piv = reinterpret_cast<int*>(lds + 80 + 2 * CY_LDS_K);   // [128] pivot row of step j
+
+    double m[CB];
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const double ov = __shfl_xor(best, off, 64);
-                const int oi = __shfl_xor(bidx, off, 64);
-                if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+    for (int k = 0; k < CB; ++k) {
+        const int col = CB * cb + k;
+        if (i < K && col < K)
+            m[k] = (identity && i == col ? 1.0 : 0.0) + scale * src[static_cast<size_t>(i) * K + col];
+        else
+            m[k] = i == col ? 1.0 : 0.0;
+    }
+    bool used = i >= K;   // rows beyond K never pivot
+    int my_step = 0;      // the step at which this row pivoted
+    for (int jb = 0; jb < CY_LDS_K / CB && CB * jb < K; ++jb) {
+#pragma unroll
+        for (int e = 0; e < CB; ++e) {
+            const int j = CB * jb + e;
+            if (j < K) {   // uniform
+                const int buf = j & 1;
+                // pivot search.  The wave's 8 rows hold column j in lanes 8 r + jb: their
+                // best |M[i][j]| on an unused row (ties to the smaller row), and its value
+                double cabs = -1.0;
+                int crow = CY_LDS_K;
+                if (cb == jb && !used) { cabs = fabs(m[e]); crow = i; }
+#pragma unroll
+                for (int off = 8; off < 64; off <<= 1) {
+                    const double oabs = __shfl_xor(cabs, off, 64);
+                    const int orow = __shfl_xor(crow, off, 64);
+                    if (oabs > cabs || (oabs == cabs && orow < crow)) { cabs = oabs; crow = orow; }
+                }
+                const double cval = __shfl(m[e], 8 * (crow & 7) + jb, 64);   // row crow is 8 wave + (crow & 7)
+                if (lane == jb) {
+                    red_abs[buf * 16 + wave] = cabs;
+                    red_val[buf * 16 + wave] = cval;
+                    red_row[buf * 16 + wave] = crow;
+                }
+                lds_barrier();
+                // best of the 16 waves' candidates: lanes 0..15 of every wave reduce them
+                static_assert(CY_SOLVE_THREADS / 64 == 16, "one candidate per wave, 16 waves");
+                double babs = red_abs[buf * 16 + (lane & 15)];
+                int brow = red_row[buf * 16 + (lane & 15)], bw = lane & 15;
+#pragma unroll
+                for (int off = 1; off < 16; off <<= 1) {
+                    const double oabs = __shfl_xor(babs, off, 64);
+                    const int orow = __shfl_xor(brow, off, 64), ow = __shfl_xor(bw, off, 64);
+                    if (oabs > babs || (oabs == babs && orow < brow)) { babs = oabs; brow = orow; bw = ow; }
+                }
+                const int p = __builtin_amdgcn_readfirstlane(brow);
+                const double bval = red_val[buf * 16 + __builtin_amdgcn_readfirstlane(bw)];
+                const double inv = 1.0 / bval;
+                // M[i][j], from the lane of this row that holds column j
+                const double colf = __shfl(m[e], (lane & ~7) | jb, 64);
+                if (i == p) {
+#pragma unroll
+                    for (int k = 0; k < CB; ++k) {
+                        m[k] = (CB * cb + k == j) ? inv : m[k] * inv;
+                        prow[buf * CY_LDS_K + CB * cb + k] = m[k];
+                    }
+                    used = true;
+                    my_step = j;
+                    if (cb == 0) piv[j] = p;
+                }
+                lds_barrier();
+                if (i != p) {
+#pragma unroll
+                    for (int k = 0; k < CB; ++k) {
+                        const int col = CB * cb + k;
+                        m[k] = col == j ? -colf * inv : m[k] - colf * prow[buf * CY_LDS_K + col];
+                    }
+                }
             }
-            if (tid == 0) piv[j] = bidx;
         }
-        __syncthreads();
-        const int p = piv[j];
-        if (p != j && tid < K) {
-            const double t = M[j * K + tid];
-            M[j * K + tid] = M[p * K + tid];
-            M[p * K + tid] = t;
-        }
-        __syncthreads();
-        const double inv = 1.0 / M[j * K + j];
-        if (tid < K) {
-            prow[tid] = tid == j ? inv : M[j * K + tid] * inv;
-            colf[tid] = tid == j ? 0.0 : M[tid * K + j];
-        }
-        __syncthreads();
-        for (int q = tid; q < K * K; q += CY_SOLVE_THREADS) {
-            const int i = q / K, k = q % K;
-            if (i == j) M[q] = prow[k];
-            else if (k == j) M[q] = -colf[i] * inv;
-            else M[q] -= colf[i] * prow[k];
-        }
-        __syncthreads();
     }
-    for (int j = K - 1; j >= 0; --j) {
-        const int p = piv[j];
-        if (p != j && tid < K) {
-            const double t = M[tid * K + j];
-            M[tid * K + j] = M[tid * K + p];
-            M[tid * K + p] = t;
+    lds_barrier();   // every piv[] entry is written
+    if (i < K) {
+#pragma unroll
+        for (int k = 0; k < CB; ++k) {
+            const int b = CB * cb + k;
+            if (b < K) out[static_cast<size_t>(my_step) * K + piv[b]] = m[k];
         }
-        __syncthreads();
     }
-    for (int q = tid; q < K * K; q += CY_SOLVE_THREADS) out[q] = M[q];
-    __syncthreads();
+    __syncthreads();   // out is complete (global) before the next product reads it
 }
 
 __device__ void solve_blocked(const CayleyDesc& d, double c, double* lds) {

@@ -535,8 +535,11 @@ __device__ void kk_gj_inverse(int K, double* out, const double* src, double scal
     double* red_abs = lds;                                  // [2][16] per-wave best |M[i][j]|
     double* red_val = lds + 32;                             // [2][16] its signed value
     int* red_row = reinterpret_cast<int*>(lds + 64);        // [2][16] its row
-    double* prow = lds + 80;                                // [2][128] scaled pivot row
-    int* piv = reinterpret_cast<int*>(lds + 80 + 2 * CY_LDS_K);   // [128] pivot row of step j
+    // scaled pivot row, [2][8][17]: column block cb at 17 cb, so the 8 blocks that
+    // one read instruction touches fall in different LDS banks
+    constexpr int PSTRIDE = CB + 1, PBUF = 8 * PSTRIDE;
+    double* prow = lds + 80;
+    int* piv = reinterpret_cast<int*>(lds + 80 + 2 * PBUF);   // [128] pivot row of step j
 
     double m[CB];
 #pragma unroll
@@ -592,7 +595,7 @@ __device__ void kk_gj_inverse(int K, double* out, const double* src, double scal
 #pragma unroll
                     for (int k = 0; k < CB; ++k) {
                         m[k] = (CB * cb + k == j) ? inv : m[k] * inv;
-                        prow[buf * CY_LDS_K + CB * cb + k] = m[k];
+                        prow[buf * PBUF + PSTRIDE * cb + k] = m[k];
                     }
                     used = true;
                     my_step = j;
@@ -603,7 +606,7 @@ __device__ void kk_gj_inverse(int K, double* out, const double* src, double scal
 #pragma unroll
                     for (int k = 0; k < CB; ++k) {
                         const int col = CB * cb + k;
-                        m[k] = col == j ? -colf * inv : m[k] - colf * prow[buf * CY_LDS_K + col];
+                        m[k] = col == j ? -colf * inv : m[k] - colf * prow[buf * PBUF + PSTRIDE * cb + k];
                     }
                 }
             }

@@ -347,12 +347,29 @@ __device__ void solve_global(const CayleyDesc& d, double cc, double* arena) {
     for (size_t q = tid; q < kk; q += CY_SOLVE_THREADS) {
         const int i = static_cast<int>(q / K), j = static_cast<int>(q % K);
         double ww = 0.0, wv = 0.0, vw = 0.0, vv = 0.0;   // (W^T W)ij, (W^T V)ij, (W^T V)ji, (V^T V)ij
-        for (int rb = 0; rb < d.nrb; ++rb) {
-            const float* pr = d.part + static_cast<size_t>(rb) * 3 * kk;
-            ww += G(pr)[q];
-            wv += G(pr)[kk + q];
-            vw += G(pr)[kk + static_cast<size_t>(j) * K + i];
-            vv += G(pr)[2 * kk + q];
+        // row blocks in ascending order; the loads of RB blocks are issued before their sums
+        constexpr int RB = 8;
+        for (int rb0 = 0; rb0 < d.nrb; rb0 += RB) {
+            float t[RB][4];
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+                if (rb0 + u < d.nrb) {
+                    const float* pr = d.part + static_cast<size_t>(rb0 + u) * 3 * kk;
+                    t[u][0] = G(pr)[q];
+                    t[u][1] = G(pr)[kk + q];
+                    t[u][2] = G(pr)[kk + static_cast<size_t>(j) * K + i];
+                    t[u][3] = G(pr)[2 * kk + q];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+                if (rb0 + u < d.nrb) {
+                    ww += t[u][0];
+                    wv += t[u][1];
+                    vw += t[u][2];
+                    vv += t[u][3];
+                }
+            }
         }
         // B U = [[W^T V, W^T W], [-V^T V, -V^T W]], with (V^T W)ij = (W^T V)ji
         C[static_cast<size_t>(i) * K2 + j] = wv;
@@ -475,41 +492,59 @@ constexpr int CY_LDS_K = 128;
 
 // out = base_scale * base + (identity ? I : 0) + alpha * A B   (K x K, pitch K, fp64, global).
 // out may be base (each element is read and written by one thread) but not A or B.
-// Thread t owns the 4 x 4 block at rows 4 (t / 32), columns 4 (t % 32).
+// Thread t owns rows 4 (t / 32) .. + 3 and columns t % 32 + 32 c, c = 0..3: for each c the
+// 32 threads of a row group read consecutive doubles of the B chunk, free of bank conflicts.
 __device__ void kk_gemm(int K, double* out, const double* A, const double* B, double alpha, const double* base,
                         double base_scale, bool identity, double* lds) {
     constexpr int KC = 16;
     double (*As)[KC + 1] = reinterpret_cast<double (*)[KC + 1]>(lds);                     // 128 x 17
     double (*Bs)[CY_LDS_K + 4] = reinterpret_cast<double (*)[CY_LDS_K + 4]>(lds + CY_LDS_K * (KC + 1));   // 16 x 132
-    const int tid = threadIdx.x, r0 = 4 * (tid / 32), c0 = 4 * (tid % 32);
+    const int tid = threadIdx.x, r0 = 4 * (tid / 32), c0 = tid % 32;
     double acc[4][4] = {};
-    for (int l0 = 0; l0 < K; l0 += KC) {
-        for (int q = tid; q < CY_LDS_K * KC; q += CY_SOLVE_THREADS) {
+    // each thread moves NQ elements of each chunk; the next chunk's are loaded into
+    // registers while the current one is multiplied
+    constexpr int NQ = CY_LDS_K * KC / CY_SOLVE_THREADS;
+    static_assert(NQ * CY_SOLVE_THREADS == CY_LDS_K * KC, "whole chunks per thread");
+    double an[NQ], bn[NQ];
+    auto fetch = [&](int l0) {
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+            const int q = tid + u * CY_SOLVE_THREADS;
             const int i = q / KC, l = q % KC;
-            As[i][l] = (i < K && l0 + l < K) ? A[static_cast<size_t>(i) * K + l0 + l] : 0.0;
+            an[u] = (i < K && l0 + l < K) ? A[static_cast<size_t>(i) * K + l0 + l] : 0.0;
             const int bl = q / CY_LDS_K, bj = q % CY_LDS_K;
-            Bs[bl][bj] = (l0 + bl < K && bj < K) ? B[static_cast<size_t>(l0 + bl) * K + bj] : 0.0;
+            bn[u] = (l0 + bl < K && bj < K) ? B[static_cast<size_t>(l0 + bl) * K + bj] : 0.0;
         }
-        __syncthreads();
+    };
+    fetch(0);
+    for (int l0 = 0; l0 < K; l0 += KC) {
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+            const int q = tid + u * CY_SOLVE_THREADS;
+            As[q / KC][q % KC] = an[u];
+            Bs[q / CY_LDS_K][q % CY_LDS_K] = bn[u];
+        }
+        lds_barrier();
+        if (l0 + KC < K) fetch(l0 + KC);
 #pragma unroll 4
         for (int l = 0; l < KC; ++l) {
             double av[4], bv[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) av[r] = As[r0 + r][l];
 #pragma unroll
-            for (int cI = 0; cI < 4; ++cI) bv[cI] = Bs[l][c0 + cI];
+            for (int cI = 0; cI < 4; ++cI) bv[cI] = Bs[l][c0 + 32 * cI];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int cI = 0; cI < 4; ++cI) acc[r][cI] = fma(av[r], bv[cI], acc[r][cI]);
         }
-        __syncthreads();
+        lds_barrier();   // the chunk is read before the next one is stored
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int cI = 0; cI < 4; ++cI) {
-            const int i = r0 + r, j = c0 + cI;
+            const int i = r0 + r, j = c0 + 32 * cI;
             if (i >= K || j >= K) continue;
             const size_t q = static_cast<size_t>(i) * K + j;
             double v = alpha * acc[r][cI];
@@ -639,12 +674,29 @@ __device__ void solve_blocked(const CayleyDesc& d, double c, double* lds) {
     for (size_t q = tid; q < kk; q += CY_SOLVE_THREADS) {
         const int i = static_cast<int>(q / K), j = static_cast<int>(q % K);
         double ww = 0.0, wv = 0.0, vw = 0.0, vv = 0.0;   // (W^T W)ij, (W^T V)ij, (W^T V)ji, (V^T V)ij
-        for (int rb = 0; rb < d.nrb; ++rb) {
-            const float* pr = d.part + static_cast<size_t>(rb) * 3 * kk;
-            ww += G(pr)[q];
-            wv += G(pr)[kk + q];
-            vw += G(pr)[kk + static_cast<size_t>(j) * K + i];
-            vv += G(pr)[2 * kk + q];
+        // row blocks in ascending order; the loads of RB blocks are issued before their sums
+        constexpr int RB = 8;
+        for (int rb0 = 0; rb0 < d.nrb; rb0 += RB) {
+            float t[RB][4];
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+                if (rb0 + u < d.nrb) {
+                    const float* pr = d.part + static_cast<size_t>(rb0 + u) * 3 * kk;
+                    t[u][0] = G(pr)[q];
+                    t[u][1] = G(pr)[kk + q];
+                    t[u][2] = G(pr)[kk + static_cast<size_t>(j) * K + i];
+                    t[u][3] = G(pr)[2 * kk + q];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+                if (rb0 + u < d.nrb) {
+                    ww += t[u][0];
+                    wv += t[u][1];
+                    vw += t[u][2];
+                    vv += t[u][3];
+                }
+            }
         }
         WV[q] = wv;
         VV[q] = vv;

@@ -59,81 +59,100 @@ __global__ __launch_bounds__(CY_THREADS) void cy_transpose_in(CayleyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// K x K partial products over a row block: out_p[i][j] = sum_r X_p[r][i] Y_p[r][j]
-// 64 x 64 output tile, 256 threads with 4 x 4 outputs each.
+// The products use 128 x 128 output tiles, 256 threads with 8 x 8 outputs each:
+// rows 4 ty + u and 64 + 4 ty + u, columns 4 tx + v and 64 + 4 tx + v of the tile
+// (ty = t / 16, tx = t % 16, u, v < 4).  A staged 16-row chunk is read as float4,
+// contiguous across the lanes that share a row, and the next chunk is loaded into
+// registers while the current one is multiplied.  Sums run in ascending k.
 // ---------------------------------------------------------------------------
-template <int NP>
-__device__ void tn_block(const float* const (&X)[NP], const float* const (&Y)[NP], int K, int rs, int re,
-                         int i0, int j0, float* const (&out)[NP]) {
-    __shared__ float xs[NP][16][CY_T], ys[NP][16][CY_T];
+__device__ __forceinline__ int gt_off(int h) { return h < 4 ? h : 60 + h; }   // 4 x + gt_off(h): h-th of the 8
+
+// X[row][col .. col + 3] (row-major, pitch ld floats), zero outside rows < nrow and cols < ncol.
+__device__ __forceinline__ float4 ld4_guard(const float* base, size_t ld, int row, int nrow, int col, int ncol, bool vec) {
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (row >= nrow) return v;
+    const float* p = base + static_cast<size_t>(row) * ld + col;
+    if (vec && col + 3 < ncol) return ld_f4(p);
+    if (col < ncol) v.x = G(p)[0];
+    if (col + 1 < ncol) v.y = G(p)[1];
+    if (col + 2 < ncol) v.z = G(p)[2];
+    if (col + 3 < ncol) v.w = G(p)[3];
+    return v;
+}
+__device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// K x K partial product over rows [rs, re): out[i][j] = sum_r X[r][i] Y[r][j] for the
+// tile at (i0, j0).
+__device__ void tn_block(const float* X, const float* Y, int K, int rs, int re, int i0, int j0, float* out) {
+    constexpr int RC = 16, C4 = CY_GT / 4, NQ = RC * C4 / CY_THREADS;
+    static_assert(NQ * CY_THREADS == RC * C4, "whole chunks per thread");
+    __shared__ float4 xs[RC][C4], ys[RC][C4];
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    float acc[NP][4][4];
+    const bool vec = (K & 3) == 0 && aligned16(X) && aligned16(Y);
+    float acc[8][8];
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int v = 0; v < 8; ++v) acc[u][v] = 0.0f;
+    float4 xn[NQ], yn[NQ];
+    auto fetch = [&](int r) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) acc[p][u][v] = 0.0f;
-    for (int r = rs; r < re; r += 16) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int q = tid + CY_THREADS * e;
-            const int rr = q / CY_T, cc = q % CY_T;
-            const bool rok = r + rr < re;
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const size_t row = static_cast<size_t>(r + rr) * K;
-                xs[p][rr][cc] = (rok && i0 + cc < K) ? G(X[p])[row + i0 + cc] : 0.0f;
-                ys[p][rr][cc] = (rok && j0 + cc < K) ? G(Y[p])[row + j0 + cc] : 0.0f;
-            }
+        for (int e = 0; e < NQ; ++e) {
+            const int q = tid + e * CY_THREADS, rr = q / C4, c4 = q % C4;
+            xn[e] = ld4_guard(X, K, r + rr, re, i0 + 4 * c4, K, vec);
+            yn[e] = ld4_guard(Y, K, r + rr, re, j0 + 4 * c4, K, vec);
         }
-        __syncthreads();
-#pragma unroll 4
-        for (int rr = 0; rr < 16; ++rr) {
+    };
+    fetch(rs);
+    for (int r = rs; r < re; r += RC) {
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                float xa[4], yb[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) { xa[u] = xs[p][rr][ty * 4 + u]; yb[u] = ys[p][rr][tx * 4 + u]; }
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[p][u][v] = fmaf(xa[u], yb[v], acc[p][u][v]);
-            }
+        for (int e = 0; e < NQ; ++e) {
+            const int q = tid + e * CY_THREADS;
+            xs[q / C4][q % C4] = xn[e];
+            ys[q / C4][q % C4] = yn[e];
         }
-        __syncthreads();
+        lds_barrier();
+        if (r + RC < re) fetch(r + RC);
+#pragma unroll 2
+        for (int rr = 0; rr < RC; ++rr) {
+            const float4 a0 = xs[rr][ty], a1 = xs[rr][16 + ty], b0 = ys[rr][tx], b1 = ys[rr][16 + tx];
+            const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float yb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int v = 0; v < 8; ++v) acc[u][v] = fmaf(xa[u], yb[v], acc[u][v]);
+        }
+        lds_barrier();   // the chunk is read before the next one is stored
     }
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int i = i0 + ty * 4 + u, j = j0 + tx * 4 + v;
-                if (i < K && j < K) G(out[p])[static_cast<size_t>(i) * K + j] = acc[p][u][v];
-            }
+        for (int v = 0; v < 8; ++v) {
+            const int i = i0 + 4 * ty + gt_off(u), j = j0 + 4 * tx + gt_off(v);
+            if (i < K && j < K) G(out)[static_cast<size_t>(i) * K + j] = acc[u][v];
+        }
 }
 
+// One K x K product tile of one row block per workgroup.  REDUCE1: W^T G and W^T M;
+// REDUCE3: W^T W, W^T V and V^T V (the partial slots 0, 1, 2 of the row block).
 template <int PHASE>
 __global__ __launch_bounds__(CY_THREADS) void cy_reduce(CayleyArgs a) {
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
-    const int per = d.tk * d.tk;
-    const int rb = local / per, t2 = local % per;
-    const int i0 = (t2 / d.tk) * CY_T, j0 = (t2 % d.tk) * CY_T;
+    const int per = d.gk * d.gk;
+    const int t2 = local % per, rest = local / per;
+    const int rb = rest % d.nrb, prod = rest / d.nrb;
+    const int i0 = (t2 / d.gk) * CY_GT, j0 = (t2 % d.gk) * CY_GT;
     const int rs = rb * CY_RB, re = min(d.N, rs + CY_RB);
     const size_t kk = static_cast<size_t>(d.K) * d.K;
-    float* base = d.part + static_cast<size_t>(rb) * 3 * kk;
+    float* out = d.part + (static_cast<size_t>(rb) * 3 + prod) * kk;
     if (PHASE == CY_REDUCE1) {
-        const float* const X[2] = {d.wf, d.wf};
-        const float* const Y[2] = {d.gf, d.mf};
-        float* const out[2] = {base, base + kk};
-        tn_block<2>(X, Y, d.K, rs, re, i0, j0, out);
+        tn_block(d.wf, prod == 0 ? d.gf : d.mf, d.K, rs, re, i0, j0, out);
     } else {
-        const float* const X[3] = {d.wf, d.wf, d.v};
-        const float* const Y[3] = {d.wf, d.v, d.v};
-        float* const out[3] = {base, base + kk, base + 2 * kk};
-        tn_block<3>(X, Y, d.K, rs, re, i0, j0, out);
+        const float* X = prod == 2 ? d.v : d.wf;
+        const float* Y = prod == 0 ? d.wf : d.v;
+        tn_block(X, Y, d.K, rs, re, i0, j0, out);
     }
 }
 
@@ -208,41 +227,52 @@ __global__ __launch_bounds__(CY_THREADS) void cy_mid(CayleyArgs a) {
     }
 }
 
-// ---------------------------------------------------------------------------
-// N x K output tile (64 x 64) of A[., 0:Kr] B[0:Kr, .] accumulated into acc
-// (A row-major with lda, B row-major K-wide), 4 x 4 outputs per thread.
-// ---------------------------------------------------------------------------
+// acc += A[r0.., 0:Kr] B[0:Kr, c0..] for a 128 x 128 output tile (A row-major N x lda,
+// B row-major K wide), in the 8 x 8 per-thread layout of the products above.
 __device__ void nn_accumulate(const float* A, int lda, int N, const float* B, int K, int Kr, int r0, int c0,
-                              float (&acc)[4][4]) {
-    __shared__ float as[16][CY_T + 1], bs[16][CY_T];
+                              float (&acc)[8][8]) {
+    constexpr int KC = 16, C4 = CY_GT / 4, NQ = KC * C4 / CY_THREADS;
+    static_assert(NQ * CY_THREADS == KC * C4, "whole chunks per thread");
+    __shared__ float as[KC][CY_GT + 4];   // the A chunk transposed, as[k][row]; the pad spreads the stores
+    __shared__ float4 bs[KC][C4];
     const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-    for (int k0 = 0; k0 < Kr; k0 += 16) {
+    const bool avec = (lda & 3) == 0 && aligned16(A), bvec = (K & 3) == 0 && aligned16(B);
+    float4 an[NQ], bn[NQ];
+    auto fetch = [&](int k0) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int q = tid + CY_THREADS * e;
-            {   // A tile: 64 rows x 16 columns, stored transposed
-                const int rr = q / 16, kc = q % 16;
-                const int r = r0 + rr, k = k0 + kc;
-                as[kc][rr] = (r < N && k < Kr) ? G(A)[static_cast<size_t>(r) * lda + k] : 0.0f;
-            }
-            {   // B tile: 16 rows x 64 columns
-                const int kr = q / CY_T, cc = q % CY_T;
-                const int k = k0 + kr, c = c0 + cc;
-                bs[kr][cc] = (k < Kr && c < K) ? G(B)[static_cast<size_t>(k) * K + c] : 0.0f;
-            }
+        for (int e = 0; e < NQ; ++e) {
+            const int q = tid + e * CY_THREADS;
+            an[e] = ld4_guard(A, lda, r0 + q / 4, N, k0 + 4 * (q % 4), Kr, avec);   // row r0 + q/4, 4 k
+            const int kr = q / C4, c4 = q % C4;
+            bn[e] = ld4_guard(B, K, k0 + kr, Kr, c0 + 4 * c4, K, bvec);
         }
-        __syncthreads();
-#pragma unroll 4
-        for (int kc = 0; kc < 16; ++kc) {
-            float xa[4], yb[4];
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < Kr; k0 += KC) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) { xa[u] = as[kc][ty * 4 + u]; yb[u] = bs[kc][tx * 4 + u]; }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(xa[u], yb[v], acc[u][v]);
+        for (int e = 0; e < NQ; ++e) {
+            const int q = tid + e * CY_THREADS, row = q / 4, k4 = q % 4;
+            as[4 * k4 + 0][row] = an[e].x;
+            as[4 * k4 + 1][row] = an[e].y;
+            as[4 * k4 + 2][row] = an[e].z;
+            as[4 * k4 + 3][row] = an[e].w;
+            bs[q / C4][q % C4] = bn[e];
         }
-        __syncthreads();
+        lds_barrier();
+        if (k0 + KC < Kr) fetch(k0 + KC);
+#pragma unroll 2
+        for (int kc = 0; kc < KC; ++kc) {
+            const float4 a0 = *reinterpret_cast<const float4*>(&as[kc][4 * ty]);
+            const float4 a1 = *reinterpret_cast<const float4*>(&as[kc][64 + 4 * ty]);
+            const float4 b0 = bs[kc][tx], b1 = bs[kc][16 + tx];
+            const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float yb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int v = 0; v < 8; ++v) acc[u][v] = fmaf(xa[u], yb[v], acc[u][v]);
+        }
+        lds_barrier();   // the chunk is read before the next one is stored
     }
 }
 
@@ -250,17 +280,17 @@ __device__ void nn_accumulate(const float* A, int lda, int N, const float* B, in
 __global__ __launch_bounds__(CY_THREADS) void cy_p2(CayleyArgs a) {
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
-    const int r0 = (local / d.tk) * CY_T, c0 = (local % d.tk) * CY_T;
-    float acc[4][4] = {};
+    const int r0 = (local / d.gk) * CY_GT, c0 = (local % d.gk) * CY_GT;
+    float acc[8][8] = {};
     const float* S = d.small + d.K;
     nn_accumulate(d.wf, d.K, d.N, S, d.K, d.K, r0, c0, acc);
     const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
     const float beta = a.beta, omb = 1.0f - a.beta;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = r0 + ty * 4 + u, j = c0 + tx * 4 + v;
+        for (int v = 0; v < 8; ++v) {
+            const int r = r0 + 4 * ty + gt_off(u), j = c0 + 4 * tx + gt_off(v);
             if (r < d.N && j < d.K) {
                 const size_t idx = static_cast<size_t>(r) * d.K + j;
                 const float mn = fmaf(beta, G(d.mf)[idx], omb * (G(d.gf)[idx] - G(d.small)[j]));
@@ -274,18 +304,18 @@ __global__ __launch_bounds__(CY_THREADS) void cy_p2(CayleyArgs a) {
 __global__ __launch_bounds__(CY_THREADS) void cy_p4(CayleyArgs a) {
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
-    const int r0 = (local / d.tk) * CY_T, c0 = (local % d.tk) * CY_T;
+    const int r0 = (local / d.gk) * CY_GT, c0 = (local % d.gk) * CY_GT;
     const size_t kk = static_cast<size_t>(d.K) * d.K;
     const float* Y = d.small + d.K + kk;
-    float acc[4][4] = {};
+    float acc[8][8] = {};
     nn_accumulate(d.v, d.K, d.N, Y, d.K, d.K, r0, c0, acc);
     nn_accumulate(d.wf, d.K, d.N, Y + kk, d.K, d.K, r0, c0, acc);
     const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int r = r0 + ty * 4 + u, j = c0 + tx * 4 + v;
+        for (int v = 0; v < 8; ++v) {
+            const int r = r0 + 4 * ty + gt_off(u), j = c0 + 4 * tx + gt_off(v);
             if (r < d.N && j < d.K) {
                 const size_t idx = static_cast<size_t>(r) * d.K + j;
                 G(d.wnew)[idx] = fmaf(-a.c, acc[u][v], G(d.wf)[idx]);

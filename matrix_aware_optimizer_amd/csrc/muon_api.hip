@@ -622,6 +622,8 @@ muon_status collect_cayley(const muon_cayley_matrix* mats, int32_t n, const muon
         d.nrb = (d.N + CY_RB - 1) / CY_RB;
         d.tk = (d.K + CY_T - 1) / CY_T;
         d.tn = (d.N + CY_T - 1) / CY_T;
+        d.gk = (d.K + CY_GT - 1) / CY_GT;
+        d.gn = (d.N + CY_GT - 1) / CY_GT;
         out.push_back(d);
     }
     return check_overlaps(iv);
@@ -637,8 +639,10 @@ muon_status build_cayley_plan(std::vector<CayleyDesc>& descs, CayleyPlan& pl) {
     int64_t tot[CY_PHASES] = {};
     for (size_t k = 0; k < nmat; ++k) {
         CayleyDesc& d = descs[k];
-        const int64_t tiles = static_cast<int64_t>(d.tn) * d.tk, red = static_cast<int64_t>(d.nrb) * d.tk * d.tk;
-        const int64_t per[CY_PHASES] = {d.tall ? 0 : tiles, red, d.nrb, CY_MID_SPLIT, tiles, red, 1, tiles, tiles};
+        const int64_t tiles = static_cast<int64_t>(d.tn) * d.tk;          // 64 x 64 transpose tiles
+        const int64_t prod = static_cast<int64_t>(d.gn) * d.gk;           // 128 x 128 N x K product tiles
+        const int64_t red = static_cast<int64_t>(d.nrb) * d.gk * d.gk;    // K x K tiles over the row blocks, per product
+        const int64_t per[CY_PHASES] = {d.tall ? 0 : tiles, 2 * red, d.nrb, CY_MID_SPLIT, prod, 3 * red, 1, prod, tiles};
         for (int ph = 0; ph < CY_PHASES; ++ph) {
             tot[ph] += per[ph];
             if (tot[ph] > INT32_MAX) return fail(MUON_ERR_UNSUPPORTED, "too many tiles in one call (split the list)");

@@ -106,7 +106,8 @@ struct AdamWArgs {
 // otherwise.  K x K reductions over N are split into row blocks of CY_RB rows
 // whose partials are summed in a fixed order.
 constexpr int CAYLEY_MAX_K = 256;
-constexpr int CY_T = 64;          // output tile edge of the small GEMMs and K x K products
+constexpr int CY_T = 64;          // tile edge of the frame transposes
+constexpr int CY_GT = 128;        // output tile edge of the N x K and K x K products
 constexpr int CY_RB = 512;        // rows per reduction block
 constexpr int CY_THREADS = 256;
 constexpr int CY_SOLVE_THREADS = 1024;
@@ -121,6 +122,8 @@ struct CayleyDesc {
     int32_t nrb;         // reduction row blocks
     int32_t tk;          // K tiles per side: ceil(K / CY_T)
     int32_t tn;          // N tiles: ceil(N / CY_T)
+    int32_t gk;          // product tiles per K side: ceil(K / CY_GT)
+    int32_t gn;          // product tiles along N: ceil(N / CY_GT)
     float* wf;           // frame W (caller's buffer when tall)
     const float* gf;     // frame G
     float* mf;           // frame M, updated in place

@@ -86,3 +86,27 @@ def test_cayley_zero_lr_and_skipped_matrices(gpu_lib):
     assert np.array_equal(Ws[0], hosts[0]["W"])
     assert _rel(Ms[0], orc.cayley_step(hosts[0]["W"], hosts[0]["G"], hosts[0]["M"], lr=0.0, beta=0.9)["M"]) <= 1e-5
     assert np.array_equal(Ws[1], hosts[1]["W"]) and np.array_equal(Ms[1], hosts[1]["M"])
+
+
+def test_cayley_full_width_blocks(gpu_lib):
+    # K = 128 fills every column block of the in-register inverse and the 128-wide product
+    # tiles; K = 100 pads the last block; the wide 128 x 2000 goes through the transposed frame
+    shapes = [(4096, 128), (1000, 100), (128, 2000)]
+    hosts = [wk.cayley_host_matrix(r, c, seed=40 + i) for i, (r, c) in enumerate(shapes)]
+    _say("full width", shapes)
+    Ws, Ms = _run(gpu_lib, hosts, 0.05, 0.9)
+    for h, w, m in zip(hosts, Ws, Ms):
+        _check(h, w, m, 0.05, 0.9)
+
+
+def test_cayley_benchmark_set(gpu_lib):
+    # the grouped set the benchmark times, in one call: four sampled matrices against the
+    # oracle (about a second each in fp64), orthonormal columns for all of them
+    hosts = [wk.cayley_host_matrix(r, c, seed=200 + i) for i, (r, c) in enumerate(wk.CAYLEY_SET)]
+    _say("benchmark set", len(hosts), "matrices")
+    Ws, Ms = _run(gpu_lib, hosts, 1e-3, 0.9)
+    n = len(hosts)
+    for i in sorted({0, n // 3, (2 * n) // 3, n - 1}):
+        _check(hosts[i], Ws[i], Ms[i], 1e-3, 0.9)
+    for w in Ws:
+        assert orc.orthogonality_error(w) <= 3e-5

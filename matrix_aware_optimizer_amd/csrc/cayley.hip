@@ -518,72 +518,6 @@ __device__ void solve_global(const CayleyDesc& d, double cc, double* arena) {
 // block is nonsingular: det C = det(I + c A) != 0 for skew A, C11 = I + c WV
 // with WV skew up to rounding, and det C = det C11 det S.
 // ---------------------------------------------------------------------------
-constexpr int CY_LDS_K = 128;
-
-// out = base_scale * base + (identity ? I : 0) + alpha * A B   (K x K, pitch K, fp64, global).
-// out may be base (each element is read and written by one thread) but not A or B.
-// Thread t owns rows 4 (t / 32) .. + 3 and columns t % 32 + 32 c, c = 0..3: for each c the
-// 32 threads of a row group read consecutive doubles of the B chunk, free of bank conflicts.
-__device__ void kk_gemm(int K, double* out, const double* A, const double* B, double alpha, const double* base,
-                        double base_scale, bool identity, double* lds) {
-    constexpr int KC = 16;
-    double (*As)[KC + 1] = reinterpret_cast<double (*)[KC + 1]>(lds);                     // 128 x 17
-    double (*Bs)[CY_LDS_K + 4] = reinterpret_cast<double (*)[CY_LDS_K + 4]>(lds + CY_LDS_K * (KC + 1));   // 16 x 132
-    const int tid = threadIdx.x, r0 = 4 * (tid / 32), c0 = tid % 32;
-    double acc[4][4] = {};
-    // each thread moves NQ elements of each chunk; the next chunk's are loaded into
-    // registers while the current one is multiplied
-    constexpr int NQ = CY_LDS_K * KC / CY_SOLVE_THREADS;
-    static_assert(NQ * CY_SOLVE_THREADS == CY_LDS_K * KC, "whole chunks per thread");
-    double an[NQ], bn[NQ];
-    auto fetch = [&](int l0) {
-#pragma unroll
-        for (int u = 0; u < NQ; ++u) {
-            const int q = tid + u * CY_SOLVE_THREADS;
-            const int i = q / KC, l = q % KC;
-            an[u] = (i < K && l0 + l < K) ? A[static_cast<size_t>(i) * K + l0 + l] : 0.0;
-            const int bl = q / CY_LDS_K, bj = q % CY_LDS_K;
-            bn[u] = (l0 + bl < K && bj < K) ? B[static_cast<size_t>(l0 + bl) * K + bj] : 0.0;
-        }
-    };
-    fetch(0);
-    for (int l0 = 0; l0 < K; l0 += KC) {
-#pragma unroll
-        for (int u = 0; u < NQ; ++u) {
-            const int q = tid + u * CY_SOLVE_THREADS;
-            As[q / KC][q % KC] = an[u];
-            Bs[q / CY_LDS_K][q % CY_LDS_K] = bn[u];
-        }
-        lds_barrier();
-        if (l0 + KC < K) fetch(l0 + KC);
-#pragma unroll 4
-        for (int l = 0; l < KC; ++l) {
-            double av[4], bv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) av[r] = As[r0 + r][l];
-#pragma unroll
-            for (int cI = 0; cI < 4; ++cI) bv[cI] = Bs[l][c0 + 32 * cI];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int cI = 0; cI < 4; ++cI) acc[r][cI] = fma(av[r], bv[cI], acc[r][cI]);
-        }
-        lds_barrier();   // the chunk is read before the next one is stored
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int cI = 0; cI < 4; ++cI) {
-            const int i = r0 + r, j = c0 + 32 * cI;
-            if (i >= K || j >= K) continue;
-            const size_t q = static_cast<size_t>(i) * K + j;
-            double v = alpha * acc[r][cI];
-            if (base) v += base_scale * base[q];
-            if (identity && i == j) v += 1.0;
-            out[q] = v;
-        }
-    __syncthreads();
-}
 
 // out = ((identity ? I : 0) + scale * src)^-1 by Gauss-Jordan with partial pivoting.
 // The working matrix, 128 x 128 with the identity beyond K, lives in registers:
@@ -592,7 +526,8 @@ __device__ void kk_gemm(int K, double* out, const double* A, const double* B, do
 // the smaller row) and eliminates column j in place, so the final matrix E holds
 // the inverse permuted, inv[a][p_b] = E[p_a][b].  Per step only the pivot search
 // and the scaled pivot row pass through LDS.  out may be src.
-__device__ void kk_gj_inverse(int K, double* out, const double* src, double scale, bool identity, double* lds) {
+__device__ __attribute__((always_inline)) void kk_gj_inverse(int K, double* out, const double* src, double scale, bool identity,
+                                                           double* lds) {
     static_assert(CY_SOLVE_THREADS == 8 * CY_LDS_K, "eight threads per row of the 128 x 128 matrix");
     constexpr int CB = 16;   // columns per thread
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -688,24 +623,116 @@ __device__ void kk_gj_inverse(int K, double* out, const double* src, double scal
     __syncthreads();   // out is complete (global) before the next product reads it
 }
 
-__device__ void solve_blocked(const CayleyDesc& d, double c, double* lds) {
-    const int K = d.K, tid = threadIdx.x;
+// ---------------------------------------------------------------------------
+// Split solve for K <= CY_LDS_K.  The K x K fp64 blocks live in the workspace
+// (pitch K); each phase reads only blocks that earlier phases wrote:
+//   SV_SUM   WW, WV, VV and bwb = -VW from the row-block partials;
+//   SV_R     r1 = WW - c (WV WW) - c (WW bwb),  r2 = bwb - c (bwb bwb) + c (VV WW);
+//   SOLVE    C11^-1 = (I + c WV)^-1 (one workgroup per matrix);
+//   SV_G1    X = c C11^-1 WW,  y = C11^-1 r1 (into WV's block);
+//   SV_G2    S = I + c bwb + c VV X (into r1's block),  r' = r2 + c VV y (into C11^-1's);
+//   SV_INV2  S^-1 in place (one workgroup per matrix);
+//   SV_G3    z2 = S^-1 r' (into VV's block);
+//   SV_G4    z1 = y - X z2, and Y = B W + Z in fp32 for the final pass.
+// The products run as 64 x 64 tiles on many workgroups, each element summed in
+// ascending k as one fma chain.
+// ---------------------------------------------------------------------------
+constexpr int SV_T = CY_SV_T;
+struct SvBlocks {
+    double *WV, *VV, *C11i, *Xm, *R1, *R2, *WW, *bwb;
+    __device__ explicit SvBlocks(const CayleyDesc& d) {
+        const size_t kk = static_cast<size_t>(d.K) * d.K;
+        WV = d.cmat; VV = d.cmat + kk; C11i = d.cmat + 2 * kk; Xm = d.cmat + 3 * kk;
+        R1 = d.rhs; R2 = d.rhs + kk; WW = d.bw; bwb = d.bw + kk;
+    }
+};
+__device__ __forceinline__ int sv_tiles(int K) { const int g = (K + SV_T - 1) / SV_T; return g * g; }
+
+// acc = A B for the 64 x 64 tile (ti, tj) of a K x K product (pitch K).  Thread t holds rows
+// 4 (t / 16) + u and columns t % 16 + 16 v (u, v < 4); the next 16-wide k-chunk is loaded
+// into registers while the current one is multiplied.
+__device__ void sv_product(int K, const double* A, const double* B, int ti, int tj, double (&acc)[4][4]) {
+    constexpr int KC = 16, NQ = SV_T * KC / CY_THREADS;
+    static_assert(NQ * CY_THREADS == SV_T * KC, "whole chunks per thread");
+    __shared__ double As[SV_T][KC + 1], Bs[KC][SV_T + 4];
+    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    const int r0 = ti * SV_T, c0 = tj * SV_T;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+    double an[NQ], bn[NQ];
+    auto fetch = [&](int l0) {
+#pragma unroll
+        for (int e = 0; e < NQ; ++e) {
+            const int q = tid + e * CY_THREADS;
+            const int i = q / KC, l = q % KC;
+            an[e] = (r0 + i < K && l0 + l < K) ? A[static_cast<size_t>(r0 + i) * K + l0 + l] : 0.0;
+            const int bl = q / SV_T, bj = q % SV_T;
+            bn[e] = (l0 + bl < K && c0 + bj < K) ? B[static_cast<size_t>(l0 + bl) * K + c0 + bj] : 0.0;
+        }
+    };
+    fetch(0);
+    for (int l0 = 0; l0 < K; l0 += KC) {
+#pragma unroll
+        for (int e = 0; e < NQ; ++e) {
+            const int q = tid + e * CY_THREADS;
+            As[q / KC][q % KC] = an[e];
+            Bs[q / SV_T][q % SV_T] = bn[e];
+        }
+        lds_barrier();
+        if (l0 + KC < K) fetch(l0 + KC);
+#pragma unroll 4
+        for (int l = 0; l < KC; ++l) {
+            double av[4], bv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) av[u] = As[4 * ty + u][l];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) bv[v] = Bs[l][tx + 16 * v];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] = fma(av[u], bv[v], acc[u][v]);
+        }
+        lds_barrier();   // the chunk is read before the next one is stored
+    }
+}
+
+// out = alpha A B + base_scale base (+ I): one tile, each element rounded as
+// alpha * acc, then + base_scale * base, then + 1 on the diagonal.
+__device__ void sv_gemm(int K, double* out, const double* A, const double* B, double alpha, const double* base,
+                        double base_scale, bool identity, int tile) {
+    const int g = (K + SV_T - 1) / SV_T, ti = tile / g, tj = tile % g;
+    double acc[4][4];
+    sv_product(K, A, B, ti, tj, acc);
+    const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = ti * SV_T + 4 * ty + u, j = tj * SV_T + tx + 16 * v;
+            if (i >= K || j >= K) continue;
+            const size_t q = static_cast<size_t>(i) * K + j;
+            double x = alpha * acc[u][v];
+            if (base) x += base_scale * base[q];
+            if (identity && i == j) x += 1.0;
+            out[q] = x;
+        }
+}
+
+// SV_SUM: the K x K blocks of one 64 x 64 tile from the partials (fp64 sums in row-block order)
+__global__ __launch_bounds__(CY_THREADS) void cy_sv_sum(CayleyArgs a) {
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const SvBlocks bk(d);
+    const int K = d.K, g = (K + SV_T - 1) / SV_T, ti = local / g, tj = local % g;
     const size_t kk = static_cast<size_t>(K) * K;
-    // K x K fp64 blocks in the workspace (pitch K)
-    double* WV = d.cmat;            // then y
-    double* VV = d.cmat + kk;
-    double* C11i = d.cmat + 2 * kk; // then r'
-    double* Xm = d.cmat + 3 * kk;
-    double* R1 = d.rhs;             // then S, then S^-1
-    double* R2 = d.rhs + kk;        // then z1
-    double* WW = d.bw;              // B W = [WW; bwb], bwb = -VW
-    double* bwb = d.bw + kk;
-    // 1. WW, WV, VV and B W from the partials (fp64 sums in row-block order)
-    for (size_t q = tid; q < kk; q += CY_SOLVE_THREADS) {
-        const int i = static_cast<int>(q / K), j = static_cast<int>(q % K);
+    for (int e = threadIdx.x; e < SV_T * SV_T; e += CY_THREADS) {
+        const int i = ti * SV_T + e / SV_T, j = tj * SV_T + e % SV_T;
+        if (i >= K || j >= K) continue;
+        const size_t q = static_cast<size_t>(i) * K + j;
         double ww = 0.0, wv = 0.0, vw = 0.0, vv = 0.0;   // (W^T W)ij, (W^T V)ij, (W^T V)ji, (V^T V)ij
-        // row blocks in ascending order; the loads of RB blocks are issued before their sums
-        constexpr int RB = 8;
+        constexpr int RB = 8;   // row blocks in ascending order, RB blocks' loads issued before their sums
         for (int rb0 = 0; rb0 < d.nrb; rb0 += RB) {
             float t[RB][4];
 #pragma unroll
@@ -728,50 +755,91 @@ __device__ void solve_blocked(const CayleyDesc& d, double c, double* lds) {
                 }
             }
         }
-        WV[q] = wv;
-        VV[q] = vv;
-        WW[q] = ww;
-        bwb[q] = -vw;
-    }
-    __syncthreads();
-    // 2. right-hand side r = B W - c (B U)(B W):
-    //    r1 = WW - c (WV WW - WW VW),  r2 = -VW - c (VW VW - VV WW)
-    kk_gemm(K, R1, WV, WW, -c, WW, 1.0, false, lds);
-    kk_gemm(K, R1, WW, bwb, -c, R1, 1.0, false, lds);      // + c WW VW = - c WW bwb
-    kk_gemm(K, R2, bwb, bwb, -c, bwb, 1.0, false, lds);    // VW VW = bwb bwb
-    kk_gemm(K, R2, VV, WW, c, R2, 1.0, false, lds);
-    // 3. C11^-1 = (I + c WV)^-1
-    kk_gj_inverse(K, C11i, WV, c, true, lds);
-    // 4. X = C11^-1 (c WW), y = C11^-1 r1 (into WV's block, no longer needed)
-    kk_gemm(K, Xm, C11i, WW, c, nullptr, 0.0, false, lds);
-    double* y = WV;
-    kk_gemm(K, y, C11i, R1, 1.0, nullptr, 0.0, false, lds);
-    // 5. S = C22 - C21 X = I + c bwb + c VV X;  r' = r2 + c VV y
-    double* S = R1;
-    kk_gemm(K, S, VV, Xm, c, bwb, c, true, lds);
-    double* rp = C11i;
-    kk_gemm(K, rp, VV, y, c, R2, 1.0, false, lds);
-    // 6. z2 = S^-1 r',  z1 = y - X z2
-    kk_gj_inverse(K, S, S, 1.0, false, lds);
-    double* z2 = VV;
-    kk_gemm(K, z2, S, rp, 1.0, nullptr, 0.0, false, lds);
-    double* z1 = R2;
-    kk_gemm(K, z1, Xm, z2, -1.0, y, 1.0, false, lds);
-    // 7. Y = B W + Z, fp32 for the final pass (rows 0..K-1: top, K..2K-1: bottom)
-    float* Y = d.small + K + kk;
-    for (size_t q = tid; q < kk; q += CY_SOLVE_THREADS) {
-        G(Y)[q] = static_cast<float>(WW[q] + z1[q]);
-        G(Y)[kk + q] = static_cast<float>(bwb[q] + z2[q]);
+        bk.WV[q] = wv;
+        bk.VV[q] = vv;
+        bk.WW[q] = ww;
+        bk.bwb[q] = -vw;
     }
 }
 
+// SV_R: right-hand side r = B W - c (B U)(B W), each block as two products in turn
+__global__ __launch_bounds__(CY_THREADS) void cy_sv_r(CayleyArgs a) {
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const SvBlocks bk(d);
+    const int nt = sv_tiles(d.K), tile = local % nt;
+    const double c = a.c;
+    if (local < nt) {   // r1 = WW - c WV WW - c WW bwb
+        sv_gemm(d.K, bk.R1, bk.WV, bk.WW, -c, bk.WW, 1.0, false, tile);
+        sv_gemm(d.K, bk.R1, bk.WW, bk.bwb, -c, bk.R1, 1.0, false, tile);
+    } else {            // r2 = bwb - c bwb bwb + c VV WW
+        sv_gemm(d.K, bk.R2, bk.bwb, bk.bwb, -c, bk.bwb, 1.0, false, tile);
+        sv_gemm(d.K, bk.R2, bk.VV, bk.WW, c, bk.R2, 1.0, false, tile);
+    }
+}
+
+// SV_G1 .. SV_G4
+template <int PHASE>
+__global__ __launch_bounds__(CY_THREADS) void cy_sv_gemm(CayleyArgs a) {
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const SvBlocks bk(d);
+    const int K = d.K, nt = sv_tiles(K), tile = local % nt, which = local / nt;
+    const double c = a.c;
+    double* y = bk.WV;
+    double* S = bk.R1;
+    double* rp = bk.C11i;
+    double* z2 = bk.VV;
+    if (PHASE == CY_SV_G1) {
+        if (which == 0) sv_gemm(K, bk.Xm, bk.C11i, bk.WW, c, nullptr, 0.0, false, tile);
+        else sv_gemm(K, y, bk.C11i, bk.R1, 1.0, nullptr, 0.0, false, tile);
+    } else if (PHASE == CY_SV_G2) {
+        if (which == 0) sv_gemm(K, S, bk.VV, bk.Xm, c, bk.bwb, c, true, tile);
+        else sv_gemm(K, rp, bk.VV, y, c, bk.R2, 1.0, false, tile);
+    } else if (PHASE == CY_SV_G3) {
+        sv_gemm(K, z2, S, rp, 1.0, nullptr, 0.0, false, tile);
+    } else {
+        // z1 = y - X z2, then Y = B W + Z in fp32 (rows 0..K-1: top, K..2K-1: bottom), each
+        // element by the thread that forms it
+        const int g = (K + SV_T - 1) / SV_T, ti = tile / g, tj = tile % g;
+        double acc[4][4];
+        sv_product(K, bk.Xm, z2, ti, tj, acc);
+        const size_t kk = static_cast<size_t>(K) * K;
+        float* Y = d.small + K + kk;
+        const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = ti * SV_T + 4 * ty + u, j = tj * SV_T + tx + 16 * v;
+                if (i >= K || j >= K) continue;
+                const size_t q = static_cast<size_t>(i) * K + j;
+                double z1 = -1.0 * acc[u][v];
+                z1 += 1.0 * y[q];
+                G(Y)[q] = static_cast<float>(bk.WW[q] + z1);
+                G(Y)[kk + q] = static_cast<float>(bk.bwb[q] + z2[q]);
+            }
+    }
+}
+
+// SOLVE: C11^-1 for K <= CY_LDS_K, the whole 2K x 2K LU solve otherwise; SV_INV2: S^-1
 __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
     __shared__ double arena[CY_LDS_K * CY_LDS_K + 3 * CY_LDS_K];
-    const CayleyDesc& d = a.descs[blockIdx.x];
-    if (d.K <= CY_LDS_K)
-        solve_blocked(d, a.c, arena);
-    else
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    if (d.K <= CY_LDS_K) {
+        const SvBlocks bk(d);
+        kk_gj_inverse(d.K, bk.C11i, bk.WV, a.c, true, arena);
+    } else {
         solve_global(d, a.c, arena);
+    }
+}
+__global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_sv_inv2(CayleyArgs a) {
+    __shared__ double arena[CY_LDS_K * CY_LDS_K + 3 * CY_LDS_K];
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const SvBlocks bk(d);
+    kk_gj_inverse(d.K, bk.R1, bk.R1, 1.0, false, arena);
 }
 
 }  // namespace
@@ -787,6 +855,13 @@ hipError_t launch_cayley(int phase, const CayleyArgs& args, hipStream_t s) {
         case CY_P2: hipLaunchKernelGGL(cy_p2, grid, block, 0, s, args); break;
         case CY_REDUCE3: hipLaunchKernelGGL(cy_reduce<CY_REDUCE3>, grid, block, 0, s, args); break;
         case CY_SOLVE: hipLaunchKernelGGL(cy_solve, grid, dim3(CY_SOLVE_THREADS), 0, s, args); break;
+        case CY_SV_SUM: hipLaunchKernelGGL(cy_sv_sum, grid, block, 0, s, args); break;
+        case CY_SV_R: hipLaunchKernelGGL(cy_sv_r, grid, block, 0, s, args); break;
+        case CY_SV_G1: hipLaunchKernelGGL(cy_sv_gemm<CY_SV_G1>, grid, block, 0, s, args); break;
+        case CY_SV_G2: hipLaunchKernelGGL(cy_sv_gemm<CY_SV_G2>, grid, block, 0, s, args); break;
+        case CY_SV_INV2: hipLaunchKernelGGL(cy_sv_inv2, grid, dim3(CY_SOLVE_THREADS), 0, s, args); break;
+        case CY_SV_G3: hipLaunchKernelGGL(cy_sv_gemm<CY_SV_G3>, grid, block, 0, s, args); break;
+        case CY_SV_G4: hipLaunchKernelGGL(cy_sv_gemm<CY_SV_G4>, grid, block, 0, s, args); break;
         case CY_P4: hipLaunchKernelGGL(cy_p4, grid, block, 0, s, args); break;
         case CY_OUT: hipLaunchKernelGGL(cy_out, grid, block, 0, s, args); break;
         default: return hipErrorInvalidValue;

@@ -578,7 +578,6 @@ muon_status collect_adamw(const muon_adamw_tensor* ts, int32_t n, const muon_ada
 // Muon-Cayley
 // ---------------------------------------------------------------------------
 
-constexpr int CY_PHASES = 9;
 
 struct CayleyPlan {
     std::vector<CayleyDesc> descs;
@@ -642,7 +641,26 @@ muon_status build_cayley_plan(std::vector<CayleyDesc>& descs, CayleyPlan& pl) {
         const int64_t tiles = static_cast<int64_t>(d.tn) * d.tk;          // 64 x 64 transpose tiles
         const int64_t prod = static_cast<int64_t>(d.gn) * d.gk;           // 128 x 128 N x K product tiles
         const int64_t red = static_cast<int64_t>(d.nrb) * d.gk * d.gk;    // K x K tiles over the row blocks, per product
-        const int64_t per[CY_PHASES] = {d.tall ? 0 : tiles, 2 * red, d.nrb, CY_MID_SPLIT, prod, 3 * red, 1, prod, tiles};
+        // split solve (K <= CY_LDS_K): tiles of the K x K blocks; a larger K solves in CY_SOLVE alone
+        const int64_t svg = (d.K + CY_SV_T - 1) / CY_SV_T;
+        const int64_t sv = d.K <= CY_LDS_K ? svg * svg : 0;
+        int64_t per[CY_PHASES] = {};
+        per[CY_TRANSPOSE_IN] = d.tall ? 0 : tiles;
+        per[CY_REDUCE1] = 2 * red;
+        per[CY_COLSUM] = d.nrb;
+        per[CY_MID] = CY_MID_SPLIT;
+        per[CY_P2] = prod;
+        per[CY_REDUCE3] = 3 * red;
+        per[CY_SV_SUM] = sv;
+        per[CY_SV_R] = 2 * sv;
+        per[CY_SOLVE] = 1;
+        per[CY_SV_G1] = 2 * sv;
+        per[CY_SV_G2] = 2 * sv;
+        per[CY_SV_INV2] = sv ? 1 : 0;
+        per[CY_SV_G3] = sv;
+        per[CY_SV_G4] = sv;
+        per[CY_P4] = prod;
+        per[CY_OUT] = tiles;
         for (int ph = 0; ph < CY_PHASES; ++ph) {
             tot[ph] += per[ph];
             if (tot[ph] > INT32_MAX) return fail(MUON_ERR_UNSUPPORTED, "too many tiles in one call (split the list)");
@@ -756,7 +774,9 @@ muon_status muon_cayley_step(const muon_cayley_matrix* mats, int32_t n, const mu
     a.nmat = static_cast<int32_t>(nmat);
     a.beta = hp->beta;
     a.c = 0.5f * hp->lr;
-    const int order[CY_PHASES] = {CY_TRANSPOSE_IN, CY_REDUCE1, CY_COLSUM, CY_MID, CY_P2, CY_REDUCE3, CY_SOLVE, CY_P4, CY_OUT};
+    const int order[CY_PHASES] = {CY_TRANSPOSE_IN, CY_REDUCE1, CY_COLSUM, CY_MID,   CY_P2,    CY_REDUCE3,
+                                  CY_SV_SUM,       CY_SV_R,    CY_SOLVE,  CY_SV_G1, CY_SV_G2, CY_SV_INV2,
+                                  CY_SV_G3,        CY_SV_G4,   CY_P4,     CY_OUT};
     for (int ph : order) {
         a.prefix = reinterpret_cast<const int32_t*>(base + pl.off_prefix + sizeof(int32_t) * ph * (nmat + 1));
         a.total = pl.prefix[ph][nmat];

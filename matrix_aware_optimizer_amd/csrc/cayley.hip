@@ -623,12 +623,74 @@ __device__ __attribute__((always_inline)) void kk_gj_inverse(int K, double* out,
     __syncthreads();   // out is complete (global) before the next product reads it
 }
 
+// out = (I + scale * src)^-1 by Gauss-Jordan without pivoting, for C11 = I + c W^T V:
+// W^T V = skew(W^T M') on the manifold, so C11's symmetric part is I and every pivot has
+// real part >= 1.  Same register layout as kk_gj_inverse; per step only the scaled pivot
+// row goes through LDS, with one barrier.  Returns false, with out untouched, if a pivot
+// falls below 1/2 in magnitude (W far off the manifold); the caller then pivots.
+__device__ __attribute__((always_inline)) bool kk_gj_inverse_unpivoted(int K, double* out, const double* src, double scale,
+                                                                     double* lds) {
+    static_assert(CY_SOLVE_THREADS == 8 * CY_LDS_K, "eight threads per row of the 128 x 128 matrix");
+    constexpr int CB = 16, PSTRIDE = CB + 1, PBUF = 8 * PSTRIDE;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int i = tid >> 3, cb = tid & 7;
+    double* prow = lds;   // [2][8][17] scaled pivot row, as in kk_gj_inverse
+    double m[CB];
+#pragma unroll
+    for (int k = 0; k < CB; ++k) {
+        const int col = CB * cb + k;
+        if (i < K && col < K)
+            m[k] = (i == col ? 1.0 : 0.0) + scale * src[static_cast<size_t>(i) * K + col];
+        else
+            m[k] = i == col ? 1.0 : 0.0;
+    }
+    bool ok = true;
+    for (int jb = 0; jb < CY_LDS_K / CB && CB * jb < K && ok; ++jb) {
+#pragma unroll
+        for (int e = 0; e < CB; ++e) {
+            const int j = CB * jb + e;
+            if (j < K && ok) {   // uniform
+                const int buf = j & 1;
+                const double colf = __shfl(m[e], (lane & ~7) | jb, 64);   // M[i][j]; M[j][j] on row j
+                if (i == j) {
+                    const double inv = 1.0 / colf;
+#pragma unroll
+                    for (int k = 0; k < CB; ++k) {
+                        m[k] = (CB * cb + k == j) ? inv : m[k] * inv;
+                        prow[buf * PBUF + PSTRIDE * cb + k] = m[k];
+                    }
+                }
+                lds_barrier();
+                const double inv = prow[buf * PBUF + PSTRIDE * jb + e];
+                ok = fabs(inv) <= 2.0;   // |pivot| >= 1/2, the same decision in every thread
+                if (i != j) {
+#pragma unroll
+                    for (int k = 0; k < CB; ++k) {
+                        const int col = CB * cb + k;
+                        m[k] = col == j ? -colf * inv : m[k] - colf * prow[buf * PBUF + PSTRIDE * cb + k];
+                    }
+                }
+            }
+        }
+    }
+    if (ok && i < K) {
+#pragma unroll
+        for (int k = 0; k < CB; ++k) {
+            const int b = CB * cb + k;
+            if (b < K) out[static_cast<size_t>(i) * K + b] = m[k];
+        }
+    }
+    __syncthreads();   // out is complete (global), and every thread has left the LDS buffers
+    return ok;
+}
+
 // ---------------------------------------------------------------------------
 // Split solve for K <= CY_LDS_K.  The K x K fp64 blocks live in the workspace
 // (pitch K); each phase reads only blocks that earlier phases wrote:
 //   SV_SUM   WW, WV, VV and bwb = -VW from the row-block partials;
 //   SV_R     r1 = WW - c (WV WW) - c (WW bwb),  r2 = bwb - c (bwb bwb) + c (VV WW);
-//   SOLVE    C11^-1 = (I + c WV)^-1 (one workgroup per matrix);
+//   SOLVE    C11^-1 = (I + c WV)^-1 (one workgroup per matrix; unpivoted, pivoting if
+//            a pivot is small);
 //   SV_G1    X = c C11^-1 WW,  y = C11^-1 r1 (into WV's block);
 //   SV_G2    S = I + c bwb + c VV X (into r1's block),  r' = r2 + c VV y (into C11^-1's);
 //   SV_INV2  S^-1 in place (one workgroup per matrix);
@@ -829,7 +891,8 @@ __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
     if (d.K <= CY_LDS_K) {
         const SvBlocks bk(d);
-        kk_gj_inverse(d.K, bk.C11i, bk.WV, a.c, true, arena);
+        if (!kk_gj_inverse_unpivoted(d.K, bk.C11i, bk.WV, a.c, arena))
+            kk_gj_inverse(d.K, bk.C11i, bk.WV, a.c, true, arena);
     } else {
         solve_global(d, a.c, arena);
     }

@@ -9,6 +9,10 @@
   sign of A and c = lr / 2.
 * The page's Woodbury form (section 6.2) equals the n x n solve.
 * Momentum of centered constant gradients: M_t = (1 - beta^t) G_centered.
+* The leading block C11 = I + c W^T V of the 2k system (section 6.2): on the
+  manifold W^T V is skew, so C11's symmetric part is I and elimination without
+  pivoting meets pivots of magnitude >= 1; off it (W = 2 Q) a pivot can fall
+  below 1/2.  The GPU path inverts C11 unpivoted and pivots when that happens.
 * Planted mistakes are each caught.
 """
 import numpy as np
@@ -151,3 +155,37 @@ def test_pins_catch_planted_mistake(kind, monkeypatch):
         n = _pins_fail(monkeypatch, cayley_step=plain)
         assert co.cayley_step is not orig
     assert n > 0, kind
+
+
+def _unpivoted_pivots(C):
+    C = np.array(C, np.float64)
+    piv = []
+    for j in range(C.shape[0]):
+        piv.append(C[j, j])
+        C[j + 1:, :] -= np.outer(C[j + 1:, j] / C[j, j], C[j, :])
+    return np.array(piv)
+
+
+def _c11(W, M, lr):
+    V = co.project_tangent(W, M)
+    return np.eye(W.shape[1]) + (lr / 2.0) * (W.T @ V)
+
+
+@pytest.mark.parametrize("lr", [0.05, 1.0, 10.0])
+def test_leading_block_needs_no_pivoting_on_the_manifold(lr):
+    rng = np.random.default_rng(21)
+    for n, k in [(300, 24), (64, 64), (1000, 128)]:
+        W = _stiefel(rng, n, k)
+        M = 3.0 * rng.standard_normal((n, k))
+        C11 = _c11(W, M, lr)
+        assert np.abs(0.5 * (C11 + C11.T) - np.eye(k)).max() < 1e-9      # symmetric part I
+        assert np.abs(_unpivoted_pivots(C11)).min() >= 1.0 - 1e-9
+
+
+def test_leading_block_off_the_manifold_can_need_pivoting():
+    # the input of the GPU test that exercises the pivoting fallback
+    import workloads as wk
+    h = wk.cayley_host_matrix(300, 24, seed=7, momentum_std=1.0)
+    W = 2.0 * h["W"].astype(np.float64)
+    M = 0.9 * h["M"].astype(np.float64) + 0.1 * co.center_columns(h["G"])
+    assert np.abs(_unpivoted_pivots(_c11(W, M, 1.0))).min() < 0.5

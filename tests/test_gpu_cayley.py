@@ -110,3 +110,15 @@ def test_cayley_benchmark_set(gpu_lib):
         _check(hosts[i], Ws[i], Ms[i], 1e-3, 0.9)
     for w in Ws:
         assert orc.orthogonality_error(w) <= 3e-5
+
+
+def test_cayley_off_manifold_falls_back_to_pivoting(gpu_lib):
+    # W = 2 x orthonormal: C11 = I + c W^T V has an unpivoted pivot below 1/2 (pinned on the
+    # CPU), so the GPU's unpivoted inverse hands over to the pivoting one
+    h = wk.cayley_host_matrix(300, 24, seed=7, momentum_std=1.0)
+    h = dict(h, W=(2.0 * h["W"]).astype(np.float32))
+    _say("off the manifold")
+    Ws, Ms = _run(gpu_lib, [h], 1.0, 0.9)
+    ref = orc.cayley_step(h["W"], h["G"], h["M"], lr=1.0, beta=0.9)
+    assert _rel(Ws[0], ref["W"]) <= 1e-5, _rel(Ws[0], ref["W"])
+    assert _rel(Ms[0], ref["M"]) <= 1e-5

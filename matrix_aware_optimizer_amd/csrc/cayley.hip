@@ -14,8 +14,10 @@
 //            (= sym(W^T M') by linearity, so M' needs no extra pass);
 //   p2       M' (in place) and V = M' - W S;
 //   reduce3  W^T W, W^T V, V^T V;
-//   solve    one workgroup per matrix: C and its right-hand side in fp64, LU with
-//            partial pivoting, Y = B W + Z;
+//   solve    in fp64, Y = B W + Z.  For K <= 128 by K x K blocks in phases: the
+//            products on many workgroups, C11 (unpivoted) and the Schur complement S
+//            (partial pivoting) inverted in registers by one workgroup per matrix.
+//            For larger K one workgroup per matrix LU-factors C with partial pivoting;
 //   p4       W' = W - c (V Y1 + W Y2) into the workspace, copied out by `out`.
 // Wide matrices (rows < cols) are transposed into frame copies first and back at
 // the end.  Reductions over rows are split into row blocks summed in a fixed

@@ -20,7 +20,9 @@
 // (global_load_lds_dwordx4, no VGPR staging) into a ring of five slabs (one
 // slab = one operand's k-step); the loads of the next Q slab and of the P slab
 // after it are spread between the current k-step's MFMA groups, and MFMA
-// fragments are double-buffered in registers.
+// fragments are double-buffered in registers.  For k-contiguous Q the loop is
+// rotated: the barrier that opens a k-step sits before the previous step's last
+// k-slice, whose MFMAs then cover the new step's first fragment reads.
 //
 // LDS layouts.  k-contiguous rows: 16-byte chunks XOR-swizzled with bits 1..3
 // of the row, so 32-row ds_read_b128 fragment reads are free of bank
@@ -36,8 +38,9 @@
 // (DPP) turns a lane's 4 rows x 1 column of a 32 x 32 block into 1 row x 4
 // columns (16-byte fp32 accesses); for bf16 a swap between lanes c and c ^ 4
 // then gives each lane 8 columns (16 bytes).  The mirrored half of a symmetric
-// output is stored from the untransposed layout.  The bf16 update stages its
-// output through LDS and stores whole tile rows.  Buffers are zero-padded to
+// output is stored from the untransposed layout.  The bf16 update adds a lo
+// after its k-loop from the tile's lo rows loaded into the idle ring, then
+// stages its output through LDS and stores whole tile rows.  Buffers are zero-padded to
 // the block tile, so there are no edge masks, and k-loops run over the real
 // extent rounded up to a k-step.
 //

@@ -15,8 +15,9 @@
 //   p2       M' (in place) and V = M' - W S;
 //   reduce3  W^T W, W^T V, V^T V;
 //   solve    in fp64, Y = B W + Z.  For K <= 128 by K x K blocks in phases: the
-//            products on many workgroups, C11 (unpivoted) and the Schur complement S
-//            (partial pivoting) inverted in registers by one workgroup per matrix.
+//            products on many workgroups, C11 and the Schur complement S inverted
+//            in registers by one workgroup per matrix, without pivoting unless a
+//            pivot is small.
 //            For larger K one workgroup per matrix LU-factors C with partial pivoting;
 //   p4       W' = W - c (V Y1 + W Y2) into the workspace, copied out by `out`.
 // Wide matrices (rows < cols) are transposed into frame copies first and back at
@@ -515,8 +516,8 @@ __device__ void solve_global(const CayleyDesc& d, double cc, double* arena) {
 // and B W = [WW; -VW].  Eliminating z1:
 //   X = C11^-1 C12,  y = C11^-1 r1,  S = C22 - C21 X,  r' = r2 - C21 y,
 //   z2 = S^-1 r',  z1 = y - X z2.
-// C11 and S are inverted by Gauss-Jordan with partial pivoting in LDS (a K x K
-// fp64 matrix fits); the products are K x K GEMMs through LDS tiles.  Every
+// C11 and S are inverted by Gauss-Jordan in registers, without pivoting unless a
+// pivot is small; the products are K x K GEMMs through LDS tiles.  Every
 // block is nonsingular: det C = det(I + c A) != 0 for skew A, C11 = I + c WV
 // with WV skew up to rounding, and det C = det C11 det S.
 // ---------------------------------------------------------------------------
@@ -625,13 +626,18 @@ __device__ __attribute__((always_inline)) void kk_gj_inverse(int K, double* out,
     __syncthreads();   // out is complete (global) before the next product reads it
 }
 
-// out = (I + scale * src)^-1 by Gauss-Jordan without pivoting, for C11 = I + c W^T V:
-// W^T V = skew(W^T M') on the manifold, so C11's symmetric part is I and every pivot has
-// real part >= 1.  Same register layout as kk_gj_inverse; per step only the scaled pivot
-// row goes through LDS, with one barrier.  Returns false, with out untouched, if a pivot
-// falls below 1/2 in magnitude (W far off the manifold); the caller then pivots.
+// out = ((identity ? I : 0) + scale * src)^-1 by Gauss-Jordan without pivoting, for
+// matrices whose symmetric part is positive definite: every pivot is then at least its
+// smallest eigenvalue.  C11 = I + c W^T V: W^T V = skew(W^T M') on the manifold, so
+// C11's symmetric part is I and every pivot is >= 1.  S, the Schur complement of C11:
+// x^T S x = z^T C z for z = [-C11^-1 C12 x; x], so S's symmetric part is at least C's,
+// I + (c / 2) [0, I - V^T V; I - V^T V, 0] on the manifold, whose smallest eigenvalue
+// is 1 - (c / 2) max |1 - sigma(V)^2|.  Same register layout as kk_gj_inverse; per step
+// only the scaled pivot row goes through LDS, with one barrier.  Returns false, with
+// out untouched, if a pivot falls below 1/2 in magnitude; the caller then pivots.
+// out may be src.
 __device__ __attribute__((always_inline)) bool kk_gj_inverse_unpivoted(int K, double* out, const double* src, double scale,
-                                                                     double* lds) {
+                                                                     bool identity, double* lds) {
     static_assert(CY_SOLVE_THREADS == 8 * CY_LDS_K, "eight threads per row of the 128 x 128 matrix");
     constexpr int CB = 16, PSTRIDE = CB + 1, PBUF = 8 * PSTRIDE;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -642,7 +648,7 @@ __device__ __attribute__((always_inline)) bool kk_gj_inverse_unpivoted(int K, do
     for (int k = 0; k < CB; ++k) {
         const int col = CB * cb + k;
         if (i < K && col < K)
-            m[k] = (i == col ? 1.0 : 0.0) + scale * src[static_cast<size_t>(i) * K + col];
+            m[k] = (identity && i == col ? 1.0 : 0.0) + scale * src[static_cast<size_t>(i) * K + col];
         else
             m[k] = i == col ? 1.0 : 0.0;
     }
@@ -695,7 +701,8 @@ __device__ __attribute__((always_inline)) bool kk_gj_inverse_unpivoted(int K, do
 //            a pivot is small);
 //   SV_G1    X = c C11^-1 WW,  y = C11^-1 r1 (into WV's block);
 //   SV_G2    S = I + c bwb + c VV X (into r1's block),  r' = r2 + c VV y (into C11^-1's);
-//   SV_INV2  S^-1 in place (one workgroup per matrix);
+//   SV_INV2  S^-1 in place (one workgroup per matrix; unpivoted, pivoting if a pivot
+//            is small);
 //   SV_G3    z2 = S^-1 r' (into VV's block);
 //   SV_G4    z1 = y - X z2, and Y = B W + Z in fp32 for the final pass.
 // The products run as 64 x 64 tiles on many workgroups, each element summed in
@@ -893,7 +900,7 @@ __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
     if (d.K <= CY_LDS_K) {
         const SvBlocks bk(d);
-        if (!kk_gj_inverse_unpivoted(d.K, bk.C11i, bk.WV, a.c, arena))
+        if (!kk_gj_inverse_unpivoted(d.K, bk.C11i, bk.WV, a.c, true, arena))
             kk_gj_inverse(d.K, bk.C11i, bk.WV, a.c, true, arena);
     } else {
         solve_global(d, a.c, arena);
@@ -904,7 +911,8 @@ __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_sv_inv2(CayleyArgs a) {
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
     const SvBlocks bk(d);
-    kk_gj_inverse(d.K, bk.R1, bk.R1, 1.0, false, arena);
+    if (!kk_gj_inverse_unpivoted(d.K, bk.R1, bk.R1, 1.0, false, arena))
+        kk_gj_inverse(d.K, bk.R1, bk.R1, 1.0, false, arena);
 }
 
 }  // namespace

@@ -13,6 +13,10 @@
   manifold W^T V is skew, so C11's symmetric part is I and elimination without
   pivoting meets pivots of magnitude >= 1; off it (W = 2 Q) a pivot can fall
   below 1/2.  The GPU path inverts C11 unpivoted and pivots when that happens.
+* The Schur complement S = C22 - C21 C11^-1 C12 of the same system: its symmetric
+  part is at least C's, whose smallest eigenvalue on the manifold is
+  1 - (c / 2) max |1 - sigma(V)^2|; on the benchmark's inputs that bound is near 1,
+  so S too is inverted without pivoting, and W = 2 Q drives its fallback as well.
 * Planted mistakes are each caught.
 """
 import numpy as np
@@ -189,3 +193,45 @@ def test_leading_block_off_the_manifold_can_need_pivoting():
     W = 2.0 * h["W"].astype(np.float64)
     M = 0.9 * h["M"].astype(np.float64) + 0.1 * co.center_columns(h["G"])
     assert np.abs(_unpivoted_pivots(_c11(W, M, 1.0))).min() < 0.5
+
+
+def _schur(W, V, lr):
+    # the 2k system C = I + c B U with B = [W^T; -V^T], U = [V, W], built whole
+    c, k = lr / 2.0, W.shape[1]
+    C = np.eye(2 * k) + c * np.vstack([W.T, -V.T]) @ np.hstack([V, W])
+    return C[k:, k:] - C[k:, :k] @ np.linalg.solve(C[:k, :k], C[:k, k:]), C
+
+
+@pytest.mark.parametrize("lr,std", [(1e-3, 1e-2), (0.05, 1e-2), (0.05, 1.0), (1.0, 0.1)])
+def test_schur_complement_pivots_are_bounded_on_the_manifold(lr, std):
+    rng = np.random.default_rng(22)
+    for n, k in [(300, 24), (1000, 100), (4096, 128)]:
+        W = _stiefel(rng, n, k)
+        V = co.project_tangent(W, std * rng.standard_normal((n, k)))
+        S, C = _schur(W, V, lr)
+        # C's symmetric part: I + (c / 2) [0, I - V^T V; I - V^T V, 0]
+        mu = 1.0 - (lr / 4.0) * np.abs(np.linalg.eigvalsh(np.eye(k) - V.T @ V)).max()
+        assert np.linalg.eigvalsh(0.5 * (C + C.T)).min() >= mu - 1e-9
+        assert np.linalg.eigvalsh(0.5 * (S + S.T)).min() >= mu - 1e-9
+        assert _unpivoted_pivots(S).min() >= mu - 1e-9
+
+
+def test_schur_complement_needs_no_pivoting_on_the_benchmark_inputs():
+    import workloads as wk
+    for seed in range(3):
+        h = wk.cayley_host_matrix(4096, 128, seed=seed)
+        W = h["W"].astype(np.float64)
+        M = 0.9 * h["M"].astype(np.float64) + 0.1 * co.center_columns(h["G"].astype(np.float64))
+        V = co.project_tangent(W, M)
+        for lr in (1e-3, 0.05, 1.0):
+            mu = 1.0 - (lr / 4.0) * np.abs(np.linalg.eigvalsh(np.eye(128) - V.T @ V)).max()
+            assert mu >= 0.5
+            assert np.abs(_unpivoted_pivots(_schur(W, V, lr)[0])).min() >= 0.5
+
+
+def test_schur_complement_off_the_manifold_can_need_pivoting():
+    import workloads as wk
+    h = wk.cayley_host_matrix(300, 24, seed=7, momentum_std=1.0)
+    W = 2.0 * h["W"].astype(np.float64)
+    M = 0.9 * h["M"].astype(np.float64) + 0.1 * co.center_columns(h["G"])
+    assert np.abs(_unpivoted_pivots(_schur(W, co.project_tangent(W, M), 1.0)[0])).min() < 0.5

@@ -62,13 +62,61 @@ __global__ __launch_bounds__(CY_THREADS) void cy_transpose_in(CayleyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// The products use 128 x 128 output tiles, 256 threads with 8 x 8 outputs each:
-// rows 4 ty + u and 64 + 4 ty + u, columns 4 tx + v and 64 + 4 tx + v of the tile
-// (ty = t / 16, tx = t % 16, u, v < 4).  A staged 16-row chunk is read as float4,
-// contiguous across the lanes that share a row, and the next chunk is loaded into
-// registers while the current one is multiplied.  Sums run in ascending k.
+// The N x K and K x K fp32 products run on the matrix cores (v_mfma_f32_32x32x2_f32).
+// A workgroup forms one 128 x 128 output tile; its 4 waves split it 2 x 2, and each
+// wave holds 2 x 2 blocks of 32 x 32 accumulators.  Operands are staged as 16-row
+// k-chunks, both k-major: a[k][i] and b[k][j] (row stride MS floats, so that the two
+// lane halves, which read rows k and k + 1, fall in opposite halves of the LDS banks).
+// The next chunk is loaded into registers while the current one is multiplied.
+// Accumulator register r of block (bi, bj) holds row 64 wm + 32 bi + 8 (r / 4) +
+// 4 h + r % 4 and column 64 wn + 32 bj + c of the tile (wave = 2 wm + wn, lane =
+// 32 h + c).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int gt_off(int h) { return h < 4 ? h : 60 + h; }   // 4 x + gt_off(h): h-th of the 8
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+constexpr int MK = 16;             // k rows per staged chunk
+constexpr int MS = CY_GT + 36;     // LDS row stride in floats (640 B: rows k, k + 1 in opposite bank halves)
+static_assert(CY_THREADS == 256 && CY_GT == 128, "4 waves, 2 x 2 of 64 x 64");
+
+struct MfmaAcc {
+    f32x16_t v[2][2];
+    __device__ void zero() {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) v[bi][bj][r] = 0.0f;
+    }
+    // acc += a^T b over one staged chunk (a: MK x CY_GT, b: MK x CY_GT, pitch MS)
+    __device__ void chunk(const float* as, const float* bs) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int c = lane & 31, h = lane >> 5;
+        const float* pa = as + h * MS + 64 * (wave >> 1) + c;
+        const float* pb = bs + h * MS + 64 * (wave & 1) + c;
+#pragma unroll
+        for (int k = 0; k < MK; k += 2) {
+            const float a0 = pa[k * MS], a1 = pa[k * MS + 32], b0 = pb[k * MS], b1 = pb[k * MS + 32];
+            v[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, v[0][0], 0, 0, 0);
+            v[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, v[0][1], 0, 0, 0);
+            v[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, v[1][0], 0, 0, 0);
+            v[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, v[1][1], 0, 0, 0);
+        }
+    }
+    // f(row, col, value) for every accumulator, row and col relative to the tile
+    template <typename F>
+    __device__ void each(F f) const {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int c = lane & 31, h = lane >> 5;
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    f(64 * (wave >> 1) + 32 * bi + 8 * (r >> 2) + 4 * h + (r & 3), 64 * (wave & 1) + 32 * bj + c,
+                      v[bi][bj][r]);
+    }
+};
 
 // X[row][col .. col + 3] (row-major, pitch ld floats), zero outside rows < nrow and cols < ncol.
 __device__ __forceinline__ float4 ld4_guard(const float* base, size_t ld, int row, int nrow, int col, int ncol, bool vec) {
@@ -83,20 +131,18 @@ __device__ __forceinline__ float4 ld4_guard(const float* base, size_t ld, int ro
     return v;
 }
 __device__ __forceinline__ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+__device__ __forceinline__ void st4_lds(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 
 // K x K partial product over rows [rs, re): out[i][j] = sum_r X[r][i] Y[r][j] for the
-// tile at (i0, j0).
+// tile at (i0, j0).  Both operands are k-major as stored (row r of X and Y).
 __device__ void tn_block(const float* X, const float* Y, int K, int rs, int re, int i0, int j0, float* out) {
-    constexpr int RC = 16, C4 = CY_GT / 4, NQ = RC * C4 / CY_THREADS;
-    static_assert(NQ * CY_THREADS == RC * C4, "whole chunks per thread");
-    __shared__ float4 xs[RC][C4], ys[RC][C4];
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    constexpr int C4 = CY_GT / 4, NQ = MK * C4 / CY_THREADS;
+    static_assert(NQ * CY_THREADS == MK * C4, "whole chunks per thread");
+    __shared__ __attribute__((aligned(16))) float xs[MK * MS], ys[MK * MS];
+    const int tid = threadIdx.x;
     const bool vec = (K & 3) == 0 && aligned16(X) && aligned16(Y);
-    float acc[8][8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) acc[u][v] = 0.0f;
+    MfmaAcc acc;
+    acc.zero();
     float4 xn[NQ], yn[NQ];
     auto fetch = [&](int r) {
 #pragma unroll
@@ -107,34 +153,22 @@ __device__ void tn_block(const float* X, const float* Y, int K, int rs, int re, 
         }
     };
     fetch(rs);
-    for (int r = rs; r < re; r += RC) {
+    for (int r = rs; r < re; r += MK) {
 #pragma unroll
         for (int e = 0; e < NQ; ++e) {
             const int q = tid + e * CY_THREADS;
-            xs[q / C4][q % C4] = xn[e];
-            ys[q / C4][q % C4] = yn[e];
+            st4_lds(xs + (q / C4) * MS + 4 * (q % C4), xn[e]);
+            st4_lds(ys + (q / C4) * MS + 4 * (q % C4), yn[e]);
         }
         lds_barrier();
-        if (r + RC < re) fetch(r + RC);
-#pragma unroll 2
-        for (int rr = 0; rr < RC; ++rr) {
-            const float4 a0 = xs[rr][ty], a1 = xs[rr][16 + ty], b0 = ys[rr][tx], b1 = ys[rr][16 + tx];
-            const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-            const float yb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int v = 0; v < 8; ++v) acc[u][v] = fmaf(xa[u], yb[v], acc[u][v]);
-        }
+        if (r + MK < re) fetch(r + MK);
+        acc.chunk(xs, ys);
         lds_barrier();   // the chunk is read before the next one is stored
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int i = i0 + 4 * ty + gt_off(u), j = j0 + 4 * tx + gt_off(v);
-            if (i < K && j < K) G(out)[static_cast<size_t>(i) * K + j] = acc[u][v];
-        }
+    acc.each([&](int ti, int tj, float x) {
+        const int i = i0 + ti, j = j0 + tj;
+        if (i < K && j < K) G(out)[static_cast<size_t>(i) * K + j] = x;
+    });
 }
 
 // One K x K product tile of one row block per workgroup.  REDUCE1: W^T G and W^T M;
@@ -231,14 +265,13 @@ __global__ __launch_bounds__(CY_THREADS) void cy_mid(CayleyArgs a) {
 }
 
 // acc += A[r0.., 0:Kr] B[0:Kr, c0..] for a 128 x 128 output tile (A row-major N x lda,
-// B row-major K wide), in the 8 x 8 per-thread layout of the products above.
+// B row-major K wide); A's chunk is staged transposed, as[k][row].
 __device__ void nn_accumulate(const float* A, int lda, int N, const float* B, int K, int Kr, int r0, int c0,
-                              float (&acc)[8][8]) {
-    constexpr int KC = 16, C4 = CY_GT / 4, NQ = KC * C4 / CY_THREADS;
-    static_assert(NQ * CY_THREADS == KC * C4, "whole chunks per thread");
-    __shared__ float as[KC][CY_GT + 4];   // the A chunk transposed, as[k][row]; the pad spreads the stores
-    __shared__ float4 bs[KC][C4];
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+                              MfmaAcc& acc) {
+    constexpr int C4 = CY_GT / 4, NQ = MK * C4 / CY_THREADS;
+    static_assert(NQ * CY_THREADS == MK * C4, "whole chunks per thread");
+    __shared__ __attribute__((aligned(16))) float as[MK * MS], bs[MK * MS];
+    const int tid = threadIdx.x;
     const bool avec = (lda & 3) == 0 && aligned16(A), bvec = (K & 3) == 0 && aligned16(B);
     float4 an[NQ], bn[NQ];
     auto fetch = [&](int k0) {
@@ -251,79 +284,62 @@ __device__ void nn_accumulate(const float* A, int lda, int N, const float* B, in
         }
     };
     fetch(0);
-    for (int k0 = 0; k0 < Kr; k0 += KC) {
+    for (int k0 = 0; k0 < Kr; k0 += MK) {
 #pragma unroll
         for (int e = 0; e < NQ; ++e) {
             const int q = tid + e * CY_THREADS, row = q / 4, k4 = q % 4;
-            as[4 * k4 + 0][row] = an[e].x;
-            as[4 * k4 + 1][row] = an[e].y;
-            as[4 * k4 + 2][row] = an[e].z;
-            as[4 * k4 + 3][row] = an[e].w;
-            bs[q / C4][q % C4] = bn[e];
+            as[(4 * k4 + 0) * MS + row] = an[e].x;
+            as[(4 * k4 + 1) * MS + row] = an[e].y;
+            as[(4 * k4 + 2) * MS + row] = an[e].z;
+            as[(4 * k4 + 3) * MS + row] = an[e].w;
+            st4_lds(bs + (q / C4) * MS + 4 * (q % C4), bn[e]);
         }
         lds_barrier();
-        if (k0 + KC < Kr) fetch(k0 + KC);
-#pragma unroll 2
-        for (int kc = 0; kc < KC; ++kc) {
-            const float4 a0 = *reinterpret_cast<const float4*>(&as[kc][4 * ty]);
-            const float4 a1 = *reinterpret_cast<const float4*>(&as[kc][64 + 4 * ty]);
-            const float4 b0 = bs[kc][tx], b1 = bs[kc][16 + tx];
-            const float xa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-            const float yb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int v = 0; v < 8; ++v) acc[u][v] = fmaf(xa[u], yb[v], acc[u][v]);
-        }
+        if (k0 + MK < Kr) fetch(k0 + MK);
+        acc.chunk(as, bs);
         lds_barrier();   // the chunk is read before the next one is stored
     }
 }
 
 // M' = beta M + (1 - beta)(G - mean), in place; V = M' - W S
-__global__ __launch_bounds__(CY_THREADS) void cy_p2(CayleyArgs a) {
+__global__ __launch_bounds__(CY_THREADS, 4) void cy_p2(CayleyArgs a) {
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
     const int r0 = (local / d.gk) * CY_GT, c0 = (local % d.gk) * CY_GT;
-    float acc[8][8] = {};
+    MfmaAcc acc;
+    acc.zero();
     const float* S = d.small + d.K;
     nn_accumulate(d.wf, d.K, d.N, S, d.K, d.K, r0, c0, acc);
-    const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
     const float beta = a.beta, omb = 1.0f - a.beta;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int r = r0 + 4 * ty + gt_off(u), j = c0 + 4 * tx + gt_off(v);
-            if (r < d.N && j < d.K) {
-                const size_t idx = static_cast<size_t>(r) * d.K + j;
-                const float mn = fmaf(beta, G(d.mf)[idx], omb * (G(d.gf)[idx] - G(d.small)[j]));
-                G(d.mf)[idx] = mn;
-                G(d.v)[idx] = mn - acc[u][v];
-            }
+    acc.each([&](int tr, int tc, float x) {
+        const int r = r0 + tr, j = c0 + tc;
+        if (r < d.N && j < d.K) {
+            const size_t idx = static_cast<size_t>(r) * d.K + j;
+            const float mn = fmaf(beta, G(d.mf)[idx], omb * (G(d.gf)[idx] - G(d.small)[j]));
+            G(d.mf)[idx] = mn;
+            G(d.v)[idx] = mn - x;
         }
+    });
 }
 
 // W' = W - c (V Y1 + W Y2), into the workspace
-__global__ __launch_bounds__(CY_THREADS) void cy_p4(CayleyArgs a) {
+__global__ __launch_bounds__(CY_THREADS, 4) void cy_p4(CayleyArgs a) {
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
     const int r0 = (local / d.gk) * CY_GT, c0 = (local % d.gk) * CY_GT;
     const size_t kk = static_cast<size_t>(d.K) * d.K;
     const float* Y = d.small + d.K + kk;
-    float acc[8][8] = {};
+    MfmaAcc acc;
+    acc.zero();
     nn_accumulate(d.v, d.K, d.N, Y, d.K, d.K, r0, c0, acc);
     nn_accumulate(d.wf, d.K, d.N, Y + kk, d.K, d.K, r0, c0, acc);
-    const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int r = r0 + 4 * ty + gt_off(u), j = c0 + 4 * tx + gt_off(v);
-            if (r < d.N && j < d.K) {
-                const size_t idx = static_cast<size_t>(r) * d.K + j;
-                G(d.wnew)[idx] = fmaf(-a.c, acc[u][v], G(d.wf)[idx]);
-            }
+    acc.each([&](int tr, int tc, float x) {
+        const int r = r0 + tr, j = c0 + tc;
+        if (r < d.N && j < d.K) {
+            const size_t idx = static_cast<size_t>(r) * d.K + j;
+            G(d.wnew)[idx] = fmaf(-a.c, x, G(d.wf)[idx]);
         }
+    });
 }
 
 // caller's W (and, for wide matrices, M) from the frame

@@ -135,7 +135,7 @@ __device__ __forceinline__ void st4_lds(float* p, float4 v) { *reinterpret_cast<
 
 // K x K partial product over rows [rs, re): out[i][j] = sum_r X[r][i] Y[r][j] for the
 // tile at (i0, j0).  Both operands are k-major as stored (row r of X and Y).
-__device__ void tn_block(const float* X, const float* Y, int K, int rs, int re, int i0, int j0, float* out) {
+__device__ __attribute__((always_inline)) void tn_block(const float* X, const float* Y, int K, int rs, int re, int i0, int j0, float* out) {
     constexpr int C4 = CY_GT / 4, NQ = MK * C4 / CY_THREADS;
     static_assert(NQ * CY_THREADS == MK * C4, "whole chunks per thread");
     __shared__ __attribute__((aligned(16))) float xs[MK * MS], ys[MK * MS];

@@ -19,7 +19,8 @@
 //            in registers by one workgroup per matrix, without pivoting unless a
 //            pivot is small.
 //            For larger K one workgroup per matrix LU-factors C with partial pivoting;
-//   p4       W' = W - c (V Y1 + W Y2) into the workspace, copied out by `out`.
+//   p4       W' = W - c (V Y1 + W Y2) into the workspace, copied out by `out` (in
+//            place for tall matrices with K <= 128, which need no copy).
 // Wide matrices (rows < cols) are transposed into frame copies first and back at
 // the end.  Reductions over rows are split into row blocks summed in a fixed
 // order, so results are deterministic.
@@ -322,7 +323,8 @@ __global__ __launch_bounds__(CY_THREADS, 4) void cy_p2(CayleyArgs a) {
     });
 }
 
-// W' = W - c (V Y1 + W Y2), into the workspace
+// W' = W - c (V Y1 + W Y2), into the workspace; in place for a tall matrix one tile
+// wide, where this workgroup's rows of W are read only here, before they are written
 __global__ __launch_bounds__(CY_THREADS, 4) void cy_p4(CayleyArgs a) {
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);

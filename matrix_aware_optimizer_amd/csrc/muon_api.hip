@@ -628,6 +628,10 @@ muon_status collect_cayley(const muon_cayley_matrix* mats, int32_t n, const muon
     return check_overlaps(iv);
 }
 
+// A tall matrix one product tile wide: p4 writes W' in place (each of its workgroups owns
+// whole rows of W, which no other workgroup reads), so there is nothing to copy out.
+bool cayley_w_in_place(const CayleyDesc& d) { return d.tall && d.gk == 1; }
+
 muon_status build_cayley_plan(std::vector<CayleyDesc>& descs, CayleyPlan& pl) {
     const size_t nmat = descs.size();
     size_t off = align_up(sizeof(CayleyDesc) * nmat, ALIGN);
@@ -660,7 +664,8 @@ muon_status build_cayley_plan(std::vector<CayleyDesc>& descs, CayleyPlan& pl) {
         per[CY_SV_G3] = sv;
         per[CY_SV_G4] = sv;
         per[CY_P4] = prod;
-        per[CY_OUT] = tiles;
+        const bool w_in_place = cayley_w_in_place(d);
+        per[CY_OUT] = w_in_place ? 0 : tiles;
         for (int ph = 0; ph < CY_PHASES; ++ph) {
             tot[ph] += per[ph];
             if (tot[ph] > INT32_MAX) return fail(MUON_ERR_UNSUPPORTED, "too many tiles in one call (split the list)");
@@ -678,7 +683,7 @@ muon_status build_cayley_plan(std::vector<CayleyDesc>& descs, CayleyPlan& pl) {
             d.mf = reinterpret_cast<float*>(take(nk));
         }
         d.v = reinterpret_cast<float*>(take(nk));
-        d.wnew = reinterpret_cast<float*>(take(nk));
+        d.wnew = w_in_place ? d.w : reinterpret_cast<float*>(take(nk));
         d.part = reinterpret_cast<float*>(take(static_cast<size_t>(d.nrb) * 3 * kk * 4));
         d.colpart = reinterpret_cast<float*>(take(static_cast<size_t>(d.nrb) * 2 * d.K * 4));
         d.small = reinterpret_cast<float*>(take((d.K + kk + 2 * kk) * 4));
@@ -703,7 +708,7 @@ void rebase_cayley(CayleyPlan& pl, char* base) {
             fix(d.mf);
         }
         fix(d.v);
-        fix(d.wnew);
+        if (!cayley_w_in_place(d)) fix(d.wnew);
         fix(d.part);
         fix(d.colpart);
         fix(d.small);

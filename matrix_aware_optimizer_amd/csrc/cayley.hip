@@ -227,41 +227,68 @@ __global__ __launch_bounds__(CY_THREADS) void cy_colsum(CayleyArgs a) {
     }
 }
 
-// mean(G) and S = sym(beta W^T M + (1 - beta)(W^T G - colsum(W) mean^T)); CY_MID_SPLIT
-// blocks per matrix, each taking a slice of S (and recomputing the K column sums)
+// K x K sums by CY_MT x CY_MT tile pairs: a workgroup sums the row-block partials of
+// its tile (i0, j0) and of the mirror tile (j0, i0), both read as coalesced rows, and
+// gets the transposed entries it needs from the mirror through LDS.  Thread t holds
+// entries (r, c) = (q / CY_MT, q % CY_MT), q = t + e CY_THREADS.
+constexpr int MID_E = CY_MT * CY_MT / CY_THREADS;
+static_assert(MID_E * CY_THREADS == CY_MT * CY_MT, "whole tiles");
+
+// mean(G) and S = sym(H), H = beta W^T M + (1 - beta)(W^T G - colsum(W) mean^T), which
+// equals sym(W^T M') by linearity
 __global__ __launch_bounds__(CY_THREADS) void cy_mid(CayleyArgs a) {
-    __shared__ float mean_s[CAYLEY_MAX_K], colw_s[CAYLEY_MAX_K];
-    int slice;
-    const CayleyDesc& d = cy_locate(a, blockIdx.x, slice);
-    const int K = d.K;
+    __shared__ float hm[CY_MT][CY_MT + 1];
+    __shared__ float mean_s[2][CY_MT], colw_s[2][CY_MT];   // [0]: the tile's rows i, [1]: its columns j
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const int K = d.K, mt = (K + CY_MT - 1) / CY_MT;
+    const int i0 = (local / mt) * CY_MT, j0 = (local % mt) * CY_MT;
     const size_t kk = static_cast<size_t>(K) * K;
-    const size_t q0 = kk * slice / CY_MID_SPLIT, q1 = kk * (slice + 1) / CY_MID_SPLIT;
-    for (int j = threadIdx.x; j < K; j += CY_THREADS) {
+    for (int e = threadIdx.x; e < 2 * CY_MT; e += CY_THREADS) {
+        const int side = e / CY_MT, col = (side ? j0 : i0) + e % CY_MT;
         float sg = 0.0f, sw = 0.0f;
-        for (int rb = 0; rb < d.nrb; ++rb) {
-            sg += G(d.colpart)[(static_cast<size_t>(rb) * 2 + 0) * K + j];
-            sw += G(d.colpart)[(static_cast<size_t>(rb) * 2 + 1) * K + j];
+        if (col < K) {
+            for (int rb = 0; rb < d.nrb; ++rb) {
+                sg += G(d.colpart)[(static_cast<size_t>(rb) * 2 + 0) * K + col];
+                sw += G(d.colpart)[(static_cast<size_t>(rb) * 2 + 1) * K + col];
+            }
         }
         const float mean = sg / static_cast<float>(d.N);
-        mean_s[j] = mean;
-        colw_s[j] = sw;
-        if (slice == 0) G(d.small)[j] = mean;
+        mean_s[side][e % CY_MT] = mean;
+        colw_s[side][e % CY_MT] = sw;
+        if (side == 1 && i0 == 0 && col < K) G(d.small)[col] = mean;
     }
     __syncthreads();
     const float beta = a.beta, omb = 1.0f - a.beta;
-    for (size_t q = q0 + threadIdx.x; q < q1; q += CY_THREADS) {
-        const int i = static_cast<int>(q / K), j = static_cast<int>(q % K);
-        float gij = 0.0f, mij = 0.0f, gji = 0.0f, mji = 0.0f;
+    float hd[MID_E];
+#pragma unroll
+    for (int e = 0; e < MID_E; ++e) {
+        const int q = threadIdx.x + e * CY_THREADS, r = q / CY_MT, c = q % CY_MT;
+        const int i = i0 + r, j = j0 + c;     // direct entry H[i][j]
+        const int im = j0 + r, jm = i0 + c;   // mirror entry H[im][jm]
+        const bool dok = i < K && j < K, mok = im < K && jm < K;
+        float g = 0.0f, m = 0.0f, gm = 0.0f, mm = 0.0f;
+#pragma unroll 4
         for (int rb = 0; rb < d.nrb; ++rb) {
             const float* pr = d.part + static_cast<size_t>(rb) * 3 * kk;
-            gij += G(pr)[static_cast<size_t>(i) * K + j];
-            mij += G(pr)[kk + static_cast<size_t>(i) * K + j];
-            gji += G(pr)[static_cast<size_t>(j) * K + i];
-            mji += G(pr)[kk + static_cast<size_t>(j) * K + i];
+            if (dok) {
+                g += G(pr)[static_cast<size_t>(i) * K + j];
+                m += G(pr)[kk + static_cast<size_t>(i) * K + j];
+            }
+            if (mok) {
+                gm += G(pr)[static_cast<size_t>(im) * K + jm];
+                mm += G(pr)[kk + static_cast<size_t>(im) * K + jm];
+            }
         }
-        const float hij = fmaf(beta, mij, omb * (gij - colw_s[i] * mean_s[j]));
-        const float hji = fmaf(beta, mji, omb * (gji - colw_s[j] * mean_s[i]));
-        G(d.small)[K + q] = 0.5f * (hij + hji);
+        hd[e] = fmaf(beta, m, omb * (g - colw_s[0][r] * mean_s[1][c]));
+        hm[r][c] = fmaf(beta, mm, omb * (gm - colw_s[1][r] * mean_s[0][c]));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < MID_E; ++e) {
+        const int q = threadIdx.x + e * CY_THREADS, r = q / CY_MT, c = q % CY_MT;
+        const int i = i0 + r, j = j0 + c;
+        if (i < K && j < K) G(d.small)[K + static_cast<size_t>(i) * K + j] = 0.5f * (hd[e] + hm[c][r]);   // H[j][i]
     }
 }
 
@@ -809,45 +836,46 @@ __device__ void sv_gemm(int K, double* out, const double* A, const double* B, do
         }
 }
 
-// SV_SUM: the K x K blocks of one 64 x 64 tile from the partials (fp64 sums in row-block order)
+// SV_SUM: the K x K blocks from the partials (fp64 sums in row-block order), by CY_MT tile
+// pairs as in the middle step; bwb = -V^T W = -(W^T V)^T comes from the mirror tile
 __global__ __launch_bounds__(CY_THREADS) void cy_sv_sum(CayleyArgs a) {
+    __shared__ double tw[CY_MT][CY_MT + 1];
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
     const SvBlocks bk(d);
-    const int K = d.K, g = (K + SV_T - 1) / SV_T, ti = local / g, tj = local % g;
+    const int K = d.K, mt = (K + CY_MT - 1) / CY_MT;
+    const int i0 = (local / mt) * CY_MT, j0 = (local % mt) * CY_MT;
     const size_t kk = static_cast<size_t>(K) * K;
-    for (int e = threadIdx.x; e < SV_T * SV_T; e += CY_THREADS) {
-        const int i = ti * SV_T + e / SV_T, j = tj * SV_T + e % SV_T;
-        if (i >= K || j >= K) continue;
-        const size_t q = static_cast<size_t>(i) * K + j;
-        double ww = 0.0, wv = 0.0, vw = 0.0, vv = 0.0;   // (W^T W)ij, (W^T V)ij, (W^T V)ji, (V^T V)ij
-        constexpr int RB = 8;   // row blocks in ascending order, RB blocks' loads issued before their sums
-        for (int rb0 = 0; rb0 < d.nrb; rb0 += RB) {
-            float t[RB][4];
 #pragma unroll
-            for (int u = 0; u < RB; ++u) {
-                if (rb0 + u < d.nrb) {
-                    const float* pr = d.part + static_cast<size_t>(rb0 + u) * 3 * kk;
-                    t[u][0] = G(pr)[q];
-                    t[u][1] = G(pr)[kk + q];
-                    t[u][2] = G(pr)[kk + static_cast<size_t>(j) * K + i];
-                    t[u][3] = G(pr)[2 * kk + q];
-                }
+    for (int e = 0; e < MID_E; ++e) {
+        const int q = threadIdx.x + e * CY_THREADS, r = q / CY_MT, c = q % CY_MT;
+        const int i = i0 + r, j = j0 + c, im = j0 + r, jm = i0 + c;
+        const bool dok = i < K && j < K, mok = im < K && jm < K;
+        const size_t qd = static_cast<size_t>(i) * K + j, qm = static_cast<size_t>(im) * K + jm;
+        double ww = 0.0, wv = 0.0, vv = 0.0, wvm = 0.0;   // (W^T W)ij, (W^T V)ij, (V^T V)ij, (W^T V)[im][jm]
+#pragma unroll 4
+        for (int rb = 0; rb < d.nrb; ++rb) {
+            const float* pr = d.part + static_cast<size_t>(rb) * 3 * kk;
+            if (dok) {
+                ww += G(pr)[qd];
+                wv += G(pr)[kk + qd];
+                vv += G(pr)[2 * kk + qd];
             }
-#pragma unroll
-            for (int u = 0; u < RB; ++u) {
-                if (rb0 + u < d.nrb) {
-                    ww += t[u][0];
-                    wv += t[u][1];
-                    vw += t[u][2];
-                    vv += t[u][3];
-                }
-            }
+            if (mok) wvm += G(pr)[kk + qm];
         }
-        bk.WV[q] = wv;
-        bk.VV[q] = vv;
-        bk.WW[q] = ww;
-        bk.bwb[q] = -vw;
+        if (dok) {
+            bk.WV[qd] = wv;
+            bk.VV[qd] = vv;
+            bk.WW[qd] = ww;
+        }
+        tw[r][c] = wvm;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < MID_E; ++e) {
+        const int q = threadIdx.x + e * CY_THREADS, r = q / CY_MT, c = q % CY_MT;
+        const int i = i0 + r, j = j0 + c;
+        if (i < K && j < K) bk.bwb[static_cast<size_t>(i) * K + j] = -tw[c][r];   // -(W^T V)[j][i]
     }
 }
 

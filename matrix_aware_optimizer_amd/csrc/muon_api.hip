@@ -652,10 +652,11 @@ muon_status build_cayley_plan(std::vector<CayleyDesc>& descs, CayleyPlan& pl) {
         per[CY_TRANSPOSE_IN] = d.tall ? 0 : tiles;
         per[CY_REDUCE1] = 2 * red;
         per[CY_COLSUM] = d.nrb;
-        per[CY_MID] = CY_MID_SPLIT;
+        const int64_t mt = (d.K + CY_MT - 1) / CY_MT;                     // K x K sums in CY_MT tiles
+        per[CY_MID] = mt * mt;
         per[CY_P2] = prod;
         per[CY_REDUCE3] = 3 * red;
-        per[CY_SV_SUM] = sv;
+        per[CY_SV_SUM] = sv ? mt * mt : 0;
         per[CY_SV_R] = 2 * sv;
         per[CY_SOLVE] = 1;
         per[CY_SV_G1] = 2 * sv;

@@ -111,7 +111,7 @@ constexpr int CY_GT = 128;        // output tile edge of the N x K and K x K pro
 constexpr int CY_RB = 512;        // rows per reduction block
 constexpr int CY_THREADS = 256;
 constexpr int CY_SOLVE_THREADS = 1024;
-constexpr int CY_MID_SPLIT = 16;         // workgroups per matrix for the K x K middle step
+constexpr int CY_MT = 32;                // tile edge of the K x K sums (middle step, split-solve blocks)
 constexpr int CY_LDS_K = 128;            // K up to which the solve is split and inverts in registers
 constexpr int CY_SV_T = 64;              // tile edge of the split solve's K x K products
 struct CayleyDesc {

@@ -741,9 +741,9 @@ __device__ __attribute__((always_inline)) bool kk_gj_inverse_unpivoted(int K, do
 // Split solve for K <= CY_LDS_K.  The K x K fp64 blocks live in the workspace
 // (pitch K); each phase reads only blocks that earlier phases wrote:
 //   SV_SUM   WW, WV, VV and bwb = -VW from the row-block partials;
-//   SV_R     r1 = WW - c (WV WW) - c (WW bwb),  r2 = bwb - c (bwb bwb) + c (VV WW);
 //   SOLVE    C11^-1 = (I + c WV)^-1 (one workgroup per matrix; unpivoted, pivoting if
-//            a pivot is small);
+//            a pivot is small), and beside it, on more workgroups, the right-hand side
+//            r1 = WW - c (WV WW) - c (WW bwb),  r2 = bwb - c (bwb bwb) + c (VV WW);
 //   SV_G1    X = c C11^-1 WW,  y = C11^-1 r1 (into WV's block);
 //   SV_G2    S = I + c bwb + c VV X (into r1's block),  r' = r2 + c VV y (into C11^-1's);
 //   SV_INV2  S^-1 in place (one workgroup per matrix; unpivoted, pivoting if a pivot
@@ -764,14 +764,20 @@ struct SvBlocks {
 };
 __device__ __forceinline__ int sv_tiles(int K) { const int g = (K + SV_T - 1) / SV_T; return g * g; }
 
-// acc = A B for the 64 x 64 tile (ti, tj) of a K x K product (pitch K).  Thread t holds rows
-// 4 (t / 16) + u and columns t % 16 + 16 v (u, v < 4); the next 16-wide k-chunk is loaded
-// into registers while the current one is multiplied.
-__device__ void sv_product(int K, const double* A, const double* B, int ti, int tj, double (&acc)[4][4]) {
-    constexpr int KC = 16, NQ = SV_T * KC / CY_THREADS;
+// acc = A B for the 64 x 64 tile (ti, tj) of a K x K product (pitch K), by 256 threads
+// (tid < 256) with SV_LDS doubles of LDS at lds.  Thread t holds rows 4 (t / 16) + u and
+// columns t % 16 + 16 v (u, v < 4); the next 16-wide k-chunk is loaded into registers
+// while the current one is multiplied.  Its barriers are workgroup-wide: every 256-thread
+// group of the workgroup runs the same k-loop.
+constexpr int SV_KC = 16;
+constexpr int SV_LDS = SV_T * (SV_KC + 1) + SV_KC * (SV_T + 4);
+__device__ __attribute__((always_inline)) void sv_product(int K, const double* A, const double* B, int ti, int tj, double (&acc)[4][4], double* lds,
+                           int tid) {
+    constexpr int KC = SV_KC, NQ = SV_T * KC / CY_THREADS;
     static_assert(NQ * CY_THREADS == SV_T * KC, "whole chunks per thread");
-    __shared__ double As[SV_T][KC + 1], Bs[KC][SV_T + 4];
-    const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+    double* As = lds;                        // [SV_T][KC + 1]
+    double* Bs = lds + SV_T * (KC + 1);      // [KC][SV_T + 4]
+    const int ty = tid / 16, tx = tid % 16;
     const int r0 = ti * SV_T, c0 = tj * SV_T;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -793,8 +799,8 @@ __device__ void sv_product(int K, const double* A, const double* B, int ti, int 
 #pragma unroll
         for (int e = 0; e < NQ; ++e) {
             const int q = tid + e * CY_THREADS;
-            As[q / KC][q % KC] = an[e];
-            Bs[q / SV_T][q % SV_T] = bn[e];
+            As[(q / KC) * (KC + 1) + q % KC] = an[e];
+            Bs[(q / SV_T) * (SV_T + 4) + q % SV_T] = bn[e];
         }
         lds_barrier();
         if (l0 + KC < K) fetch(l0 + KC);
@@ -802,9 +808,9 @@ __device__ void sv_product(int K, const double* A, const double* B, int ti, int 
         for (int l = 0; l < KC; ++l) {
             double av[4], bv[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) av[u] = As[4 * ty + u][l];
+            for (int u = 0; u < 4; ++u) av[u] = As[(4 * ty + u) * (KC + 1) + l];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) bv[v] = Bs[l][tx + 16 * v];
+            for (int v = 0; v < 4; ++v) bv[v] = Bs[l * (SV_T + 4) + tx + 16 * v];
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -816,12 +822,15 @@ __device__ void sv_product(int K, const double* A, const double* B, int ti, int 
 
 // out = alpha A B + base_scale base (+ I): one tile, each element rounded as
 // alpha * acc, then + base_scale * base, then + 1 on the diagonal.
-__device__ void sv_gemm(int K, double* out, const double* A, const double* B, double alpha, const double* base,
-                        double base_scale, bool identity, int tile) {
+// Called by 256 threads (tid < 256) with SV_LDS doubles at lds; with store false the
+// product runs (for the workgroup's barriers) but nothing is read from base or stored.
+__device__ __attribute__((always_inline)) void sv_gemm(int K, double* out, const double* A, const double* B, double alpha, const double* base,
+                        double base_scale, bool identity, int tile, double* lds, int tid, bool store = true) {
     const int g = (K + SV_T - 1) / SV_T, ti = tile / g, tj = tile % g;
     double acc[4][4];
-    sv_product(K, A, B, ti, tj, acc);
-    const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+    sv_product(K, A, B, ti, tj, acc, lds, tid);
+    if (!store) return;
+    const int ty = tid / 16, tx = tid % 16;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -879,19 +888,25 @@ __global__ __launch_bounds__(CY_THREADS) void cy_sv_sum(CayleyArgs a) {
     }
 }
 
-// SV_R: right-hand side r = B W - c (B U)(B W), each block as two products in turn
-__global__ __launch_bounds__(CY_THREADS) void cy_sv_r(CayleyArgs a) {
-    int local;
-    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+// The right-hand side r = B W - c (B U)(B W), each block as two products in turn, by the
+// extra workgroups of the SOLVE launch (it needs only the block sums, so it runs beside
+// the C11 inversion): workgroup w takes tiles 4 w .. 4 w + 3 of the 2 x sv_tiles(K), one
+// per 256-thread quarter, each in its own part of the LDS arena.
+__device__ __attribute__((noinline)) void sv_rhs(const CayleyDesc& d, double c, int w, double* arena) {
+    static_assert(CY_SOLVE_THREADS == 4 * CY_THREADS, "four tile products per workgroup");
+    static_assert(4 * SV_LDS <= CY_LDS_K * CY_LDS_K + 3 * CY_LDS_K, "the quarters fit the arena");
     const SvBlocks bk(d);
-    const int nt = sv_tiles(d.K), tile = local % nt;
-    const double c = a.c;
-    if (local < nt) {   // r1 = WW - c WV WW - c WW bwb
-        sv_gemm(d.K, bk.R1, bk.WV, bk.WW, -c, bk.WW, 1.0, false, tile);
-        sv_gemm(d.K, bk.R1, bk.WW, bk.bwb, -c, bk.R1, 1.0, false, tile);
-    } else {            // r2 = bwb - c bwb bwb + c VV WW
-        sv_gemm(d.K, bk.R2, bk.bwb, bk.bwb, -c, bk.bwb, 1.0, false, tile);
-        sv_gemm(d.K, bk.R2, bk.VV, bk.WW, c, bk.R2, 1.0, false, tile);
+    const int quarter = threadIdx.x / CY_THREADS, tid = threadIdx.x % CY_THREADS;
+    const int nt = sv_tiles(d.K), idx = 4 * w + quarter;
+    const bool valid = idx < 2 * nt;                // a spare quarter repeats tile 0 without storing
+    const int t = valid ? idx : 0, tile = t % nt;
+    double* lds = arena + quarter * SV_LDS;
+    if (t < nt) {   // r1 = WW - c WV WW - c WW bwb
+        sv_gemm(d.K, bk.R1, bk.WV, bk.WW, -c, bk.WW, 1.0, false, tile, lds, tid, valid);
+        sv_gemm(d.K, bk.R1, bk.WW, bk.bwb, -c, bk.R1, 1.0, false, tile, lds, tid, valid);
+    } else {        // r2 = bwb - c bwb bwb + c VV WW
+        sv_gemm(d.K, bk.R2, bk.bwb, bk.bwb, -c, bk.bwb, 1.0, false, tile, lds, tid, valid);
+        sv_gemm(d.K, bk.R2, bk.VV, bk.WW, c, bk.R2, 1.0, false, tile, lds, tid, valid);
     }
 }
 
@@ -903,24 +918,26 @@ __global__ __launch_bounds__(CY_THREADS) void cy_sv_gemm(CayleyArgs a) {
     const SvBlocks bk(d);
     const int K = d.K, nt = sv_tiles(K), tile = local % nt, which = local / nt;
     const double c = a.c;
+    __shared__ double lds[SV_LDS];
+    const int tid = threadIdx.x;
     double* y = bk.WV;
     double* S = bk.R1;
     double* rp = bk.C11i;
     double* z2 = bk.VV;
     if (PHASE == CY_SV_G1) {
-        if (which == 0) sv_gemm(K, bk.Xm, bk.C11i, bk.WW, c, nullptr, 0.0, false, tile);
-        else sv_gemm(K, y, bk.C11i, bk.R1, 1.0, nullptr, 0.0, false, tile);
+        if (which == 0) sv_gemm(K, bk.Xm, bk.C11i, bk.WW, c, nullptr, 0.0, false, tile, lds, tid);
+        else sv_gemm(K, y, bk.C11i, bk.R1, 1.0, nullptr, 0.0, false, tile, lds, tid);
     } else if (PHASE == CY_SV_G2) {
-        if (which == 0) sv_gemm(K, S, bk.VV, bk.Xm, c, bk.bwb, c, true, tile);
-        else sv_gemm(K, rp, bk.VV, y, c, bk.R2, 1.0, false, tile);
+        if (which == 0) sv_gemm(K, S, bk.VV, bk.Xm, c, bk.bwb, c, true, tile, lds, tid);
+        else sv_gemm(K, rp, bk.VV, y, c, bk.R2, 1.0, false, tile, lds, tid);
     } else if (PHASE == CY_SV_G3) {
-        sv_gemm(K, z2, S, rp, 1.0, nullptr, 0.0, false, tile);
+        sv_gemm(K, z2, S, rp, 1.0, nullptr, 0.0, false, tile, lds, tid);
     } else {
         // z1 = y - X z2, then Y = B W + Z in fp32 (rows 0..K-1: top, K..2K-1: bottom), each
         // element by the thread that forms it
         const int g = (K + SV_T - 1) / SV_T, ti = tile / g, tj = tile % g;
         double acc[4][4];
-        sv_product(K, bk.Xm, z2, ti, tj, acc);
+        sv_product(K, bk.Xm, z2, ti, tj, acc, lds, tid);
         const size_t kk = static_cast<size_t>(K) * K;
         float* Y = d.small + K + kk;
         const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
@@ -944,6 +961,10 @@ __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
     __shared__ double arena[CY_LDS_K * CY_LDS_K + 3 * CY_LDS_K];
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    if (local > 0) {   // the right-hand side, beside the inversion
+        sv_rhs(d, a.c, local - 1, arena);
+        return;
+    }
     if (d.K <= CY_LDS_K) {
         const SvBlocks bk(d);
         if (!kk_gj_inverse_unpivoted(d.K, bk.C11i, bk.WV, a.c, true, arena))
@@ -975,7 +996,6 @@ hipError_t launch_cayley(int phase, const CayleyArgs& args, hipStream_t s) {
         case CY_REDUCE3: hipLaunchKernelGGL(cy_reduce<CY_REDUCE3>, grid, block, 0, s, args); break;
         case CY_SOLVE: hipLaunchKernelGGL(cy_solve, grid, dim3(CY_SOLVE_THREADS), 0, s, args); break;
         case CY_SV_SUM: hipLaunchKernelGGL(cy_sv_sum, grid, block, 0, s, args); break;
-        case CY_SV_R: hipLaunchKernelGGL(cy_sv_r, grid, block, 0, s, args); break;
         case CY_SV_G1: hipLaunchKernelGGL(cy_sv_gemm<CY_SV_G1>, grid, block, 0, s, args); break;
         case CY_SV_G2: hipLaunchKernelGGL(cy_sv_gemm<CY_SV_G2>, grid, block, 0, s, args); break;
         case CY_SV_INV2: hipLaunchKernelGGL(cy_sv_inv2, grid, dim3(CY_SOLVE_THREADS), 0, s, args); break;

@@ -657,8 +657,7 @@ muon_status build_cayley_plan(std::vector<CayleyDesc>& descs, CayleyPlan& pl) {
         per[CY_P2] = prod;
         per[CY_REDUCE3] = 3 * red;
         per[CY_SV_SUM] = sv ? mt * mt : 0;
-        per[CY_SV_R] = 2 * sv;
-        per[CY_SOLVE] = 1;
+        per[CY_SOLVE] = 1 + (2 * sv + 3) / 4;   // the inversion, and the right-hand side's tiles four a workgroup
         per[CY_SV_G1] = 2 * sv;
         per[CY_SV_G2] = 2 * sv;
         per[CY_SV_INV2] = sv ? 1 : 0;
@@ -781,7 +780,7 @@ muon_status muon_cayley_step(const muon_cayley_matrix* mats, int32_t n, const mu
     a.beta = hp->beta;
     a.c = 0.5f * hp->lr;
     const int order[CY_PHASES] = {CY_TRANSPOSE_IN, CY_REDUCE1, CY_COLSUM, CY_MID,   CY_P2,    CY_REDUCE3,
-                                  CY_SV_SUM,       CY_SV_R,    CY_SOLVE,  CY_SV_G1, CY_SV_G2, CY_SV_INV2,
+                                  CY_SV_SUM,       CY_SOLVE,   CY_SV_G1,  CY_SV_G2, CY_SV_INV2,
                                   CY_SV_G3,        CY_SV_G4,   CY_P4,     CY_OUT};
     for (int ph : order) {
         a.prefix = reinterpret_cast<const int32_t*>(base + pl.off_prefix + sizeof(int32_t) * ph * (nmat + 1));

@@ -677,61 +677,96 @@ __device__ __attribute__((always_inline)) void kk_gj_inverse(int K, double* out,
 // C11's symmetric part is I and every pivot is >= 1.  S, the Schur complement of C11:
 // x^T S x = z^T C z for z = [-C11^-1 C12 x; x], so S's symmetric part is at least C's,
 // I + (c / 2) [0, I - V^T V; I - V^T V, 0] on the manifold, whose smallest eigenvalue
-// is 1 - (c / 2) max |1 - sigma(V)^2|.  Same register layout as kk_gj_inverse; per step
-// only the scaled pivot row goes through LDS, with one barrier.  Returns false, with
-// out untouched, if a pivot falls below 1/2 in magnitude; the caller then pivots.
-// out may be src.
+// is 1 - (c / 2) max |1 - sigma(V)^2|.  Returns false, with out untouched, if a pivot
+// fell below 1/2 in magnitude; the caller then pivots.  out may be src.
+//
+// The 128 x 128 working matrix (identity beyond K) sits in registers as 4 x 4 blocks:
+// thread t holds rows 4 (t / 32) + r and columns 4 (t % 32) + e, so the 32 threads of a
+// block row form one half-wave.  Step j: the pivot row's threads scale it and put it in
+// LDS (one barrier); every thread reads the 4 entries over its columns, and takes M[i][j]
+// for its rows from the lane of its half-wave that holds column j (readlane, no LDS).
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+    const long long v = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(v), lane);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), lane);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
 __device__ __attribute__((always_inline)) bool kk_gj_inverse_unpivoted(int K, double* out, const double* src, double scale,
                                                                      bool identity, double* lds) {
-    static_assert(CY_SOLVE_THREADS == 8 * CY_LDS_K, "eight threads per row of the 128 x 128 matrix");
-    constexpr int CB = 16, PSTRIDE = CB + 1, PBUF = 8 * PSTRIDE;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int i = tid >> 3, cb = tid & 7;
-    double* prow = lds;   // [2][8][17] scaled pivot row, as in kk_gj_inverse
-    double m[CB];
+    static_assert(CY_SOLVE_THREADS == (CY_LDS_K / 4) * (CY_LDS_K / 4), "one 4 x 4 block per thread");
+    constexpr int NB = CY_LDS_K / 4;   // 4 x 4 blocks per side
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rb = tid / NB, cb = tid % NB;
+    const int half = lane >> 5;
+    double* prow = lds;                                              // [2][CY_LDS_K] scaled pivot row
+    int* wbad = reinterpret_cast<int*>(lds + 2 * CY_LDS_K);          // [16] per-wave small-pivot flags
+    double m[4][4];
 #pragma unroll
-    for (int k = 0; k < CB; ++k) {
-        const int col = CB * cb + k;
-        if (i < K && col < K)
-            m[k] = (identity && i == col ? 1.0 : 0.0) + scale * src[static_cast<size_t>(i) * K + col];
-        else
-            m[k] = i == col ? 1.0 : 0.0;
-    }
-    bool ok = true;
-    for (int jb = 0; jb < CY_LDS_K / CB && CB * jb < K && ok; ++jb) {
+    for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int e = 0; e < CB; ++e) {
-            const int j = CB * jb + e;
-            if (j < K && ok) {   // uniform
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * rb + r, col = 4 * cb + e;
+            if (i < K && col < K)
+                m[r][e] = (identity && i == col ? 1.0 : 0.0) + scale * src[static_cast<size_t>(i) * K + col];
+            else
+                m[r][e] = i == col ? 1.0 : 0.0;
+        }
+    int bad = 0;   // a pivot of this wave's block rows fell below 1/2 (uniform in the wave)
+    for (int jb = 0; 4 * jb < K; ++jb) {
+#pragma unroll
+        for (int je = 0; je < 4; ++je) {
+            const int j = 4 * jb + je;
+            if (j < K) {   // uniform
                 const int buf = j & 1;
-                const double colf = __shfl(m[e], (lane & ~7) | jb, 64);   // M[i][j]; M[j][j] on row j
-                if (i == j) {
-                    const double inv = 1.0 / colf;
+                // M[4 rb + r][j], from the lane of this half-wave that holds block column jb
+                double colf[4];
 #pragma unroll
-                    for (int k = 0; k < CB; ++k) {
-                        m[k] = (CB * cb + k == j) ? inv : m[k] * inv;
-                        prow[buf * PBUF + PSTRIDE * cb + k] = m[k];
+                for (int r = 0; r < 4; ++r) {
+                    const double c0 = readlane_f64(m[r][je], jb), c1 = readlane_f64(m[r][je], 32 + jb);
+                    colf[r] = half ? c1 : c0;
+                }
+                if (wave == jb >> 1) {   // the wave that holds pivot row j
+                    const double diag = readlane_f64(m[je][je], 32 * (jb & 1) + jb);
+                    bad |= !(fabs(diag) >= 0.5);
+                    if (rb == jb) {
+                        const double inv = 1.0 / diag;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) m[je][e] = (4 * cb + e == j) ? inv : m[je][e] * inv;
+                        f32x4_t* dst = reinterpret_cast<f32x4_t*>(prow + buf * CY_LDS_K + 4 * cb);
+                        dst[0] = __builtin_bit_cast(f32x4_t, make_double2(m[je][0], m[je][1]));
+                        dst[1] = __builtin_bit_cast(f32x4_t, make_double2(m[je][2], m[je][3]));
                     }
                 }
                 lds_barrier();
-                const double inv = prow[buf * PBUF + PSTRIDE * jb + e];
-                ok = fabs(inv) <= 2.0;   // |pivot| >= 1/2, the same decision in every thread
-                if (i != j) {
+                const f32x4_t* srcp = reinterpret_cast<const f32x4_t*>(prow + buf * CY_LDS_K + 4 * cb);
+                const double2 p01 = __builtin_bit_cast(double2, srcp[0]), p23 = __builtin_bit_cast(double2, srcp[1]);
+                const double pv[4] = {p01.x, p01.y, p23.x, p23.y};
 #pragma unroll
-                    for (int k = 0; k < CB; ++k) {
-                        const int col = CB * cb + k;
-                        m[k] = col == j ? -colf * inv : m[k] - colf * prow[buf * PBUF + PSTRIDE * cb + k];
+                for (int r = 0; r < 4; ++r) {
+                    if (4 * rb + r != j) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int col = 4 * cb + e;
+                            m[r][e] = col == j ? -colf[r] * pv[e] : m[r][e] - colf[r] * pv[e];
+                        }
                     }
                 }
             }
         }
     }
-    if (ok && i < K) {
+    if (lane == 0) wbad[wave] = bad;
+    __syncthreads();
+    bool ok = true;
 #pragma unroll
-        for (int k = 0; k < CB; ++k) {
-            const int b = CB * cb + k;
-            if (b < K) out[static_cast<size_t>(i) * K + b] = m[k];
-        }
+    for (int w = 0; w < CY_SOLVE_THREADS / 64; ++w) ok = ok && !wbad[w];
+    if (ok) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * rb + r, col = 4 * cb + e;
+                if (i < K && col < K) out[static_cast<size_t>(i) * K + col] = m[r][e];
+            }
     }
     __syncthreads();   // out is complete (global), and every thread has left the LDS buffers
     return ok;
@@ -958,7 +993,7 @@ __global__ __launch_bounds__(CY_THREADS) void cy_sv_gemm(CayleyArgs a) {
 
 // SOLVE: C11^-1 for K <= CY_LDS_K, the whole 2K x 2K LU solve otherwise; SV_INV2: S^-1
 __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
-    __shared__ double arena[CY_LDS_K * CY_LDS_K + 3 * CY_LDS_K];
+    __shared__ __attribute__((aligned(16))) double arena[CY_LDS_K * CY_LDS_K + 3 * CY_LDS_K];
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
     if (local > 0) {   // the right-hand side, beside the inversion
@@ -974,7 +1009,7 @@ __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_solve(CayleyArgs a) {
     }
 }
 __global__ __launch_bounds__(CY_SOLVE_THREADS) void cy_sv_inv2(CayleyArgs a) {
-    __shared__ double arena[CY_LDS_K * CY_LDS_K + 3 * CY_LDS_K];
+    __shared__ __attribute__((aligned(16))) double arena[CY_LDS_K * CY_LDS_K + 3 * CY_LDS_K];
     int local;
     const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
     const SvBlocks bk(d);

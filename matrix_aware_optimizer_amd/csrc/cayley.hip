@@ -339,13 +339,20 @@ __global__ __launch_bounds__(CY_THREADS, 4) void cy_p2(CayleyArgs a) {
     const float* S = d.small + d.K;
     nn_accumulate(d.wf, d.K, d.N, S, d.K, d.K, r0, c0, acc);
     const float beta = a.beta, omb = 1.0f - a.beta;
+    // descriptor fields in registers: the stores below could alias the descriptor table,
+    // so reading them through d would reload them after every store
+    const int N = d.N, K = d.K;
+    float* const mf = d.mf;
+    float* const vo = d.v;
+    const float* const gf = d.gf;
+    const float* const mean = d.small;
     acc.each([&](int tr, int tc, float x) {
         const int r = r0 + tr, j = c0 + tc;
-        if (r < d.N && j < d.K) {
-            const size_t idx = static_cast<size_t>(r) * d.K + j;
-            const float mn = fmaf(beta, G(d.mf)[idx], omb * (G(d.gf)[idx] - G(d.small)[j]));
-            G(d.mf)[idx] = mn;
-            G(d.v)[idx] = mn - x;
+        if (r < N && j < K) {
+            const size_t idx = static_cast<size_t>(r) * K + j;
+            const float mn = fmaf(beta, G(mf)[idx], omb * (G(gf)[idx] - G(mean)[j]));
+            G(mf)[idx] = mn;
+            G(vo)[idx] = mn - x;
         }
     });
 }
@@ -362,11 +369,15 @@ __global__ __launch_bounds__(CY_THREADS, 4) void cy_p4(CayleyArgs a) {
     acc.zero();
     nn_accumulate(d.v, d.K, d.N, Y, d.K, d.K, r0, c0, acc);
     nn_accumulate(d.wf, d.K, d.N, Y + kk, d.K, d.K, r0, c0, acc);
+    const int N = d.N, K = d.K;   // in registers, as in p2
+    float* const wnew = d.wnew;
+    const float* const wf = d.wf;
+    const float c = a.c;
     acc.each([&](int tr, int tc, float x) {
         const int r = r0 + tr, j = c0 + tc;
-        if (r < d.N && j < d.K) {
-            const size_t idx = static_cast<size_t>(r) * d.K + j;
-            G(d.wnew)[idx] = fmaf(-a.c, x, G(d.wf)[idx]);
+        if (r < N && j < K) {
+            const size_t idx = static_cast<size_t>(r) * K + j;
+            G(wnew)[idx] = fmaf(-c, x, G(wf)[idx]);
         }
     });
 }

@@ -148,7 +148,9 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
 
     for (int t = t0; t < t1; ++t) {
         while (t >= args.prefix[mi + 1]) ++mi;
-        const MatDesc& d = args.descs[mi];
+        // by value: the fields are read once per tile into registers (the stores below could
+        // alias the descriptor table, so reads through a reference would follow every store)
+        const MatDesc d = args.descs[mi];
         int i0, j0;
         ew_tile_origin(d, t - args.prefix[mi], i0, j0);
         float u[EW_PASSES][EW_GROUP];

@@ -937,8 +937,11 @@ __device__ __attribute__((always_inline)) void apply_epilogue(f32x16_t (&acc)[E:
     const bool hh = (threadIdx.x >> 5) & 1;
     const bool odd = odd_quad();
     const int mbase = q.raw_row - (hh ? 4 : 0);
+    // descriptor fields in registers: the weight stores could alias the descriptor table, so
+    // reading them through d would reload them after every store
     const float coef = d.apply_coef, decay = d.decay;
     const bool tall = d.tall != 0, vec = d.uvec != 0;
+    const int rows = d.rows, cols = d.cols;
     char* const w = static_cast<char*>(d.w);
 #pragma unroll
     for (int i = 0; i < E::SM; ++i) {
@@ -960,14 +963,14 @@ __device__ __attribute__((always_inline)) void apply_epilogue(f32x16_t (&acc)[E:
         float wv[E::SN * 2][8];
 #pragma unroll
         for (int k = 0; k < E::SN * 2; ++k) {
-            const bool in = ur[k] < d.rows && uc[k] < d.cols;
-            const size_t idx = static_cast<size_t>(ur[k]) * d.cols + uc[k];
+            const bool in = ur[k] < rows && uc[k] < cols;
+            const size_t idx = static_cast<size_t>(ur[k]) * cols + uc[k];
             if (vec) {
                 if (in) IO::load8(w + idx * sizeof(T), wv[k]);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    wv[k][e] = (in && uc[k] + e < d.cols) ? IO::load1(w + (idx + e) * sizeof(T)) : 0.0f;
+                    wv[k][e] = (in && uc[k] + e < cols) ? IO::load1(w + (idx + e) * sizeof(T)) : 0.0f;
             }
         }
 #pragma unroll
@@ -1000,17 +1003,17 @@ __device__ __attribute__((always_inline)) void apply_epilogue(f32x16_t (&acc)[E:
                         x[4 + p] = odd ? keep : recv;
                     }
                 }
-                if (ur[k] >= d.rows || uc[k] >= d.cols) continue;
+                if (ur[k] >= rows || uc[k] >= cols) continue;
                 float o[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) o[e] = fmaf(-coef, x[e], decay * wv[k][e]);
-                const size_t idx = static_cast<size_t>(ur[k]) * d.cols + uc[k];
+                const size_t idx = static_cast<size_t>(ur[k]) * cols + uc[k];
                 if (vec) {
                     IO::store8(w + idx * sizeof(T), o);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
-                        if (uc[k] + e < d.cols) IO::store1(w + (idx + e) * sizeof(T), o[e]);
+                        if (uc[k] + e < cols) IO::store1(w + (idx + e) * sizeof(T), o[e]);
                 }
             }
     }

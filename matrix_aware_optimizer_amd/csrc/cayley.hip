@@ -9,7 +9,8 @@
 // The retraction goes through the 2K x 2K form: with U = [V, W], B = [W^T; -V^T]
 // (A = U B), C = I + c B U, B W = [W^T W; -V^T W] and Z = C^-1 (B W - c (B U)(B W)),
 // W' = W - c U (B W + Z).  Everything N-sized is then four passes:
-//   reduce1  W^T G, W^T M (K x K partials per row block) and column sums of G, W;
+//   reduce1  W^T G, W^T M (K x K partials per row block) and, in the same launch,
+//            column sums of G, W;
 //   mid      mean(G), S = sym(beta W^T M + (1 - beta)(W^T G - colsum(W) mean^T))
 //            (= sym(W^T M') by linearity, so M' needs no extra pass);
 //   p2       M' (in place) and V = M' - W S;
@@ -172,34 +173,10 @@ __device__ __attribute__((always_inline)) void tn_block(const float* X, const fl
     });
 }
 
-// One K x K product tile of one row block per workgroup.  REDUCE1: W^T G and W^T M;
-// REDUCE3: W^T W, W^T V and V^T V (the partial slots 0, 1, 2 of the row block).
-template <int PHASE>
-__global__ __launch_bounds__(CY_THREADS) void cy_reduce(CayleyArgs a) {
-    int local;
-    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
-    const int per = d.gk * d.gk;
-    const int t2 = local % per, rest = local / per;
-    const int rb = rest % d.nrb, prod = rest / d.nrb;
-    const int i0 = (t2 / d.gk) * CY_GT, j0 = (t2 % d.gk) * CY_GT;
-    const int rs = rb * CY_RB, re = min(d.N, rs + CY_RB);
-    const size_t kk = static_cast<size_t>(d.K) * d.K;
-    float* out = d.part + (static_cast<size_t>(rb) * 3 + prod) * kk;
-    if (PHASE == CY_REDUCE1) {
-        tn_block(d.wf, prod == 0 ? d.gf : d.mf, d.K, rs, re, i0, j0, out);
-    } else {
-        const float* X = prod == 2 ? d.v : d.wf;
-        const float* Y = prod == 0 ? d.wf : d.v;
-        tn_block(X, Y, d.K, rs, re, i0, j0, out);
-    }
-}
-
-// column sums of G and W over a row block (thread j owns column j)
-__global__ __launch_bounds__(CY_THREADS) void cy_colsum(CayleyArgs a) {
+// column sums of G and W over row block rb (thread j owns column j)
+__device__ void colsum_block(const CayleyDesc& d, int rb) {
     __shared__ float part[2][CY_THREADS];
-    int local;
-    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
-    const int rb = local, K = d.K, tid = threadIdx.x;
+    const int K = d.K, tid = threadIdx.x;
     // column j = tid % K; the CY_THREADS / K row subsets of the block are summed
     // separately (rows s, s + S, ...) and combined in a fixed order
     const int S = max(1, CY_THREADS / K), j = tid % K, sub = tid / K;
@@ -226,6 +203,35 @@ __global__ __launch_bounds__(CY_THREADS) void cy_colsum(CayleyArgs a) {
         G(d.colpart)[(static_cast<size_t>(rb) * 2 + 1) * K + tid] = tw;
     }
 }
+
+// One K x K product tile of one row block per workgroup.  REDUCE1: W^T G and W^T M, and
+// after them the column sums of G and W, one row block per workgroup (they read the same
+// inputs and fill workgroup slots the products leave free); REDUCE3: W^T W, W^T V and
+// V^T V (the partial slots 0, 1, 2 of the row block).
+template <int PHASE>
+__global__ __launch_bounds__(CY_THREADS) void cy_reduce(CayleyArgs a) {
+    int local;
+    const CayleyDesc& d = cy_locate(a, blockIdx.x, local);
+    const int per = d.gk * d.gk;
+    if (PHASE == CY_REDUCE1 && local >= 2 * d.nrb * per) {
+        colsum_block(d, local - 2 * d.nrb * per);
+        return;
+    }
+    const int t2 = local % per, rest = local / per;
+    const int rb = rest % d.nrb, prod = rest / d.nrb;
+    const int i0 = (t2 / d.gk) * CY_GT, j0 = (t2 % d.gk) * CY_GT;
+    const int rs = rb * CY_RB, re = min(d.N, rs + CY_RB);
+    const size_t kk = static_cast<size_t>(d.K) * d.K;
+    float* out = d.part + (static_cast<size_t>(rb) * 3 + prod) * kk;
+    if (PHASE == CY_REDUCE1) {
+        tn_block(d.wf, prod == 0 ? d.gf : d.mf, d.K, rs, re, i0, j0, out);
+    } else {
+        const float* X = prod == 2 ? d.v : d.wf;
+        const float* Y = prod == 0 ? d.wf : d.v;
+        tn_block(X, Y, d.K, rs, re, i0, j0, out);
+    }
+}
+
 
 // K x K sums by CY_MT x CY_MT tile pairs: a workgroup sums the row-block partials of
 // its tile (i0, j0) and of the mirror tile (j0, i0), both read as coalesced rows, and
@@ -1036,7 +1042,6 @@ hipError_t launch_cayley(int phase, const CayleyArgs& args, hipStream_t s) {
     switch (phase) {
         case CY_TRANSPOSE_IN: hipLaunchKernelGGL(cy_transpose_in, grid, block, 0, s, args); break;
         case CY_REDUCE1: hipLaunchKernelGGL(cy_reduce<CY_REDUCE1>, grid, block, 0, s, args); break;
-        case CY_COLSUM: hipLaunchKernelGGL(cy_colsum, grid, block, 0, s, args); break;
         case CY_MID: hipLaunchKernelGGL(cy_mid, grid, block, 0, s, args); break;
         case CY_P2: hipLaunchKernelGGL(cy_p2, grid, block, 0, s, args); break;
         case CY_REDUCE3: hipLaunchKernelGGL(cy_reduce<CY_REDUCE3>, grid, block, 0, s, args); break;

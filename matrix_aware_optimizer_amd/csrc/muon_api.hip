@@ -650,8 +650,7 @@ muon_status build_cayley_plan(std::vector<CayleyDesc>& descs, CayleyPlan& pl) {
         const int64_t sv = d.K <= CY_LDS_K ? svg * svg : 0;
         int64_t per[CY_PHASES] = {};
         per[CY_TRANSPOSE_IN] = d.tall ? 0 : tiles;
-        per[CY_REDUCE1] = 2 * red;
-        per[CY_COLSUM] = d.nrb;
+        per[CY_REDUCE1] = 2 * red + d.nrb;   // W^T G, W^T M tiles, then one column-sum block per row block
         const int64_t mt = (d.K + CY_MT - 1) / CY_MT;                     // K x K sums in CY_MT tiles
         per[CY_MID] = mt * mt;
         per[CY_P2] = prod;
@@ -779,9 +778,8 @@ muon_status muon_cayley_step(const muon_cayley_matrix* mats, int32_t n, const mu
     a.nmat = static_cast<int32_t>(nmat);
     a.beta = hp->beta;
     a.c = 0.5f * hp->lr;
-    const int order[CY_PHASES] = {CY_TRANSPOSE_IN, CY_REDUCE1, CY_COLSUM, CY_MID,   CY_P2,    CY_REDUCE3,
-                                  CY_SV_SUM,       CY_SOLVE,   CY_SV_G1,  CY_SV_G2, CY_SV_INV2,
-                                  CY_SV_G3,        CY_SV_G4,   CY_P4,     CY_OUT};
+    const int order[CY_PHASES] = {CY_TRANSPOSE_IN, CY_REDUCE1, CY_MID,   CY_P2,    CY_REDUCE3, CY_SV_SUM, CY_SOLVE,
+                                  CY_SV_G1,        CY_SV_G2,   CY_SV_INV2, CY_SV_G3, CY_SV_G4,   CY_P4,     CY_OUT};
     for (int ph : order) {
         a.prefix = reinterpret_cast<const int32_t*>(base + pl.off_prefix + sizeof(int32_t) * ph * (nmat + 1));
         a.total = pl.prefix[ph][nmat];

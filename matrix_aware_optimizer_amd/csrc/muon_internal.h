@@ -149,10 +149,10 @@ struct CayleyArgs {
 // Kernel launchers (defined next to the kernels).
 // CY_SOLVE inverts C11 and forms the right-hand side (K <= 128) or solves the whole
 // system (K > 128); the CY_SV_* phases are the rest of the split solve for K <= 128.
-enum CayleyPhase : int32_t { CY_TRANSPOSE_IN = 0, CY_REDUCE1 = 1, CY_COLSUM = 2, CY_MID = 3, CY_P2 = 4,
-                             CY_REDUCE3 = 5, CY_SOLVE = 6, CY_P4 = 7, CY_OUT = 8, CY_SV_SUM = 9,
-                             CY_SV_G1 = 10, CY_SV_G2 = 11, CY_SV_INV2 = 12, CY_SV_G3 = 13, CY_SV_G4 = 14 };
-constexpr int CY_PHASES = 15;
+enum CayleyPhase : int32_t { CY_TRANSPOSE_IN = 0, CY_REDUCE1 = 1, CY_MID = 2, CY_P2 = 3, CY_REDUCE3 = 4,
+                             CY_SOLVE = 5, CY_P4 = 6, CY_OUT = 7, CY_SV_SUM = 8, CY_SV_G1 = 9, CY_SV_G2 = 10,
+                             CY_SV_INV2 = 11, CY_SV_G3 = 12, CY_SV_G4 = 13 };
+constexpr int CY_PHASES = 14;
 hipError_t launch_cayley(int phase, const CayleyArgs& args, hipStream_t s);
 hipError_t launch_adamw(int dtype, const AdamWArgs& args, int grid, hipStream_t s);
 hipError_t launch_momentum_norm(int dtype, bool ns_only, const EwArgs& args, int grid, hipStream_t s);

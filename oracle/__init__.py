@@ -54,7 +54,7 @@ from .jacobi_svd import jacobi_svd, msign_via_svd  # noqa: F401
 from .adamw_oracle import adamw_step  # noqa: F401
 from .cayley_oracle import (  # noqa: F401
     cayley_retraction,
-    cayley_retraction_woodbury,
+    cayley_retraction_lowrank,
     cayley_step,
     center_columns,
     orthogonality_error,

@@ -14,8 +14,9 @@ Source: [Muon在Stiefel流形上的精确闭式更新解析] (mlqm.cn/news/13391
 * section 3.3: the order of one step is: center the gradient, update the
   momentum as M = beta M + (1 - beta) G_centered, project M onto the tangent
   space at W to get V, apply the Cayley update;
-* section 6.2: the same update through a 2k x 2k system (Woodbury form), with
-  U = [V, W] and B = [W^T; -V^T], so A = U B.
+* section 6.2: the same update reduces to a 2k x 2k linear system, because A
+  has rank at most 2k (see cayley_retraction_lowrank for the derivation used
+  here).
 
 Readings where the pages leave a choice:
 * centering subtracts each column's mean over the rows (the page's code takes
@@ -59,18 +60,23 @@ def cayley_retraction(W, V, lr):
     return np.linalg.solve(eye + c * A, (eye - c * A) @ W)
 
 
-def cayley_retraction_woodbury(W, V, lr):
-    """The same update through the 2k x 2k system of the page's Woodbury form."""
+def cayley_retraction_lowrank(W, V, lr):
+    """The same update through a 2k x 2k solve instead of an n x n one.
+
+    Derivation (section 6.2 states that the n x n system reduces to 2k x 2k):
+    A = V W^T - W V^T factors as A = L R with L = [V, W] (n x 2k) and
+    R = [W^T; -V^T] (2k x n).  Since I - cA = 2I - (I + cA), the Cayley factor
+    is (I + cA)^(-1) (I - cA) = 2 (I + cA)^(-1) - I.  The Woodbury identity
+    gives (I + c L R)^(-1) = I - c L (I_2k + c R L)^(-1) R, hence
+        W' = 2 (I + cA)^(-1) W - W = W - 2c L (I_2k + c R L)^(-1) (R W).
+    """
     W = np.asarray(W, np.float64)
     V = np.asarray(V, np.float64)
-    k = W.shape[1]
     c = np.float64(lr) / 2.0
-    U = np.concatenate([V, W], axis=1)          # n x 2k
-    B = np.concatenate([W.T, -V.T], axis=0)     # 2k x n
-    C = np.eye(2 * k) + c * (B @ U)
-    b = W - c * (U @ (B @ W))                   # (I - c A) W
-    z = np.linalg.solve(C, B @ b)
-    return b - c * (U @ z)
+    left = np.hstack([V, W])
+    right = np.vstack([W.T, -V.T])
+    inner = np.eye(left.shape[1]) + c * (right @ left)
+    return W - 2.0 * c * (left @ np.linalg.solve(inner, right @ W))
 
 
 def cayley_step(W, G, M, *, lr, beta, retraction=cayley_retraction):

@@ -7,7 +7,7 @@
   and leaves tangent vectors unchanged.
 * First order: (W'(lr) - W) / lr -> -(V - W V^T W) as lr -> 0, which fixes the
   sign of A and c = lr / 2.
-* The page's Woodbury form (section 6.2) equals the n x n solve.
+* The 2k x 2k (low-rank, Woodbury) form of section 6.2 equals the n x n solve.
 * Momentum of centered constant gradients: M_t = (1 - beta^t) G_centered.
 * The leading block C11 = I + c W^T V of the 2k system (section 6.2): on the
   manifold W^T V is skew, so C11's symmetric part is I and elimination without
@@ -71,13 +71,13 @@ def test_first_order_direction():
 
 
 @pytest.mark.parametrize("shape", [(64, 16), (33, 5), (8, 8)])
-def test_woodbury_form_equals_direct_solve(shape):
+def test_lowrank_form_equals_direct_solve(shape):
     rng = np.random.default_rng(4)
     W = _stiefel(rng, *shape)
     V = orc.project_tangent(W, rng.standard_normal(shape))
     for lr in (1e-3, 0.3, 2.0):
         a = orc.cayley_retraction(W, V, lr)
-        b = orc.cayley_retraction_woodbury(W, V, lr)
+        b = orc.cayley_retraction_lowrank(W, V, lr)
         assert np.max(np.abs(a - b)) < 1e-12
 
 

@@ -174,9 +174,13 @@ muon_status muon_adamw_step(const muon_adamw_tensor* tensors, int32_t n, const m
  *   M' = beta M + (1 - beta) (G - 1 mean(G)^T)      mean over the rows
  *   V  = M' - W sym(W^T M'),   sym(S) = (S + S^T) / 2
  *   W' = (I + c A)^-1 (I - c A) W,  A = V W^T - W V^T,  c = lr / 2
- * computed through the 2k x 2k Woodbury form (k = min(rows, cols)).  fp32
- * buffers; the 2k x 2k solve runs in fp64 with partial pivoting.  No weight
- * decay on this path.
+ * computed through a 2k x 2k linear system (A has rank at most 2k,
+ * k = min(rows, cols)).  fp32 buffers; the 2k x 2k solve runs in fp64.  For
+ * k <= 128 it eliminates by k x k blocks and inverts the two diagonal blocks
+ * by Gauss-Jordan without pivoting (on the manifold the symmetric part of each
+ * is positive definite), switching to partial pivoting for a block whose
+ * pivot falls below 1/2; for k > 128 it is an LU factorization with partial
+ * pivoting.  No weight decay on this path.
  * --------------------------------------------------------------------------- */
 typedef struct {
     float*       weight;    /* in/out rows x cols, fp32, row-major */

@@ -196,6 +196,28 @@ def _stream_handle(stream):
     return ctypes.c_void_p(int(stream.cuda_stream))
 
 
+def _workspace_for(need: int, workspace, device, stream):
+    """The workspace a call runs with, safe for torch's caching allocator.
+
+    The kernels use the workspace on ``stream``.  A workspace allocated here
+    is allocated on that stream, so the allocator orders its reuse after the
+    work enqueued there; a caller's workspace used on a stream other than the
+    current one is recorded on it (``record_stream``), so dropping it does not
+    hand its memory to other work while the call's kernels still read it.
+    """
+    import torch
+    if workspace is None:
+        if stream is None:
+            return allocate_workspace(need, device)
+        with torch.cuda.stream(stream):
+            return allocate_workspace(need, device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise MuonError(MUON_ERR_WORKSPACE, f"workspace has {workspace.numel()} bytes, {need} needed")
+    if stream is not None and stream != torch.cuda.current_stream(workspace.device):
+        workspace.record_stream(stream)
+    return workspace
+
+
 def _matrices(weights, grads, moms):
     weights, grads, moms = list(weights), list(grads), list(moms)
     if not (len(weights) == len(grads) == len(moms)):
@@ -260,10 +282,7 @@ def muon_step(weights: Iterable, grads: Iterable, moms: Iterable, *, lr, beta=0.
     need = lib.muon_workspace_bytes(arr, n, ctypes.byref(hp))
     if need == 0:
         raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error_message())
-    if workspace is None:
-        workspace = allocate_workspace(need, weights[0].device if weights else None)
-    elif workspace.numel() * workspace.element_size() < need:
-        raise MuonError(MUON_ERR_WORKSPACE, f"workspace has {workspace.numel()} bytes, {need} needed")
+    workspace = _workspace_for(need, workspace, weights[0].device if weights else None, stream)
     _check(lib.muon_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                          workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return workspace
@@ -308,10 +327,7 @@ def muon_ns(inputs, outputs, *, schedule, eps=1e-7, workspace=None, stream=None)
     need = lib.muon_ns_workspace_bytes(arr, n, ctypes.byref(hp))
     if need == 0:
         raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error_message())
-    if workspace is None:
-        workspace = allocate_workspace(need, inputs[0].device if inputs else None)
-    elif workspace.numel() * workspace.element_size() < need:
-        raise MuonError(MUON_ERR_WORKSPACE, f"workspace has {workspace.numel()} bytes, {need} needed")
+    workspace = _workspace_for(need, workspace, inputs[0].device if inputs else None, stream)
     _check(lib.muon_ns(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                        workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return workspace
@@ -367,10 +383,7 @@ def muon_adamw_step(params, grads, exp_avgs, exp_avg_sqs, *, lr, betas=(0.9, 0.9
     need = lib.muon_adamw_workspace_bytes(arr, n, ctypes.byref(hp))
     if need == 0:
         raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error_message())
-    if workspace is None:
-        workspace = allocate_workspace(need, params[0].device if params else None)
-    elif workspace.numel() * workspace.element_size() < need:
-        raise MuonError(MUON_ERR_WORKSPACE, f"workspace has {workspace.numel()} bytes, {need} needed")
+    workspace = _workspace_for(need, workspace, params[0].device if params else None, stream)
     _check(lib.muon_adamw_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                                workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return workspace
@@ -414,10 +427,7 @@ def muon_cayley_step(weights, grads, moms, *, lr, beta=0.9, workspace=None, stre
     need = lib.muon_cayley_workspace_bytes(arr, n, ctypes.byref(hp))
     if need == 0:
         raise MuonError(MUON_ERR_INVALID_ARG, muon_last_error_message())
-    if workspace is None:
-        workspace = allocate_workspace(need, weights[0].device if weights else None)
-    elif workspace.numel() * workspace.element_size() < need:
-        raise MuonError(MUON_ERR_WORKSPACE, f"workspace has {workspace.numel()} bytes, {need} needed")
+    workspace = _workspace_for(need, workspace, weights[0].device if weights else None, stream)
     _check(lib.muon_cayley_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                                 workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return workspace

@@ -1,20 +1,23 @@
-"""DIAGNOSTIC, NOT THE ORACLE: why the GPU path keeps the Newton-Schulz iterate in fp32.
+"""DIAGNOSTIC, NOT THE ORACLE: why the GPU path keeps about 16 bits of the Newton-Schulz iterate.
 
 Emulates a bf16-MFMA Newton-Schulz on the CPU (operands rounded to bf16,
-products accumulated in fp32) under two storage plans and compares both with
+products accumulated in fp32) under three storage plans and compares each with
 the fp64 oracle on the same bf16 inputs:
 
 * "bf16 storage": X is rounded to bf16 between steps (what a plain bf16
   implementation of the pages' listing does);
 * "fp32 iterate": X stays fp32, and only the operand copies of X, A and B are
-  rounded to bf16 (the plan the kernels follow).
+  rounded to bf16;
+* "bf16 pair": X is stored as hi + lo with hi = bf16(X) and lo = bf16(X - hi)
+  (about 16 significant bits) and hi serves as the MFMA operand.  This is the
+  plan the bf16 kernels follow (fp32 matrices keep an fp32 iterate).
 
 Each step multiplies small singular values by about a = 3.4445
 ([Muon优化器], Newton-Schulz coefficient section), so rounding noise in those
 directions is amplified with them; storing X in bf16 re-injects that noise
 every step.  Run as a script for the table at sizes shaped like the workloads:
 
-    python tests/diag_bf16_emulation.py [--full]
+    python tests/diag_bf16_emulation.py [--seeds N]
 
 ``tests/test_diag_bf16_emulation.py`` runs one small case in the CPU suite.
 """

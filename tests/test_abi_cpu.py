@@ -235,3 +235,71 @@ def test_adamw_workspace_errors_and_noops():
     assert lib.muon_adamw_step(None, 0, ctypes.byref(hp), None, 0, None) == mao.MUON_OK
     skip = _adamw([(FAKE, None, FAKE + (2 << 30), FAKE + (3 << 30), 1000)])
     assert lib.muon_adamw_step(skip, 1, ctypes.byref(hp), None, 0, None) == mao.MUON_OK
+
+
+def _cayley_mats(specs):
+    arr = (mao.MuonCayleyMatrix * len(specs))()
+    for i, (w, g, m, r, c) in enumerate(specs):
+        arr[i] = mao.MuonCayleyMatrix(w, g, m, r, c)
+    return arr
+
+
+@pytest.mark.parametrize("case", [
+    "null_hp", "beta_high", "beta_neg", "beta_nan", "nan_lr", "zero_cols", "null_weight", "null_momentum",
+    "overlap", "misaligned",
+])
+def test_cayley_invalid_arguments_are_rejected(case):
+    lib = mao.load()
+    specs = [(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 512, 64)]
+    hp = mao.MuonCayleyHparams(1e-3, 0.9)
+    if case == "beta_high":
+        hp.beta = 1.0
+    elif case == "beta_neg":
+        hp.beta = -0.1
+    elif case == "beta_nan":
+        hp.beta = float("nan")
+    elif case == "nan_lr":
+        hp.lr = float("inf")
+    elif case == "zero_cols":
+        specs = [(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 512, 0)]
+    elif case == "null_weight":
+        specs = [(None, FAKE + (1 << 30), FAKE + (2 << 30), 512, 64)]
+    elif case == "null_momentum":
+        specs = [(FAKE, FAKE + (1 << 30), None, 512, 64)]
+    elif case == "overlap":
+        # momentum starts inside the weight
+        specs = [(FAKE, FAKE + (1 << 30), FAKE + 4096, 512, 64)]
+    elif case == "misaligned":
+        specs = [(FAKE, FAKE + (1 << 30) + 2, FAKE + (2 << 30), 512, 64)]
+    arr = _cayley_mats(specs)
+    hpp = None if case == "null_hp" else ctypes.byref(hp)
+    st = lib.muon_cayley_step(arr, 1, hpp, ctypes.c_void_p(FAKE + (8 << 30)), 1 << 40, None)
+    assert st == mao.MUON_ERR_INVALID_ARG, (case, st, mao.muon_last_error_message())
+    assert mao.muon_last_error_message() != ""
+    assert lib.muon_cayley_workspace_bytes(arr, 1, hpp) == 0
+
+
+def test_cayley_size_limit_and_workspace_errors():
+    lib = mao.load()
+    hp = mao.MuonCayleyHparams(1e-3, 0.9)
+    # min(rows, cols) above the limit is unsupported, in either orientation
+    for r, c in ((4096, 257), (257, 4096)):
+        arr = _cayley_mats([(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), r, c)])
+        st = lib.muon_cayley_step(arr, 1, ctypes.byref(hp), ctypes.c_void_p(FAKE + (8 << 30)), 1 << 40, None)
+        assert st == mao.MUON_ERR_UNSUPPORTED, (r, c, st)
+        assert lib.muon_cayley_workspace_bytes(arr, 1, ctypes.byref(hp)) == 0
+    # the limit itself is accepted by the host checks
+    arr = _cayley_mats([(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 4096, 256)])
+    need = lib.muon_cayley_workspace_bytes(arr, 1, ctypes.byref(hp))
+    assert need > 0
+    ws = FAKE + (8 << 30)
+    assert lib.muon_cayley_step(arr, 1, ctypes.byref(hp), None, need, None) == mao.MUON_ERR_WORKSPACE
+    assert lib.muon_cayley_step(arr, 1, ctypes.byref(hp), ctypes.c_void_p(ws), need - 1, None) == mao.MUON_ERR_WORKSPACE
+    assert lib.muon_cayley_step(arr, 1, ctypes.byref(hp), ctypes.c_void_p(ws + 16), need, None) == mao.MUON_ERR_WORKSPACE
+    # a workspace overlapping a matrix is an argument error
+    st = lib.muon_cayley_step(arr, 1, ctypes.byref(hp), ctypes.c_void_p(FAKE + (1 << 30)), need, None)
+    assert st == mao.MUON_ERR_INVALID_ARG
+    # empty list and all-skipped lists do nothing and succeed without a workspace
+    assert lib.muon_cayley_step(None, 0, ctypes.byref(hp), None, 0, None) == mao.MUON_OK
+    skip = _cayley_mats([(FAKE, None, FAKE + (2 << 30), 512, 64)])
+    assert lib.muon_cayley_step(skip, 1, ctypes.byref(hp), None, 0, None) == mao.MUON_OK

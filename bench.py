@@ -39,17 +39,17 @@ HBM_PEAK_GBS = 8000.0
 PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o transformer "
-    "-- python3 $R/bench.py --steps 5 --warmup 2 --no-cpu-baseline",
+    "-- python3 $R/bench.py --steps 5 --warmup 2 --only --no-cpu-baseline",
     "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"ns_gemm_kernel<unsigned short, 2>\" --output-format csv "
-    "-d $R/gpurun_out/prof/fetch -o upd -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "-d $R/gpurun_out/prof/fetch -o upd -- python3 $R/bench.py --steps 2 --warmup 1 --only --no-cpu-baseline",
     "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"ns_gemm_kernel<unsigned short, 2>\" --output-format csv "
-    "-d $R/gpurun_out/prof/write -o upd -- python3 $R/bench.py --steps 2 --warmup 1 --no-cpu-baseline",
+    "-d $R/gpurun_out/prof/write -o upd -- python3 $R/bench.py --steps 2 --warmup 1 --only --no-cpu-baseline",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/cfetch -o copy "
     "-- python3 $R/bench.py --calibrate-copy",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/cwrite -o copy "
     "-- python3 $R/bench.py --calibrate-copy",
     "rocprofv3 --kernel-trace --pmc GRBM_COUNT GRBM_GUI_ACTIVE --kernel-include-regex \"ns_gemm_kernel\" "
-    "--output-format csv -d $R/gpurun_out/prof/clock -o clk -- python3 $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+    "--output-format csv -d $R/gpurun_out/prof/clock -o clk -- python3 $R/bench.py --steps 1 --warmup 1 --only --no-cpu-baseline",
     "python3 bench.py --summarize-profiles gpurun_out/prof",
 ]
 
@@ -322,12 +322,127 @@ def cpu_baseline(wl, budget_s=20.0):
     }
 
 
+def time_workload(wid, steps, warmup, dev):
+    """Whole muon_step calls on one workload, inputs resident in HBM: wall time
+    between two device synchronizations, and per-kernel time from the library's
+    HIP events recorded on the launch stream."""
+    import torch
+    import matrix_aware_optimizer_amd as mao
+    import workloads as wk
+    wl = wk.WORKLOADS[wid]
+    hp = wl.hp
+    print(f"# workload {wid}: generating {wl.n} matrices on the device ({wl.name})", file=sys.stderr, flush=True)
+    W, G, M = [], [], []
+    for i in range(wl.n):
+        d = wk.device_matrix(wl, i, dev)
+        W.append(d["W"]); G.append(d["G"]); M.append(d["M"])
+    torch.cuda.synchronize()
+    kw = dict(lr=hp["lr"], beta=hp["beta"], weight_decay=hp["weight_decay"], schedule=hp["schedule"],
+              scale_rule=hp["scale_rule"], eps=hp["eps"])
+    ws = mao.allocate_workspace(mao.muon_workspace_bytes(W, G, M, **kw), dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        mao.muon_step(W, G, M, workspace=ws, stream=stream, **kw)
+    torch.cuda.synchronize()
+    print(f"# workload {wid}: warmup done, timing {steps} steps", file=sys.stderr, flush=True)
+    mao.muon_profile_enable(True)
+    mao.muon_profile_read()          # reset counters
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        mao.muon_step(W, G, M, workspace=ws, stream=stream, **kw)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = mao.muon_profile_read()
+    mao.muon_profile_enable(False)
+    del W, G, M, ws
+    torch.cuda.empty_cache()
+
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    steps_ns = len(hp["schedule"])
+    flops_ns = ns_flops(wl.shapes, steps_ns)
+    ns_ms = (prof["gram"]["ms"] + prof["poly"]["ms"] + prof["update"]["ms"] + prof["update_apply"]["ms"]) / steps
+    # the roofline kernel: the update launches that write the iterate (all but the
+    # last of a step, whose kernel also applies the step to W and is timed apart)
+    upd = prof["update"] if prof["update"]["launches"] else prof["update_apply"]
+    upd_ms = upd["ms"] / max(1, upd["launches"])
+    upd_tflops = update_flops_per_launch(wl.shapes) / (upd_ms * 1e-3) / 1e12
+    bf16 = wl.dtype == "bf16"
+    peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
+    elem = sum(r * c for r, c in wl.shapes)
+    es = 2 if bf16 else 4
+    k1_ms = prof["momentum_norm"]["ms"] / max(1, prof["momentum_norm"]["launches"])
+    # muon_step's apply runs inside its last update launch; a separate apply launch
+    # only happens for muon_ns and for ns_steps = 0
+    k5_ms = prof["apply"]["ms"] / prof["apply"]["launches"] if prof["apply"]["launches"] else None
+    gram_ms = prof["gram"]["ms"] / max(1, prof["gram"]["launches"])
+    poly_ms = prof["poly"]["ms"] / max(1, prof["poly"]["launches"])
+    gram_fl = sum(min(r, c) ** 2 * max(r, c) for r, c in wl.shapes)
+    poly_fl = sum(min(r, c) ** 3 for r, c in wl.shapes)
+    return {
+        "wl": wl,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "matrices_per_s": wl.n / (ms_per_step * 1e-3),
+        "ns_steps": steps_ns,
+        "flops_ns": flops_ns,
+        "ns_ms": ns_ms,
+        "peak": peak,
+        "prof": prof,
+        "upd": upd,
+        "upd_ms": upd_ms,
+        "upd_tflops": upd_tflops,
+        "gram_ms": gram_ms,
+        "gram_tflops": gram_fl / (gram_ms * 1e-3) / 1e12,
+        "poly_ms": poly_ms,
+        "poly_tflops": poly_fl / (poly_ms * 1e-3) / 1e12,
+        "elem": elem,
+        "es": es,
+        "k1_ms": k1_ms,
+        "k5_ms": k5_ms,
+    }
+
+
+def workload_summary(r):
+    """The per-workload object of the bench line."""
+    ns_tf = r["flops_ns"] / (r["ns_ms"] * 1e-3) / 1e12
+    return {
+        "workload": r["wl"].name,
+        "dtype": r["wl"].dtype,
+        "matrices": r["wl"].n,
+        "ns_steps": r["ns_steps"],
+        "steps_timed": r["steps"],
+        "ms_per_step": round(r["ms_per_step"], 4),
+        "matrices_per_s": round(r["matrices_per_s"], 2),
+        "ns_ms_per_step": round(r["ns_ms"], 4),
+        "ns_tflops_algorithmic": round(ns_tf, 2),
+        "ns_frac_of_peak": round(ns_tf / r["peak"], 4),
+        "peak_tflops": r["peak"],
+        "update_frac_of_peak": round(r["upd_tflops"] / r["peak"], 4),
+        "gram_frac_of_peak": round(r["gram_tflops"] / r["peak"], 4),
+        "poly_frac_of_peak": round(r["poly_tflops"] / r["peak"], 4),
+        "momentum_norm_gbs": round(3 * r["es"] * r["elem"] / (r["k1_ms"] * 1e-3) / 1e9, 1),
+    }
+
+
+# The pages' own figure for the method, with no hardware stated: context, not a target.
+PAGES_CONTEXT = {
+    "figure": "Muon reaches AdamW's loss with about 52% of AdamW's training FLOPs (16B-parameter MoE, 5.7T tokens)",
+    "source": "[DeepSeek V4 summary] prism.simon-ai.net/article/8795, section on Muon's training efficiency",
+    "hardware": "not stated",
+    "role": "context only; not comparable with a per-step throughput",
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", type=int, default=3, help="workload id (1-5)")
+    ap.add_argument("--workload", type=int, default=3, help="workload id (1-5) of the headline line")
+    ap.add_argument("--only", action="store_true", help="time the headline workload only (no other workloads, "
+                    "no AdamW / Cayley rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -355,64 +470,19 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     mao.load()
-    wl = wk.WORKLOADS[args.workload]
+    r = time_workload(args.workload, args.steps, args.warmup, dev)
+    wl = r["wl"]
     hp = wl.hp
-
-    print(f"# generating {wl.n} matrices on the device ({wl.name})", file=sys.stderr, flush=True)
-    W, G, M = [], [], []
-    for i in range(wl.n):
-        d = wk.device_matrix(wl, i, dev)
-        W.append(d["W"]); G.append(d["G"]); M.append(d["M"])
-    torch.cuda.synchronize()
-    kw = dict(lr=hp["lr"], beta=hp["beta"], weight_decay=hp["weight_decay"], schedule=hp["schedule"],
-              scale_rule=hp["scale_rule"], eps=hp["eps"])
-    need = mao.muon_workspace_bytes(W, G, M, **kw)
-    ws = mao.allocate_workspace(need, dev)
-    stream = torch.cuda.current_stream()
-
-    for _ in range(args.warmup):
-        mao.muon_step(W, G, M, workspace=ws, stream=stream, **kw)
-    torch.cuda.synchronize()
-    print(f"# warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
-
-    mao.muon_profile_enable(True)
-    mao.muon_profile_read()          # reset counters
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        mao.muon_step(W, G, M, workspace=ws, stream=stream, **kw)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    prof = mao.muon_profile_read()
-    mao.muon_profile_enable(False)
-
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    steps_ns = len(hp["schedule"])
-    flops_ns = ns_flops(wl.shapes, steps_ns)
-    ns_ms = (prof["gram"]["ms"] + prof["poly"]["ms"] + prof["update"]["ms"] + prof["update_apply"]["ms"]) / args.steps
-    # the roofline kernel: the update launches that write the iterate (all but the
-    # last of a step, whose kernel also applies the step to W and is timed apart)
-    upd = prof["update"] if prof["update"]["launches"] else prof["update_apply"]
-    upd_ms = upd["ms"] / max(1, upd["launches"])
-    upd_tflops = update_flops_per_launch(wl.shapes) / (upd_ms * 1e-3) / 1e12
-    bf16 = wl.dtype == "bf16"
-    peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
-
-    elem = sum(r * c for r, c in wl.shapes)
-    es = 2 if bf16 else 4
-    k1_ms = prof["momentum_norm"]["ms"] / max(1, prof["momentum_norm"]["launches"])
-    # muon_step's apply runs inside its last update launch; a separate apply launch
-    # only happens for muon_ns and for ns_steps = 0
-    k5_ms = prof["apply"]["ms"] / prof["apply"]["launches"] if prof["apply"]["launches"] else None
-
+    prof = r["prof"]
+    peak = r["peak"]
     out = {
         "metric": "Muon step matrices/s and NS TFLOP/s as % of MI355X bf16 MFMA peak",
-        "value": round(wl.n / (ms_per_step * 1e-3), 3),
+        "value": round(r["matrices_per_s"], 3),
         "unit": "matrices/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(r["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -421,35 +491,48 @@ def main():
         "config": {
             "workload": wl.name,
             "matrices": wl.n,
-            "ns_steps": steps_ns,
-            "schedule": "8 fast + 2 stable" if args.workload == 3 else f"{steps_ns} fast",
+            "ns_steps": r["ns_steps"],
+            "schedule": "8 fast + 2 stable" if args.workload == 3 else f"{r['ns_steps']} fast",
             "scale_rule": hp["scale_rule"],
         },
-        "ns_tflops_algorithmic": round(flops_ns / (ns_ms * 1e-3) / 1e12, 2),
-        "ns_frac_of_peak": round(flops_ns / (ns_ms * 1e-3) / 1e12 / peak, 4),
-        "ns_ms_per_step": round(ns_ms, 4),
-        "step_tflops_algorithmic": round(flops_ns / (ms_per_step * 1e-3) / 1e12, 2),
+        "ns_tflops_algorithmic": round(r["flops_ns"] / (r["ns_ms"] * 1e-3) / 1e12, 2),
+        "ns_frac_of_peak": round(r["flops_ns"] / (r["ns_ms"] * 1e-3) / 1e12 / peak, 4),
+        "ns_ms_per_step": round(r["ns_ms"], 4),
+        "step_tflops_algorithmic": round(r["flops_ns"] / (r["ms_per_step"] * 1e-3) / 1e12, 2),
         "kernel_ms_per_step": {k: round(v["ms"] / args.steps, 4) for k, v in prof.items()},
         "elementwise_gbs": {
-            "momentum_norm": round(3 * es * elem / (k1_ms * 1e-3) / 1e9, 1),
-            "apply": round((2 * es + 4) * elem / (k5_ms * 1e-3) / 1e9, 1) if k5_ms else "fused into the last update",
+            "momentum_norm": round(3 * r["es"] * r["elem"] / (r["k1_ms"] * 1e-3) / 1e9, 1),
+            "apply": round((2 * r["es"] + 4) * r["elem"] / (r["k5_ms"] * 1e-3) / 1e9, 1) if r["k5_ms"]
+            else "fused into the last update",
         },
         "roofline": {
             "kernel": "update (X <- aX + BX)",
             "bound": "mfma",
-            "achieved": round(upd_tflops, 2),
+            "achieved": round(r["upd_tflops"], 2),
             "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(upd_tflops / peak, 4),
+            "frac": round(r["upd_tflops"] / peak, 4),
             "traffic": measured_traffic(args.workload),
-            "avg_launch_ms": round(upd_ms, 4),
-            "launches_per_step": round(upd["launches"] / args.steps, 2),
+            "avg_launch_ms": round(r["upd_ms"], 4),
+            "launches_per_step": round(r["upd"]["launches"] / args.steps, 2),
             "flops_per_launch": update_flops_per_launch(wl.shapes),
         },
+        "pages_context": PAGES_CONTEXT,
     }
-    # the other rows of the optimizer step, timed after the headline region
-    out["adamw"] = measure_adamw(dev, 10)
-    out["cayley"] = measure_cayley(dev, 5)
+    if not args.only:
+        # the other workloads (parity cases of the same path), fewer steps each
+        others = {}
+        plan = {1: (50, 5), 2: (10, 2), 3: (args.steps, args.warmup), 4: (10, 2), 5: (3, 1)}
+        for wid in (1, 2, 3, 4, 5):
+            if wid == args.workload:
+                others[str(wid)] = workload_summary(r)
+                continue
+            st, wu = plan[wid]
+            others[str(wid)] = workload_summary(time_workload(wid, st, wu, dev))
+        out["workloads"] = others
+        # the other rows of the optimizer step, timed after the headline region
+        out["adamw"] = measure_adamw(dev, 10)
+        out["cayley"] = measure_cayley(dev, 5)
 
     if not args.no_cpu_baseline:
         print("# timing the fp64 oracle on a sample", file=sys.stderr, flush=True)

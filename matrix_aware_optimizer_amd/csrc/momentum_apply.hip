@@ -68,13 +68,13 @@ __device__ __forceinline__ int ew_col() { return (threadIdx.x & 7) * EW_GROUP; }
 
 // Deterministic block sum (fixed shuffle pattern, fixed wave order).
 // LDS barriers only: the tile's global stores stay in flight across them.
-__device__ inline float block_sum_256(float v, float* red) {
+__device__ inline double block_sum_256(double v, double* red) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) red[wave] = v;
     lds_barrier();
-    float total = ((red[0] + red[1]) + (red[2] + red[3]));
+    double total = ((red[0] + red[1]) + (red[2] + red[3]));
     lds_barrier();
     return total;
 }
@@ -139,7 +139,7 @@ __device__ __forceinline__ void momentum_group(const MatDesc& d, float beta, int
 template <typename T, bool NS_ONLY>
 __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) {
     __shared__ float tile[EW_TILE][EW_TILE + 1];
-    __shared__ float red[4];
+    __shared__ double red[4];
     const int t0 = blockIdx.x * args.tiles_per_block;
     const int t1 = min(args.total, t0 + args.tiles_per_block);
     if (t0 >= t1) return;
@@ -174,12 +174,16 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
                 for (int e = 0; e < EW_GROUP; ++e) u[p][e] = tile[ew_row(p)][jl + e];
         }
 
-        // ---- NS-frame rows: X32 (and the bf16 operand copy)
-        float sq = 0.0f;
+        // ---- NS-frame rows: X32 (and the bf16 operand copy).  The squares are
+        // summed in fp64: any fp32 value squares without overflow or underflow.
+        double sq = 0.0;
 #pragma unroll
         for (int p = 0; p < EW_PASSES; ++p) {
 #pragma unroll
-            for (int e = 0; e < EW_GROUP; ++e) sq = fmaf(u[p][e], u[p][e], sq);
+            for (int e = 0; e < EW_GROUP; ++e) {
+                const double v = static_cast<double>(u[p][e]);
+                sq = fma(v, v, sq);
+            }
             const size_t idx = static_cast<size_t>(i0 + ew_row(p)) * d.np + (j0 + jl);
             if (sizeof(T) == 2) {
                 // the iterate as the pair hi + lo: hi = bf16(U), lo = bf16(U - hi)
@@ -196,21 +200,26 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
                 store8<float>(d.x32[0], idx, u[p]);
             }
         }
-        const float total = block_sum_256(sq, red);   // also orders LDS reuse
+        const double total = block_sum_256(sq, red);   // also orders LDS reuse
         if (threadIdx.x == 0) G(args.partials)[t] = total;
     }
 }
 
 // ----------------------------------------------------------------------------
 // Norm finalize: one block per matrix sums its tile partials in a fixed order
-// (fp64) and stores s = 1 / (||U||_F + eps).
+// (fp64) and stores s = 1 / (||U||_F + eps).  When the norm lies outside
+// [2^-NS_SHIFT_LIMIT, 2^NS_SHIFT_LIMIT] the stored iterate is shifted by an
+// exact power of two E (rescale_kernel) so that its norm is in [1/2, 1):
+// X0 = U / (nu + eps) = U' / (nu' + eps 2^-E) with U' = 2^-E U, nu' = 2^-E nu.
+// The Newton-Schulz products then neither overflow (huge inputs) nor lose
+// their entries to underflow (tiny inputs, or eps = 0).
 // ----------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* descs, const float* partials,
+__global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* descs, const double* partials,
                                                             float eps) {
     __shared__ double red[256];
     const MatDesc& d = descs[blockIdx.x];
     double acc = 0.0;
-    for (int i = threadIdx.x; i < d.ew_tiles; i += 256) acc += static_cast<double>(partials[d.ew_tile0 + i]);
+    for (int i = threadIdx.x; i < d.ew_tiles; i += 256) acc += partials[d.ew_tile0 + i];
     red[threadIdx.x] = acc;
     __syncthreads();
     for (int off = 128; off > 0; off >>= 1) {
@@ -219,8 +228,65 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* descs
     }
     if (threadIdx.x == 0) {
         const double nrm = sqrt(red[0]);
-        G(d.scal)[0] = static_cast<float>(1.0 / (nrm + static_cast<double>(eps)));
+        int e = 0;
+        const double lim = static_cast<double>(1ull << NS_SHIFT_LIMIT);
+        if (nrm > lim || (nrm > 0.0 && nrm < 1.0 / lim)) (void)frexp(nrm, &e);   // nrm = f 2^e, f in [1/2, 1)
+        const double s = 1.0 / (ldexp(nrm, -e) + ldexp(static_cast<double>(eps), -e));
+        G(d.scal)[0] = static_cast<float>(s);
         G(d.scal)[1] = static_cast<float>(nrm);
+        G(d.scal)[2] = static_cast<float>(e);
+    }
+}
+
+// ----------------------------------------------------------------------------
+// Rescale: U' = 2^-E U for the matrices whose shift E is not zero (ldexp is
+// exact; hi' = 2^-E hi and lo' = 2^-E lo stay the bf16 pair of U').  Blocks
+// skip every matrix with E = 0 after one scalar read, so in the common case
+// the launch does no memory traffic beyond that.
+// ----------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(EW_THREADS) void rescale_kernel(EwArgs args) {
+    const int t0 = blockIdx.x * args.tiles_per_block;
+    const int t1 = min(args.total, t0 + args.tiles_per_block);
+    if (t0 >= t1) return;
+    int mi = find_matrix(args.prefix, args.nmat, t0);
+    const int jl = ew_col();
+    int t = t0;
+    while (t < t1) {
+        while (t >= args.prefix[mi + 1]) ++mi;
+        const MatDesc d = args.descs[mi];
+        const int e = static_cast<int>(G(d.scal)[2]);
+        if (e == 0) {   // nothing to do for this matrix: jump past its tiles
+            t = args.prefix[mi + 1];
+            continue;
+        }
+        const int tend = min(t1, args.prefix[mi + 1]);
+        for (; t < tend; ++t) {
+            int i0, j0;
+            ew_tile_origin(d, t - args.prefix[mi], i0, j0);
+#pragma unroll
+            for (int p = 0; p < EW_PASSES; ++p) {
+                const size_t idx = static_cast<size_t>(i0 + ew_row(p)) * d.np + (j0 + jl);
+                if (sizeof(T) == 2) {
+                    float h[EW_GROUP], l[EW_GROUP];
+                    load8<uint16_t>(d.xop[0], idx, h);
+                    load8<uint16_t>(d.xlo, idx, l);
+#pragma unroll
+                    for (int k = 0; k < EW_GROUP; ++k) {
+                        h[k] = ldexpf(h[k], -e);
+                        l[k] = ldexpf(l[k], -e);
+                    }
+                    store8<uint16_t>(d.xop[0], idx, h);
+                    store8<uint16_t>(d.xlo, idx, l);
+                } else {
+                    float x[EW_GROUP];
+                    load8<float>(d.x32[0], idx, x);
+#pragma unroll
+                    for (int k = 0; k < EW_GROUP; ++k) x[k] = ldexpf(x[k], -e);
+                    store8<float>(d.x32[0], idx, x);
+                }
+            }
+        }
     }
 }
 
@@ -327,8 +393,14 @@ hipError_t launch_momentum_norm(int dtype, bool ns_only, const EwArgs& args, int
     return hipGetLastError();
 }
 
-hipError_t launch_norm_finalize(const MatDesc* descs, const float* partials, int nmat, float eps, hipStream_t s) {
+hipError_t launch_norm_finalize(const MatDesc* descs, const double* partials, int nmat, float eps, hipStream_t s) {
     hipLaunchKernelGGL(norm_finalize_kernel, dim3(nmat), dim3(256), 0, s, descs, partials, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_rescale(int dtype, const EwArgs& args, int grid, hipStream_t s) {
+    if (dtype == DT_BF16) hipLaunchKernelGGL((rescale_kernel<uint16_t>), dim3(grid), dim3(EW_THREADS), 0, s, args);
+    else hipLaunchKernelGGL((rescale_kernel<float>), dim3(grid), dim3(EW_THREADS), 0, s, args);
     return hipGetLastError();
 }
 

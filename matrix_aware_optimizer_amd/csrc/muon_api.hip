@@ -159,7 +159,7 @@ muon_status build_plan(std::vector<Item>& items, const muon_hparams* hp, bool ns
     off = align_up(off + sizeof(int32_t) * 3 * (nmat + 1), ALIGN);
     pl.header_bytes = off;                       // uploaded from the host
     pl.off_scal = off;
-    off = align_up(off + sizeof(float) * 2 * nmat, ALIGN);
+    off = align_up(off + sizeof(float) * NS_SCAL * nmat, ALIGN);
 
     int64_t ew = 0, sym = 0, upd = 0;
     for (int k = 0; k < nmat; ++k) {
@@ -207,13 +207,13 @@ muon_status build_plan(std::vector<Item>& items, const muon_hparams* hp, bool ns
             d.apply_coef = static_cast<float>(lr * static_cast<double>(scale_rule_value(hp->scale_rule, it.rows, it.cols)));
             d.decay = static_cast<float>(1.0 - lr * wd);
         }
-        d.scal = reinterpret_cast<float*>(pl.off_scal + sizeof(float) * 2 * k);
+        d.scal = reinterpret_cast<float*>(pl.off_scal + sizeof(float) * NS_SCAL * k);
     }
     pl.total_ew = ew;
     pl.total_sym = sym;
     pl.total_upd = upd;
     pl.off_partials = off;
-    off = align_up(off + sizeof(float) * ew, ALIGN);
+    off = align_up(off + sizeof(double) * ew, ALIGN);
 
     for (int k = 0; k < nmat; ++k) {
         MatDesc& d = pl.descs[k];
@@ -430,7 +430,7 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
 
     const MatDesc* d_descs = reinterpret_cast<const MatDesc*>(base + pl.off_descs);
     const int32_t* d_pre = reinterpret_cast<const int32_t*>(base + pl.off_prefix);
-    float* d_partials = reinterpret_cast<float*>(base + pl.off_partials);
+    double* d_partials = reinterpret_cast<double*>(base + pl.off_partials);
 
     EwArgs ew{};
     ew.descs = d_descs;
@@ -450,6 +450,10 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
     st = timed_launch(0, stream, "momentum/norm kernel", [&] { return launch_momentum_norm(dtype, ns_only, ew, ew_grid, stream); });
     if (st != MUON_OK) return st;
     st = timed_launch(1, stream, "norm finalize kernel", [&] { return launch_norm_finalize(d_descs, d_partials, nmat, hp->eps, stream); });
+    if (st != MUON_OK) return st;
+    // shifts the stored iterate of the (rare) matrices whose norm is outside the plain range;
+    // its workgroups leave at once for every other matrix
+    st = timed_launch(1, stream, "rescale kernel", [&] { return launch_rescale(dtype, ew, ew_grid, stream); });
     if (st != MUON_OK) return st;
 
     NsArgs na{};

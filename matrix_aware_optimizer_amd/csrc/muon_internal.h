@@ -46,7 +46,12 @@ struct MatDesc {
     uint16_t* xlo;      // bf16 only, updated in place
     void* amat;         // mp x mp, A = X X^T (symmetric, stored in full)
     void* bmat;         // mp x mp, B = b A + c A A (symmetric, stored in full)
-    float* scal;        // [0] = 1 / (||U||_F + eps), [1] = ||U||_F
+    // Normalization scalars, NS_SCAL floats per matrix:
+    //   [0] s = 1 / (nu' + eps 2^-E), the scale of X0 = s U' with U' = 2^-E U
+    //   [1] nu = ||U||_F (fp32, saturating)
+    //   [2] E, the exact power-of-two shift applied to the stored iterate (0
+    //       unless nu lies outside [2^-NS_SHIFT_LIMIT, 2^NS_SHIFT_LIMIT])
+    float* scal;
     float apply_coef;   // lr * scale_rule(rows, cols)
     float decay;        // 1 - lr * weight_decay
     int32_t ew_tile0, ew_tiles;    // elementwise tiles: first global index, count
@@ -54,10 +59,17 @@ struct MatDesc {
     int32_t upd_tile0, upd_tiles;  // update tiles
 };
 
+// Scalars kept per matrix for the normalization (see MatDesc::scal), and the
+// norm range in which the iterate is stored unshifted.  Inside it the first
+// step's Gram products s^2 U U^T stay far from fp32 overflow (nu^2 <= 2^96)
+// and their entries far from underflow.
+constexpr int NS_SCAL = 4;
+constexpr int NS_SHIFT_LIMIT = 48;
+
 struct EwArgs {
     const MatDesc* descs;
     const int32_t* prefix;   // nmat + 1 exclusive prefix sums of ew_tiles
-    float* partials;         // one sum of squares per elementwise tile
+    double* partials;        // one sum of squares per elementwise tile (fp64)
     int32_t nmat;
     int32_t total;
     int32_t tiles_per_block;
@@ -156,8 +168,9 @@ constexpr int CY_PHASES = 14;
 hipError_t launch_cayley(int phase, const CayleyArgs& args, hipStream_t s);
 hipError_t launch_adamw(int dtype, const AdamWArgs& args, int grid, hipStream_t s);
 hipError_t launch_momentum_norm(int dtype, bool ns_only, const EwArgs& args, int grid, hipStream_t s);
-hipError_t launch_norm_finalize(const MatDesc* descs, const float* partials, int nmat, float eps,
+hipError_t launch_norm_finalize(const MatDesc* descs, const double* partials, int nmat, float eps,
                                 hipStream_t s);
+hipError_t launch_rescale(int dtype, const EwArgs& args, int grid, hipStream_t s);
 hipError_t launch_apply(int dtype, bool ns_only, const EwArgs& args, int grid, hipStream_t s);
 hipError_t launch_gram(int dtype, const NsArgs& args, hipStream_t s);
 hipError_t launch_poly(int dtype, const NsArgs& args, hipStream_t s);

@@ -44,3 +44,24 @@ def singular_values(x):
 def to_numpy_f32(t):
     import torch
     return t.detach().to(device="cpu", dtype=torch.float32).numpy()
+
+
+def record_parity(**fields):
+    """Append one parity record (a JSON line) to the file named by the
+    MUON_PARITY_LOG environment variable, if it is set.  The records are the
+    margins of the GPU parity checks (O error, singular-value range against
+    the band, M' and W' ulps); tests/parity_summary.py tabulates them."""
+    import json
+    import os
+    path = os.environ.get("MUON_PARITY_LOG")
+    if not path:
+        return
+    clean = {}
+    for k, v in fields.items():
+        if isinstance(v, (np.floating, np.integer)):
+            v = v.item()
+        elif isinstance(v, tuple):
+            v = list(v)
+        clean[k] = v
+    with open(path, "a") as fh:
+        fh.write(json.dumps(clean) + "\n")

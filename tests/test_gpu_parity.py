@@ -23,7 +23,7 @@ import torch
 
 import oracle as orc
 import workloads as wk
-from tests._util import rel_frob, singular_values, to_numpy_f32, ulp_distance
+from tests._util import record_parity, rel_frob, singular_values, to_numpy_f32, ulp_distance
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +49,7 @@ def _check_band(o_gpu, o_ref, tag):
     s_gpu = singular_values(o_gpu)
     lo, hi = s_ref.min() - 0.05, s_ref.max() + 0.05
     assert s_gpu.min() >= lo and s_gpu.max() <= hi, (tag, s_gpu.min(), s_gpu.max(), lo, hi)
+    return (float(s_gpu.min()), float(s_gpu.max())), (float(lo), float(hi))
 
 
 # ----------------------------------------------------------------------------
@@ -154,6 +155,56 @@ def test_scale_invariance_across_expert_scales(gpu_lib):
         assert rel_frob(g, got[0]) <= 2e-2
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_extreme_magnitudes_against_oracle(gpu_lib, dtype):
+    """Scale invariance against the oracle itself, over the storage dtype's range.
+
+    From c = 1e-30 (where eps dominates the norm and the iteration acts almost
+    linearly) to c = 1e18 (squares near fp32's limit; 1e30 for fp32 inputs):
+    the library shifts the stored iterate by an exact power of two when the norm
+    is outside its plain range, so no product overflows or underflows."""
+    rng = np.random.default_rng(9)
+    base = rng.standard_normal((384, 640))
+    scales = (1e-30, 1e-10, 1e-3, 1e10, 1e15, 1e18) + ((1e30,) if dtype == "f32" else ())
+    if dtype == "bf16":
+        mats = [wk.to_bf16_bits_f32((base * c).astype(np.float32)) for c in scales]
+    else:
+        mats = [(base * c).astype(np.float32) for c in scales]
+    got = _ns_gpu(gpu_lib, mats, dtype, KJ5)
+    for c, m, g in zip(scales, mats, got):
+        ref = orc.muon_ns(m, KJ5)
+        err = rel_frob(g, ref)
+        _say(f"scale {c:.0e} {dtype}: O rel err {err:.3e}")
+        assert np.all(np.isfinite(g)), c
+        assert err <= TOL[dtype] + (2e-7 if dtype == "f32" else 0.0), (c, err)
+        if dtype == "bf16":
+            _check_band(g, ref, c)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_eps_tiny_input(gpu_lib, dtype):
+    # eps = 0: X0 = U / ||U||_F exactly, for norms far below fp32's squared range
+    rng = np.random.default_rng(10)
+    base = rng.standard_normal((200, 300))
+    mats = [(base * c).astype(np.float32) for c in (1e-25, 1e-3, 1e25)]
+    if dtype == "bf16":
+        mats = [wk.to_bf16_bits_f32(m) for m in mats]
+    got = _ns_gpu(gpu_lib, mats, dtype, KJ5, eps=0.0)
+    for m, g in zip(mats, got):
+        ref = orc.muon_ns(m, KJ5, eps=0.0)
+        assert np.all(np.isfinite(g))
+        assert rel_frob(g, ref) <= TOL[dtype] + (2e-7 if dtype == "f32" else 0.0)
+
+
+def test_step_with_huge_gradients(gpu_lib):
+    # the whole step (momentum in bf16 at 1e18, state rounding, the shifted
+    # iterate, decay and apply) against the oracle
+    wl = wk.custom_workload([(256, 384), (384, 256)], dtype="bf16", wid=213, grad_std=1e18,
+                            lr=3e-4, weight_decay=0.01, scale_rule="moonlight")
+    host = [wk.host_matrix(wl, i) for i in range(2)]
+    _check_step(gpu_lib, wl, [0, 1], host)
+
+
 def test_deterministic_bitwise(gpu_lib):
     wl = wk.custom_workload([(300, 517), (517, 300), (256, 1024)], dtype="bf16", wid=206)
     mats = [wk.host_matrix(wl, i, need=("G",))["G"] for i in range(3)]
@@ -190,7 +241,7 @@ def _oracle_step(h, dtype, hp, zero_w=False, lr=None):
                          dtype=dtype)
 
 
-def _check_step(mao, wl, indices, host):
+def _check_step(mao, wl, indices, host, label=None):
     """Full step on all of `host` (one grouped call); oracle checks on `indices`."""
     dtype, hp = wl.dtype, wl.hp
     # pass 1: real weights -> M' and W'
@@ -210,12 +261,16 @@ def _check_step(mao, wl, indices, host):
         err = rel_frob(o_gpu, ref["O"])
         tol = TOL[dtype] if dtype == "bf16" else TOL[dtype] + 2e-7
         assert err <= tol, (i, (rows, cols), "O", err)
+        sig = band = None
         if dtype == "bf16" and min(rows, cols) > 1:
-            _check_band(o_gpu, ref["O"], i)
+            sig, band = _check_band(o_gpu, ref["O"], i)
+        rec = dict(config=label or wl.name, matrix=int(i), shape=(rows, cols), dtype=dtype, o_rel_err=err,
+                   tol=tol, sigma=sig, band=band, m_ulp_max=int(du.max()))
         # W'
         if dtype == "f32":
             e = rel_frob(Wg[i], ref["W"])
             assert e <= 1e-6, (i, "W'", e)
+            record_parity(**rec, w_rel_err=e)
         else:
             du = ulp_distance(Wg[i], ref["W_rounded"], dtype)
             lr32 = orc.as_f32(hp["lr"])
@@ -228,13 +283,14 @@ def _check_step(mao, wl, indices, host):
             exact = slack < 0.25 * ulp
             assert np.all(du[exact] <= 1), (i, "W' ulp", int(du[exact].max()))
             assert exact.any()
+            record_parity(**rec, w_ulp_max=int(du.max()), w_ulp_max_where_o_negligible=int(du[exact].max()))
 
 
 def test_step_fp32_single_matrix_workload(gpu_lib):
     wl = wk.WORKLOADS[1]
     host = [wk.host_matrix(wl, 0)]
     _say("step fp32 128x256")
-    _check_step(gpu_lib, wl, [0], host)
+    _check_step(gpu_lib, wl, [0], host, label="c1 single fp32 128x256")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -324,10 +380,10 @@ def test_full_single_4096_lowrank(gpu_lib):
     wl = wk.WORKLOADS[2]
     host = [wk.host_matrix(wl, 0)]
     _say("full 4096^2 low-rank")
-    _check_step(gpu_lib, wl, [0], host)
+    _check_step(gpu_lib, wl, [0], host, label="c2 single bf16 4096^2 low rank")
 
 
-def _full_workload_check(mao, wl, sample):
+def _full_workload_check(mao, wl, sample, label):
     """The whole workload in one grouped call (as the benchmark runs it);
     oracle checks on the host-drawn `sample` matrices."""
     dtype, hp = wl.dtype, wl.hp
@@ -362,121 +418,137 @@ def _full_workload_check(mao, wl, sample):
         h = host[i]
         ref = _oracle_step(h, dtype, hp)
         s = ref["scale"]
-        assert ulp_distance(Mg[i], ref["M_rounded"], dtype).max() <= 1, (i, "M'")
+        mu = ulp_distance(Mg[i], ref["M_rounded"], dtype).max()
+        assert mu <= 1, (i, "M'")
         o_gpu = -Wo[i].astype(np.float64) / s
         err = rel_frob(o_gpu, ref["O"])
         _say(f"matrix {i} {wl.shapes[i]}: O rel err {err:.3e}")
         assert err <= TOL[dtype], (i, err)
-        _check_band(o_gpu, ref["O"], i)
+        sig, band = _check_band(o_gpu, ref["O"], i)
         lr32 = orc.as_f32(hp["lr"])
         slack = lr32 * s * (np.abs(o_gpu - ref["O"]) + 0.01 * np.abs(ref["O"]))
         ulp = np.abs(ref["W_rounded"].astype(np.float64)) * 2.0 ** -7 + 2.0 ** -133
         assert np.all(np.abs(Wg[i].astype(np.float64) - ref["W"]) <= ulp + slack), (i, "W'")
+        wu = ulp_distance(Wg[i], ref["W_rounded"], dtype)
+        record_parity(config=label, matrix=int(i), shape=wl.shapes[i], dtype=dtype, o_rel_err=err, tol=TOL[dtype],
+                      sigma=sig, band=band, m_ulp_max=int(mu), w_ulp_max=int(wu.max()))
 
 
 def test_full_transformer_parameter_set(gpu_lib):
     wl = wk.WORKLOADS[3]
     _say("full transformer set, 144 matrices")
     # layer 0: Q (square), up (tall), down (wide); layer 23: down
-    _full_workload_check(gpu_lib, wl, [0, 4, 5, 143])
+    _full_workload_check(gpu_lib, wl, [0, 4, 5, 143], "c3 transformer d=2048 x 24 layers (144 matrices)")
 
 
 def test_full_moe_expert_set(gpu_lib):
     wl = wk.WORKLOADS[4]
     _say("full MoE set, 192 matrices")
     # expert 0 gate, expert 7 down, expert 63 up (different per-expert scales)
-    _full_workload_check(gpu_lib, wl, [0, 23, 190])
+    _full_workload_check(gpu_lib, wl, [0, 23, 190], "c4 MoE 64 experts (192 matrices)")
 
 
 def _gram_eigs(x):
-    """Eigenvalues (ascending, fp64) of x^T x for a tall device matrix x."""
-    xd = x.to(torch.float64)
+    """Eigenvalues (ascending, fp64) of x^T x for a tall matrix x (host array or
+    device tensor): the Gram is formed in fp64 on the device with torch, its
+    eigenvalues on the host in fp64."""
+    xd = (torch.from_numpy(np.ascontiguousarray(x)).to(DEV) if isinstance(x, np.ndarray) else x).to(torch.float64)
     g = (xd.T @ xd).cpu().numpy()
     del xd
     return np.linalg.eigvalsh(g)
 
 
-def test_full_large_mlp_set(gpu_lib):
-    """16 x 28672x8192 in one grouped call.  The oracle cannot run the iteration
-    at this size inside a test, so it checks what it computes at any size:
-      * M' at sampled positions, to 1 ulp of the once-rounded oracle value;
-      * W' at sampled positions against the oracle's apply with the observed O;
-      * the singular values of O: in exact arithmetic the iteration maps each
-        singular value x of M' / (||M'||_F + eps) through the schedule's odd
-        polynomials (oracle ``phi_schedule``), so sigma(O) must lie inside
-        [min - 0.05, max + 0.05] of that map, and the sorted spectra must agree
-        to 0.05 (the bf16 band).
-    The two 8192 x 8192 Gram matrices are formed in fp64 with torch on the
-    device; their eigenvalues are taken on the host in fp64."""
+LARGE_SAMPLE = (0, 15)
+
+
+@pytest.fixture(scope="module")
+def large_mlp_run(gpu_lib):
+    """16 x 28672x8192 in one grouped call, as the benchmark launches it.
+    Matrices 0 and 15 are drawn on the host (the bits the oracle reads), the
+    other 14 on the device.  Two calls from the same state: real weights
+    (-> W', M'), then W = 0 and lr = 1, which gives W' = -s O rounded once."""
     wl = wk.WORKLOADS[5]
     hp = wl.hp
-    sample = 0
-    t0 = time.time()
-    _say("full large MLP set, 16 x 28672x8192: drawing inputs")
+    _say("large MLP set: host draws of matrices", LARGE_SAMPLE)
+    host = {i: wk.host_matrix(wl, i) for i in LARGE_SAMPLE}
     W, G, M = [], [], []
     for i in range(wl.n):
-        d = wk.device_matrix(wl, i, DEV)
-        W.append(d["W"]); G.append(d["G"]); M.append(d["M"])
-    W0 = W[sample].clone()
-    M0 = M[sample].clone()
+        if i in host:
+            W.append(wk.upload(host[i]["W"], "bf16", DEV))
+            G.append(wk.upload(host[i]["G"], "bf16", DEV))
+            M.append(wk.upload(host[i]["M"], "bf16", DEV))
+        else:
+            d = wk.device_matrix(wl, i, DEV)
+            W.append(d["W"]); G.append(d["G"]); M.append(d["M"])
+    M0 = {i: M[i].clone() for i in LARGE_SAMPLE}
     kw = dict(beta=hp["beta"], weight_decay=hp["weight_decay"], schedule=hp["schedule"],
               scale_rule=hp["scale_rule"], eps=hp["eps"])
     _say("step 1 (real weights)")
     ws = gpu_lib.muon_step(W, G, M, lr=hp["lr"], **kw)
     torch.cuda.synchronize()
-    rows, cols = wl.shapes[sample]
-    rng = np.random.default_rng(5)
-    pos = rng.choice(rows * cols, size=8192, replace=False)
-
-    def at(t):
-        return to_numpy_f32(t.reshape(-1)[torch.from_numpy(pos).to(DEV)]).astype(np.float64)
-
-    Wp, Mp = at(W[sample]), at(M[sample])
-    # second call from the same state: W = 0, lr = 1 gives W' = -s O
+    Wg = {i: to_numpy_f32(W[i]) for i in LARGE_SAMPLE}
+    Mg = {i: to_numpy_f32(M[i]) for i in LARGE_SAMPLE}
     for i in range(wl.n):
         W[i].zero_()
-    M[sample].copy_(M0)
+        if i in M0:
+            M[i].copy_(M0[i])   # the others start from zero momentum and are only timed here
     _say("step 2 (W = 0, lr = 1)")
     gpu_lib.muon_step(W, G, M, lr=1.0, workspace=ws, **kw)
     torch.cuda.synchronize()
-    del ws
-    s = orc.scale_factor(rows, cols, hp["scale_rule"])
-    O = W[sample].to(torch.float32) / (-s)
-    Gs = G[sample]
-    for i in range(wl.n):
-        if i != sample:
-            W[i] = G[i] = M[i] = None
+    Wo = {i: to_numpy_f32(W[i]) for i in LARGE_SAMPLE}
+    del W, G, M, M0, ws
     torch.cuda.empty_cache()
+    return {"wl": wl, "host": host, "Wg": Wg, "Mg": Mg, "Wo": Wo}
 
-    # M' at sampled positions
-    g_at, m0_at = at(Gs), at(M0)
-    m_ref = orc.rne(orc.momentum_update(m0_at, g_at, orc.as_f32(hp["beta"])), "bf16")
-    assert ulp_distance(Mp.astype(np.float32), m_ref, "bf16").max() <= 1
 
-    # W' at sampled positions: the oracle's apply with the observed O (itself
-    # rounded once to bf16 in the second call, hence the 2^-8 |O| slack)
-    o_at, w0_at = at(O), at(W0)
-    lr32, wd32 = orc.as_f32(hp["lr"]), orc.as_f32(hp["weight_decay"])
-    w_ref = orc.apply_update(w0_at, o_at, lr32, wd32, s)
-    ulp = np.abs(orc.rne(w_ref, "bf16").astype(np.float64)) * 2.0 ** -7 + 2.0 ** -133
-    slack = lr32 * s * np.abs(o_at) * 2.0 ** -8
-    assert np.all(np.abs(Wp - w_ref) <= ulp + slack)
-
-    # singular values: input through the oracle's scalar map vs the GPU's O
-    _say("spectra", f"{time.time() - t0:.1f}s")
-    # the iteration starts from the unrounded M' = beta M + G (exact in fp64 here)
-    M1 = orc.as_f32(hp["beta"]) * M0.to(torch.float64) + Gs.to(torch.float64)
-    ev_in = np.clip(_gram_eigs(M1), 0.0, None)
-    del M1
-    x = np.sqrt(ev_in) / (np.sqrt(ev_in.sum()) + hp["eps"])
-    s_exp = orc.phi_schedule(x, hp["schedule"])
-    s_gpu = np.sqrt(np.clip(_gram_eigs(O), 0.0, None))
-    lo, hi = s_exp.min() - 0.05, s_exp.max() + 0.05
-    dev = np.abs(np.sort(s_gpu) - np.sort(s_exp)).max()
-    _say(f"sigma(O) in [{s_gpu.min():.4f}, {s_gpu.max():.4f}], band [{lo:.4f}, {hi:.4f}], "
-         f"max sorted deviation {dev:.4f}, {time.time() - t0:.1f}s")
+@pytest.mark.parametrize("index", LARGE_SAMPLE)
+def test_full_large_mlp_set(gpu_lib, large_mlp_run, index):
+    """Matrix `index` of the 16 x 28672x8192 call against the fp64 oracle run in full:
+      * O: relative Frobenius error <= 3e-2 and every singular value inside the
+        band [min - 0.05, max + 0.05] of the oracle's;
+      * M' within 1 ulp of the once-rounded oracle value;
+      * W' within 1 ulp plus the share of O's own error;
+      * the singular values of O against the oracle's scalar map of the input's
+        (the iteration acts on each singular value through the schedule's odd
+        polynomials), sorted, to 0.05."""
+    wl, run = large_mlp_run["wl"], large_mlp_run
+    hp = wl.hp
+    h = run["host"][index]
+    t0 = time.time()
+    ref = _oracle_step(h, "bf16", hp)
+    _say(f"oracle for matrix {index}: {time.time() - t0:.1f}s")
+    s = ref["scale"]
+    mu = ulp_distance(run["Mg"][index], ref["M_rounded"], "bf16").max()
+    assert mu <= 1, (index, "M'", mu)
+    o_gpu = -run["Wo"][index].astype(np.float64) / s
+    err = rel_frob(o_gpu, ref["O"])
+    _say(f"matrix {index}: O rel err {err:.3e}")
+    assert err <= TOL["bf16"], (index, err)
+    lr32 = orc.as_f32(hp["lr"])
+    slack = lr32 * s * (np.abs(o_gpu - ref["O"]) + 0.01 * np.abs(ref["O"]))
+    ulp = np.abs(ref["W_rounded"].astype(np.float64)) * 2.0 ** -7 + 2.0 ** -133
+    assert np.all(np.abs(run["Wg"][index].astype(np.float64) - ref["W"]) <= ulp + slack), (index, "W'")
+    wu = int(ulp_distance(run["Wg"][index], ref["W_rounded"], "bf16").max())
+    o_ref = ref["O"]
+    m_new = ref["M"]
+    del ref
+    # singular values (tall: through the 8192 x 8192 Gram)
+    s_ref = np.sqrt(np.clip(_gram_eigs(o_ref), 0.0, None))
+    s_gpu = np.sqrt(np.clip(_gram_eigs(o_gpu), 0.0, None))
+    lo, hi = s_ref.min() - 0.05, s_ref.max() + 0.05
+    _say(f"sigma(O) in [{s_gpu.min():.4f}, {s_gpu.max():.4f}], oracle band [{lo:.4f}, {hi:.4f}]")
     assert s_gpu.min() >= lo and s_gpu.max() <= hi
-    assert dev <= 0.05
+    ev_in = np.clip(_gram_eigs(m_new), 0.0, None)
+    x = np.sqrt(ev_in) / (np.sqrt(ev_in.sum()) + orc.as_f32(hp["eps"]))
+    s_map = orc.phi_schedule(x, hp["schedule"])
+    dev_map = float(np.abs(np.sort(s_gpu) - np.sort(s_map)).max())
+    dev_ref = float(np.abs(np.sort(s_ref) - np.sort(s_map)).max())
+    _say(f"max sorted deviation from the scalar map: gpu {dev_map:.4f}, oracle {dev_ref:.2e}, "
+         f"{time.time() - t0:.1f}s")
+    assert dev_map <= 0.05
+    record_parity(config="c5 16 x 28672x8192 low rank", matrix=int(index), shape=wl.shapes[index], dtype="bf16",
+                  o_rel_err=err, tol=TOL["bf16"], sigma=(float(s_gpu.min()), float(s_gpu.max())),
+                  band=(float(lo), float(hi)), m_ulp_max=int(mu), w_ulp_max=wu, spectrum_dev=dev_map)
 
 
 def test_bf16_state_rounding_is_round_to_nearest_even(gpu_lib):

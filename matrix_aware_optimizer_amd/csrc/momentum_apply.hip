@@ -194,7 +194,9 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
                     h[k] = pack_bf16x2(a, b);
                     l[k] = pack_bf16x2(a - __uint_as_float(h[k] << 16), b - __uint_as_float(h[k] & 0xffff0000u));
                 }
-                G(reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(d.xop[0]) + idx))[0] = u32x4_t{h[0], h[1], h[2], h[3]};
+                // with hi_alias the caller's buffer already holds hi (the stored M', or the input)
+                if (!d.hi_alias)
+                    G(reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(d.xop[0]) + idx))[0] = u32x4_t{h[0], h[1], h[2], h[3]};
                 G(reinterpret_cast<u32x4_t*>(d.xlo + idx))[0] = u32x4_t{l[0], l[1], l[2], l[3]};
             } else {
                 store8<float>(d.x32[0], idx, u[p]);
@@ -242,7 +244,10 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* descs
 // Rescale: U' = 2^-E U for the matrices whose shift E is not zero (ldexp is
 // exact; hi' = 2^-E hi and lo' = 2^-E lo stay the bf16 pair of U').  Blocks
 // skip every matrix with E = 0 after one scalar read, so in the common case
-// the launch does no memory traffic beyond that.
+// the launch does no memory traffic beyond that.  A matrix whose hi is the
+// caller's buffer (hi_alias) gets its shifted hi in the workspace copy xop[0],
+// and its first-step operand pointer hi0 is redirected there (every block of
+// the matrix stores the same value; the GEMM launches that read it come later).
 // ----------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(EW_THREADS) void rescale_kernel(EwArgs args) {
@@ -260,6 +265,9 @@ __global__ __launch_bounds__(EW_THREADS) void rescale_kernel(EwArgs args) {
             t = args.prefix[mi + 1];
             continue;
         }
+        // source of hi: the caller's buffer (never written here) or the workspace copy, in place
+        const void* hsrc = d.hi_alias ? (d.mom ? static_cast<const void*>(d.mom) : d.g) : d.xop[0];
+        if (d.hi_alias && threadIdx.x == 0) const_cast<MatDesc*>(args.descs)[mi].hi0 = d.xop[0];
         const int tend = min(t1, args.prefix[mi + 1]);
         for (; t < tend; ++t) {
             int i0, j0;
@@ -269,7 +277,7 @@ __global__ __launch_bounds__(EW_THREADS) void rescale_kernel(EwArgs args) {
                 const size_t idx = static_cast<size_t>(i0 + ew_row(p)) * d.np + (j0 + jl);
                 if (sizeof(T) == 2) {
                     float h[EW_GROUP], l[EW_GROUP];
-                    load8<uint16_t>(d.xop[0], idx, h);
+                    load8<uint16_t>(hsrc, idx, h);
                     load8<uint16_t>(d.xlo, idx, l);
 #pragma unroll
                     for (int k = 0; k < EW_GROUP; ++k) {

@@ -182,6 +182,11 @@ muon_status build_plan(std::vector<Item>& items, const muon_hparams* hp, bool ns
             auto ok = [](const void* ptr) { return ptr == nullptr || reinterpret_cast<uintptr_t>(ptr) % 16 == 0; };
             d.uvec = (it.cols % 8 == 0 && ok(it.w) && ok(it.g) && ok(it.mom) && ok(it.out)) ? 1 : 0;
         }
+        // the first step can read hi straight from the caller's buffer when that buffer
+        // holds bf16(U) in the NS frame with the padded pitch and no padding rows
+        d.hi_alias = (dtype == MUON_BF16 && hp->ns_steps > 0 && !(hp->flags & MUON_FLAG_NESTEROV && !ns_only) &&
+                      !d.tall && d.uvec && it.rows % pad == 0 && it.cols % pad == 0) ? 1 : 0;
+        d.hi0 = d.hi_alias ? (ns_only ? it.g : static_cast<const void*>(it.mom)) : nullptr;
         const int64_t ewt = (s.mp / EW_TILE) * (s.np / EW_TILE);
         const int64_t tm = s.mp / pad, tn = s.np / pad;
         const int64_t symt = tm * (tm + 1) / 2, updt = tm * tn;
@@ -226,6 +231,7 @@ muon_status build_plan(std::vector<Item>& items, const muon_hparams* hp, bool ns
                 d.xop[p] = reinterpret_cast<void*>(off);
                 off = align_up(off + mn * 2, ALIGN);
             }
+            // xop[0] stays in the layout when hi is aliased: the rescale kernel may need it
             d.xlo = reinterpret_cast<uint16_t*>(off);
             off = align_up(off + mn * 2, ALIGN);
         } else {
@@ -255,11 +261,13 @@ void rebase(Plan& pl, char* base) {
             fix(d.xop[0]);
             fix(d.xop[1]);
             fix(d.xlo);
+            if (!d.hi_alias) d.hi0 = d.xop[0];
         } else {
             fix(d.x32[0]);
             fix(d.x32[1]);
             d.xop[0] = d.x32[0];
             d.xop[1] = d.x32[1];
+            d.hi0 = d.xop[0];
         }
         fix(d.amat);
         fix(d.bmat);

@@ -43,6 +43,16 @@ struct MatDesc {
     //         significant bits in all); x32 is unused.
     float* x32[2];
     void* xop[2];       // operand copies, ping-pong; equal to x32 for fp32
+    // Operand read by the first step (Gram and update): xop[0], or, when
+    // hi_alias is set, the caller's buffer that already holds hi = bf16(U)
+    // bit for bit (the stored momentum M' = U, or muon_ns's bf16 input), in
+    // which case K1 writes only lo.  Set for bf16, no Nesterov, at least one
+    // step, untransposed, rows and cols multiples of the GEMM tile, 16-byte
+    // aligned pointers.  If the norm shift applies, the rescale kernel writes
+    // the shifted hi to xop[0] and points hi0 there.
+    const void* hi0;
+    int32_t hi_alias;
+    int32_t pad_alias;
     uint16_t* xlo;      // bf16 only, updated in place
     void* amat;         // mp x mp, A = X X^T (symmetric, stored in full)
     void* bmat;         // mp x mp, B = b A + c A A (symmetric, stored in full)

@@ -1042,7 +1042,8 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
     const int ks_m = (d.m + E::KS - 1) / E::KS, ks_n = (d.n + E::KS - 1) / E::KS;
     f32x16_t acc[E::SM][E::SN];
     if (PHASE == PH_GRAM) {
-        const char* X = static_cast<const char*>(d.xop[ping]);
+        // the first step reads hi0 (the workspace copy, or the caller's buffer holding the same bits)
+        const char* X = static_cast<const char*>(args.first ? d.hi0 : d.xop[ping]);
         const size_t ld = static_cast<size_t>(np) * sizeof(T);
         E::run(X + row0 * ld, ld, X + col0 * ld, ld, ks_n, lds, acc, ZeroInit{}, NoHook{});
         // first step: X0 = s * M' is folded in as A0 = s^2 M' M'^T
@@ -1061,7 +1062,7 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.bmat, mp, args.c, nullptr, 0.0f, 0.0f);
     } else {
         const char* B = static_cast<const char*>(d.bmat);
-        const char* X = static_cast<const char*>(d.xop[ping]);
+        const char* X = static_cast<const char*>(args.first ? d.hi0 : d.xop[ping]);
         const size_t ldb = static_cast<size_t>(mp) * sizeof(T), ldx = static_cast<size_t>(np) * sizeof(T);
         if constexpr (sizeof(T) == 2) {
             E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, ks_m, lds, acc, ZeroInit{},

@@ -36,24 +36,29 @@ def main(log_path, out_path, command):
         "seeded host draws the oracle reads.  Bars: O relative Frobenius error <= 3e-2 (bf16) or",
         "1e-5 (fp32); for bf16 every singular value of O inside the oracle's [min - 0.05, max + 0.05];",
         "stored M' within 1 ulp of the once-rounded oracle value; W' within 1 ulp plus the share",
-        "of O's own error (the largest ulp distance is listed as measured).",
+        "of O's own error.  'W' bound' is the largest |W'_gpu - W'_oracle| / (1 ulp + O's share) over",
+        "the matrix (the test requires <= 1; for fp32 the relative Frobenius error of W' is listed).",
+        "'spectrum' is the largest deviation of the sorted singular values of O from the schedule's",
+        "scalar map of the input's (28672x8192 only; bar 0.05).",
         "",
         "Command (from the repository root):",
         "",
         f"    {command}",
         "",
-        "| workload | matrix | shape | dtype | O rel err | bar | margin | sigma(O_gpu) | oracle band | M' max ulp | W' max ulp |",
-        "|---|---|---|---|---|---|---|---|---|---|---|",
+        "| case | matrix | shape | dtype | O rel err | bar | margin | sigma(O_gpu) | oracle band | M' max ulp | W' bound | spectrum |",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|",
     ]
     for r in keep:
         err, tol = r["o_rel_err"], r["tol"]
-        w = r.get("w_ulp_max", "—")
+        w = f"{r['w_bound_ratio']:.3f}" if "w_bound_ratio" in r else "—"
         if "w_rel_err" in r:
             w = f"rel {r['w_rel_err']:.1e}"
+        m = r.get("m_ulp_max", "—")
+        sp = f"{r['spectrum_dev']:.4f}" if "spectrum_dev" in r else "—"
         lines.append(
             f"| {r['config']} | {r['matrix']} | {r['shape'][0]}x{r['shape'][1]} | {r['dtype']} | {err:.3e} | "
             f"{tol:.0e} | {tol / max(err, 1e-300):.1f}x | {fmt_range(r.get('sigma'))} | {fmt_range(r.get('band'))} | "
-            f"{r['m_ulp_max']} | {w} |")
+            f"{m} | {w} | {sp} |")
     lines.append("")
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines))

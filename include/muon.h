@@ -113,6 +113,24 @@ size_t muon_workspace_bytes(const muon_matrix* mats, int32_t n, const muon_hpara
 muon_status muon_step(const muon_matrix* mats, int32_t n, const muon_hparams* hp,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): muon_step
+ * with its workspace in a library-owned device array of
+ * MUON_NOALLOC_SCRATCH_BYTES bytes per GPU.  The array is part of the
+ * library's device code; its address is looked up on the first call on each
+ * device, and each GPU the library runs on holds it until the process ends.
+ * The call allocates nothing, on the device or the host: the descriptors
+ * travel as kernel arguments.
+ *  - A list whose muon_workspace_bytes() exceeds MUON_NOALLOC_SCRATCH_BYTES is
+ *    rejected with MUON_ERR_WORKSPACE before anything is enqueued (128 MiB
+ *    holds, for example, any one 2048 x 8192 matrix in bf16).
+ *  - Every call on one GPU uses that GPU's one array, which keeps the last
+ *    call's contents (nothing in it has to start at zero).  Calls that overlap
+ *    on one GPU, from other streams or threads, race: the caller serializes them.
+ *  - Validation, results and errors are otherwise those of muon_step. */
+#define MUON_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+muon_status muon_step_noalloc(const muon_matrix* mats, int32_t n, const muon_hparams* hp, void* stream);
+
 /* Orthogonalization only (the zeropower_via_newtonschulz contract of
  * [Muon优化器]): out = NS(in / (||in||_F + eps)) with hp's schedule.
  * `in` has hp->dtype; `out` is fp32, same shape, row-major; in and out must

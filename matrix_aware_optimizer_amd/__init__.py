@@ -6,7 +6,7 @@ device memory and streams.  There is no CPU fallback: if the library is not
 built, or the device is not gfx950, the calls raise.
 
 The names mirror the C entry points:
-``muon_step``, ``muon_ns``, ``muon_workspace_bytes``,
+``muon_step``, ``muon_step_noalloc``, ``muon_ns``, ``muon_workspace_bytes``,
 ``muon_ns_workspace_bytes``, ``muon_adamw_step``,
 ``muon_adamw_workspace_bytes``, ``muon_cayley_step``,
 ``muon_cayley_workspace_bytes``, ``muon_status_string``,
@@ -88,6 +88,8 @@ SIGNATURES = {
     "muon_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MuonMatrix), ctypes.c_int32, ctypes.POINTER(MuonHparams)]),
     "muon_step": (ctypes.c_int32, [ctypes.POINTER(MuonMatrix), ctypes.c_int32, ctypes.POINTER(MuonHparams),
                                    ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "muon_step_noalloc": (ctypes.c_int32, [ctypes.POINTER(MuonMatrix), ctypes.c_int32, ctypes.POINTER(MuonHparams),
+                                           ctypes.c_void_p]),
     "muon_ns_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MuonNsMatrix), ctypes.c_int32,
                                                   ctypes.POINTER(MuonHparams)]),
     "muon_ns": (ctypes.c_int32, [ctypes.POINTER(MuonNsMatrix), ctypes.c_int32, ctypes.POINTER(MuonHparams),
@@ -286,6 +288,21 @@ def muon_step(weights: Iterable, grads: Iterable, moms: Iterable, *, lr, beta=0.
     _check(lib.muon_step(arr, n, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                          workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return workspace
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # MUON_NOALLOC_SCRATCH_BYTES
+
+
+def muon_step_noalloc(weights: Iterable, grads: Iterable, moms: Iterable, *, lr, beta=0.95, weight_decay=0.0,
+                      schedule=(), scale_rule="naive", eps=1e-7, nesterov=False, stream=None):
+    """:func:`muon_step` without a workspace and without any allocation: the library
+    uses its own per-GPU device array of ``NOALLOC_SCRATCH_BYTES``.  Calls that
+    overlap on one GPU race; lists that need more workspace raise MuonError."""
+    weights, grads, moms = list(weights), list(grads), list(moms)
+    arr, n, dtype = _matrices(weights, grads, moms)
+    hp, keep = make_hparams(lr=lr, beta=beta, weight_decay=weight_decay, eps=eps, scale_rule=scale_rule,
+                            schedule=schedule, dtype=dtype, nesterov=nesterov)
+    _check(load().muon_step_noalloc(arr, n, ctypes.byref(hp), _stream_handle(stream)))
 
 
 def _ns_matrices(inputs, outputs):

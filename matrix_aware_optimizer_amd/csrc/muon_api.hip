@@ -391,11 +391,67 @@ muon_status timed_launch(int cls, hipStream_t s, const char* what, F launch) {
 }
 
 // ---------------------------------------------------------------------------
+// Workspace of muon_step_noalloc: a file-scope device array, one copy per GPU,
+// held until the process ends.  In host code the name `scratch` is a host-side
+// stand-in, not the device memory: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is ever handed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[MUON_NOALLOC_SCRATCH_BYTES];
+std::vector<char*> g_scratch_ptr;   // per device; nullptr until set up
+
+muon_status scratch_address(int dev, char** out) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (static_cast<int>(g_scratch_ptr.size()) <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(MUON_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = static_cast<char*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return MUON_OK;
+}
+
+// The descriptor header written by kernels whose arguments carry it, 3 KB per
+// launch: no pinned staging buffer (and so no allocation) is needed, and the
+// bytes are copied at launch time, so nothing on the host must outlive the call.
+constexpr int HDR_CHUNK_WORDS = 768;
+struct HeaderChunk {
+    uint32_t word0;    // first 4-byte word of the destination
+    uint32_t nwords;
+    uint32_t w[HDR_CHUNK_WORDS];
+};
+
+__global__ __launch_bounds__(256) void header_write_kernel(HeaderChunk c, uint32_t* dst) {
+    for (uint32_t i = threadIdx.x; i < c.nwords; i += 256) dst[c.word0 + i] = c.w[i];
+}
+
+muon_status upload_by_args(void* dst, const void* src, size_t bytes, hipStream_t s) {
+    if (bytes % 4) return fail(MUON_ERR_INVALID_ARG, "header of %zu bytes is not a whole number of words", bytes);
+    const uint32_t* words = static_cast<const uint32_t*>(src);
+    const size_t nw = bytes / 4;
+    HeaderChunk c;
+    for (size_t w0 = 0; w0 < nw; w0 += HDR_CHUNK_WORDS) {
+        c.word0 = static_cast<uint32_t>(w0);
+        c.nwords = static_cast<uint32_t>(std::min<size_t>(HDR_CHUNK_WORDS, nw - w0));
+        std::memcpy(c.w, words + w0, 4 * c.nwords);
+        hipLaunchKernelGGL(header_write_kernel, dim3(1), dim3(256), 0, s, c, static_cast<uint32_t*>(dst));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "header write kernel");
+    }
+    return MUON_OK;
+}
+
+// ---------------------------------------------------------------------------
 // The launch sequence shared by muon_step and muon_ns
 // ---------------------------------------------------------------------------
 
+// header_by_args: write the descriptor header with kernel launches instead of a
+// copy from the pinned staging ring (muon_step_noalloc, which allocates nothing).
 muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, void* workspace,
-                size_t ws_bytes, hipStream_t stream) {
+                size_t ws_bytes, hipStream_t stream, bool header_by_args = false) {
     Plan pl;
     muon_status st = build_plan(items, hp, ns_only, pl);
     if (st != MUON_OK) return st;
@@ -433,7 +489,8 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
     std::memcpy(pre, pl.ew_prefix.data(), sizeof(int32_t) * (nmat + 1));
     std::memcpy(pre + (nmat + 1), pl.sym_prefix.data(), sizeof(int32_t) * (nmat + 1));
     std::memcpy(pre + 2 * (nmat + 1), pl.upd_prefix.data(), sizeof(int32_t) * (nmat + 1));
-    st = upload(dev, base, header.data(), pl.header_bytes, stream);
+    st = header_by_args ? upload_by_args(base, header.data(), pl.header_bytes, stream)
+                        : upload(dev, base, header.data(), pl.header_bytes, stream);
     if (st != MUON_OK) return st;
 
     const MatDesc* d_descs = reinterpret_cast<const MatDesc*>(base + pl.off_descs);
@@ -892,6 +949,29 @@ muon_status muon_step(const muon_matrix* mats, int32_t n, const muon_hparams* hp
     if (st != MUON_OK) return st;
     if (items.empty()) { g_last_error.clear(); return MUON_OK; }
     return run(items, hp, false, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+muon_status muon_step_noalloc(const muon_matrix* mats, int32_t n, const muon_hparams* hp, void* stream) {
+    std::vector<Item> items;
+    muon_status st = collect_step(mats, n, hp, items);
+    if (st != MUON_OK) return st;
+    if (items.empty()) { g_last_error.clear(); return MUON_OK; }
+    {
+        Plan pl;
+        st = build_plan(items, hp, false, pl);
+        if (st != MUON_OK) return st;
+        if (pl.total_bytes > MUON_NOALLOC_SCRATCH_BYTES)
+            return fail(MUON_ERR_WORKSPACE, "this list needs %zu bytes of workspace; muon_step_noalloc holds at most %zu "
+                        "(use muon_step with a caller workspace, or split the list)",
+                        pl.total_bytes, static_cast<size_t>(MUON_NOALLOC_SCRATCH_BYTES));
+    }
+    int dev = 0, cu_count = 0;
+    st = check_device(&dev, &cu_count);
+    if (st != MUON_OK) return st;
+    char* ws = nullptr;
+    st = scratch_address(dev, &ws);
+    if (st != MUON_OK) return st;
+    return run(items, hp, false, ws, MUON_NOALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream), true);
 }
 
 size_t muon_ns_workspace_bytes(const muon_ns_matrix* mats, int32_t n, const muon_hparams* hp) {

@@ -303,3 +303,27 @@ def test_cayley_size_limit_and_workspace_errors():
     assert lib.muon_cayley_step(None, 0, ctypes.byref(hp), None, 0, None) == mao.MUON_OK
     skip = _cayley_mats([(FAKE, None, FAKE + (2 << 30), 512, 64)])
     assert lib.muon_cayley_step(skip, 1, ctypes.byref(hp), None, 0, None) == mao.MUON_OK
+
+
+def test_noalloc_entry_validation_is_host_side():
+    lib = mao.load()
+    hp, keep = _hp(dtype=mao.MUON_BF16)
+    # empty and all-skipped lists succeed without touching the GPU
+    assert lib.muon_step_noalloc(None, 0, ctypes.byref(hp), None) == mao.MUON_OK
+    skip = _mats([(FAKE, None, FAKE + (2 << 30), 2048, 2048)])
+    assert lib.muon_step_noalloc(skip, 1, ctypes.byref(hp), None) == mao.MUON_OK
+    # the same argument checks as muon_step
+    assert lib.muon_step_noalloc(_mats([(None, FAKE + (1 << 30), FAKE + (2 << 30), 64, 96)]), 1,
+                                 ctypes.byref(hp), None) == mao.MUON_ERR_INVALID_ARG
+    assert lib.muon_step_noalloc(_mats([(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 64, 96)]), 1,
+                                 None, None) == mao.MUON_ERR_INVALID_ARG
+    # a list needing more workspace than the library's array is refused before anything runs
+    big = _mats([(FAKE + (k << 32), FAKE + (k << 32) + (1 << 30), FAKE + (k << 32) + (2 << 30), 2048, 8192)
+                 for k in range(4)])
+    assert lib.muon_workspace_bytes(big, 4, ctypes.byref(hp)) > mao.NOALLOC_SCRATCH_BYTES
+    assert lib.muon_step_noalloc(big, 4, ctypes.byref(hp), None) == mao.MUON_ERR_WORKSPACE
+    assert "128" in mao.muon_last_error_message() or str(mao.NOALLOC_SCRATCH_BYTES) in mao.muon_last_error_message()
+    # the header's limit and the binding's agree
+    src = open(HEADER).read()
+    assert "#define MUON_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in src
+    assert mao.NOALLOC_SCRATCH_BYTES == 128 << 20

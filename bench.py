@@ -197,6 +197,132 @@ def summarize_profiles(prof_dir, workload_id, commands):
     print(json.dumps({"written": [os.path.relpath(out, ROOT), os.path.relpath(TRAFFIC_FILE, ROOT)]}))
 
 
+COUNTER_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp",
+    "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o transformer "
+    "-- python3 $R/bench.py --steps 5 --warmup 2 --only --no-cpu-baseline",
+    "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_BUSY_CU_CYCLES GRBM_COUNT --kernel-include-regex muon:: "
+    "--output-format csv -d $R/gpurun_out/prof/mfma -o mfma -- python3 $R/bench.py --steps 1 --warmup 1 --only --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE; then TD_TD_BUSY_sum TA_TA_BUSY_sum GRBM_GUI_ACTIVE; then "
+    "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_WAIT_INST_LDS) with the same options, directories "
+    "fetch, write, tdta, lds",
+    "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d $R/gpurun_out/prof/cfetch (cwrite) -o copy "
+    "-- python3 $R/bench.py --calibrate-copy",
+    "python3 bench.py --summarize-counters gpurun_out/prof",
+]
+
+# Library kernels by their rocprofv3 names, with the algorithmic work of one launch on a
+# workload: ('flop', n) for the matrix-core kernels, ('bytes', n) for the HBM-bound ones.
+def _kernel_table(wl):
+    shapes = wl.shapes
+    elem = sum(r * c for r, c in shapes)
+    es = 2 if wl.dtype == "bf16" else 4
+    gram = sum(min(r, c) ** 2 * max(r, c) for r, c in shapes)
+    poly = sum(min(r, c) ** 3 for r, c in shapes)
+    upd = sum(2 * min(r, c) ** 2 * max(r, c) for r, c in shapes)
+    t = "unsigned short" if wl.dtype == "bf16" else "float"
+    return [
+        (f"momentum_norm_kernel<{t}, false>", "K1 momentum + norm", ("bytes", 3 * es * elem)),
+        ("norm_finalize_kernel", "norm finalize", None),
+        (f"rescale_kernel<{t}>", "norm shift (no-op here)", None),
+        (f"ns_gemm_kernel<{t}, 0>", "K2 Gram", ("flop", gram)),
+        (f"ns_gemm_kernel<{t}, 3>", "K3 polynomial", ("flop", poly)),
+        (f"ns_gemm_kernel<{t}, 2>", "K4 update", ("flop", upd)),
+        (f"ns_gemm_kernel<{t}, 4>", "K4 last update + apply", ("flop", upd)),
+    ]
+
+
+def summarize_counters(prof_dir, workload_id, commands):
+    """Per-kernel counter table from one rocprofv3 session (see COUNTER_COMMANDS):
+    time, engine clock, MFMA busy, TD / TA busy, HBM bytes, LDS conflicts."""
+    import csv
+    import glob
+    import workloads as wk
+    wl = wk.WORKLOADS[workload_id]
+
+    def short(k):
+        return k.replace("void ", "").replace("muon::(anonymous namespace)::", "").split("(")[0]
+
+    stats = sorted(glob.glob(os.path.join(prof_dir, "trace", "*_kernel_stats.csv")))[0]
+    avg_ns = {}
+    with open(stats) as fh:
+        for r in csv.DictReader(fh):
+            avg_ns[short(r["Name"])] = float(r["AverageNs"])
+    cnt = {}
+    for sub in ("mfma", "fetch", "write", "tdta", "lds"):
+        for r in _counter_rows(os.path.join(prof_dir, sub)):
+            k = short(r["Kernel_Name"])
+            cnt.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+
+    def avg(k, c):
+        v = cnt.get(k, {}).get(c)
+        return sum(v) / len(v) if v else None
+
+    cf = [float(r["Counter_Value"]) for r in _counter_rows(os.path.join(prof_dir, "cfetch"), "copyBuffer")]
+    cw = [float(r["Counter_Value"]) for r in _counter_rows(os.path.join(prof_dir, "cwrite"), "copyBuffer")]
+    fetch_factor = (1 << 30) / (sum(cf) / len(cf) * 1024.0)
+    write_factor = (1 << 30) / (sum(cw) / len(cw) * 1024.0)
+    CUS, SIMDS, XCDS = 256, 4, 8
+    lines = [f"# Counters per kernel, {wl.name}", "",
+             "One rocprofv3 session on the library's kernels (`bench.py --only`, one step after one warm-up",
+             "for the counter passes; five steps for the kernel trace).  Each counter pass is its own run.", "",
+             "Commands (from the repository root; `R` is its absolute path):", ""]
+    lines += [f"    {c}" for c in commands] + [""]
+    lines += [
+        "How the columns are formed:",
+        "",
+        "- `ms`: average duration per launch from the kernel trace.",
+        "- `GHz`: GRBM_GUI_ACTIVE / 8 (the counter is summed over the 8 XCDs) / the dispatch's duration.",
+        "- `MFMA busy`: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 256 CUs x 4 SIMDs).  The counter",
+        "  sums busy cycles over the SIMDs: one 32x32x16 bf16 MFMA (32768 FLOP) keeps a SIMD's matrix core",
+        "  busy 32 cycles, so its per-launch value equals the executed FLOP / 1024 (the update: 4.83e9 =",
+        "  4.948e12 / 1024).  This is utilization at the clock the kernel ran at, executed work (diagonal",
+        "  Gram and polynomial tiles are computed whole), not the published-peak fraction.",
+        "- `alg. frac`: algorithmic FLOP (or bytes) per launch / duration / published peak (2516.6 TFLOP/s",
+        "  bf16, 8 TB/s HBM), as the benchmark reports it.",
+        "- `TD busy`, `TA busy`: TD_TD_BUSY_sum, TA_TA_BUSY_sum / (GRBM_GUI_ACTIVE / 8 x 256).  TD returns",
+        "  the operand data to the CU (here mostly direct-to-LDS loads).",
+        f"- `HBM read / write`: FETCH_SIZE x {fetch_factor:.3f} and WRITE_SIZE x {write_factor:.3f} (KiB per dispatch;",
+        "  factors from a 1 GiB device copy, which reads 0.5 GiB and writes 1 GiB by these counters).",
+        "- `LDS conflict`: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles stalled on bank conflicts per",
+        "  active LDS cycle).",
+        "",
+        "| kernel | ms | GHz | MFMA busy | alg. frac | TD busy | TA busy | HBM read GB | HBM write GB | LDS conflict |",
+        "|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for name, label, work in _kernel_table(wl):
+        ms = avg_ns.get(name, 0.0) / 1e6
+        gui = avg(name, "GRBM_GUI_ACTIVE")
+        if not ms or not gui:
+            continue
+        cyc = gui / XCDS
+        ghz = cyc / (ms * 1e6)
+        mb = avg(name, "SQ_VALU_MFMA_BUSY_CYCLES")
+        mfma = f"{100 * mb / (cyc * CUS * SIMDS):.1f}%" if mb else "—"
+        td = avg(name, "TD_TD_BUSY_sum")
+        ta = avg(name, "TA_TA_BUSY_sum")
+        fr = avg(name, "FETCH_SIZE")
+        wr = avg(name, "WRITE_SIZE")
+        bc, ia = avg(name, "SQ_LDS_BANK_CONFLICT"), avg(name, "SQ_LDS_IDX_ACTIVE")
+        if work is None:
+            alg = "—"
+        elif work[0] == "flop":
+            alg = f"{work[1] / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS * 100:.1f}%"
+        else:
+            alg = f"{work[1] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS * 100:.1f}% HBM"
+        ghz_s = f"{ghz:.2f}" if ms >= 0.05 else "—"   # launch overhead dominates tiny kernels
+        lines.append(
+            f"| {label} `{name}` | {ms:.4f} | {ghz_s} | {mfma} | {alg} | "
+            f"{100 * td / (cyc * CUS):.1f}% | {100 * ta / (cyc * CUS):.1f}% | "
+            f"{fr * 1024 * fetch_factor / 1e9:.3f} | {wr * 1024 * write_factor / 1e9:.3f} | "
+            f"{(100 * bc / ia) if ia else 0:.1f}% |")
+    lines.append("")
+    out = os.path.join(ROOT, "profiles", f"counters_{wk.short_name(workload_id)}.md")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print(json.dumps({"written": os.path.relpath(out, ROOT)}))
+
+
 def measure_adamw(dev, steps, dtype="bf16"):
     """The AdamW half of the step: the transformer's non-matrix parameters (token
     embedding and head, 32000 x 2048 each, and 49 norm vectors of 2048), timed with
@@ -449,6 +575,8 @@ def main():
                     help="only run a 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write the profiles/ summaries from a rocprofv3 session under DIR (no GPU)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="write the per-kernel counter table from a rocprofv3 counter session under DIR (no GPU)")
     args = ap.parse_args()
 
     if args.calibrate_copy:
@@ -456,6 +584,9 @@ def main():
         return
     if args.summarize_profiles:
         summarize_profiles(args.summarize_profiles, args.workload, PROFILE_COMMANDS)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload, COUNTER_COMMANDS)
         return
 
     if args.gpus != 1:

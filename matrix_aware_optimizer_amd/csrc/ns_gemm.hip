@@ -20,9 +20,9 @@
 // (global_load_lds_dwordx4, no VGPR staging) into a ring of five slabs (one
 // slab = one operand's k-step); the loads of the next Q slab and of the P slab
 // after it are spread between the current k-step's MFMA groups, and MFMA
-// fragments are double-buffered in registers.  For k-contiguous Q the loop is
-// rotated: the barrier that opens a k-step sits before the previous step's last
-// k-slice, whose MFMAs then cover the new step's first fragment reads.
+// fragments are double-buffered in registers.  The loop is rotated: the barrier
+// that opens a k-step sits before the previous step's last k-slice, whose MFMAs
+// then cover the new step's first fragment reads.
 //
 // LDS layouts.  k-contiguous rows: 16-byte chunks XOR-swizzled with bits 1..3
 // of the row, so 32-row ds_read_b128 fragment reads are free of bank
@@ -34,13 +34,16 @@
 // addressing X[k0 + i/4][n0 + 4 (i%4)] receive column n0 + l, rows k0..k0+3:
 // two such reads form the 8-element k-slice of an MFMA B operand.
 //
-// Epilogues work from registers: a 4 x 4 transpose inside each lane quad
-// (DPP) turns a lane's 4 rows x 1 column of a 32 x 32 block into 1 row x 4
-// columns (16-byte fp32 accesses); for bf16 a swap between lanes c and c ^ 4
-// then gives each lane 8 columns (16 bytes).  The mirrored half of a symmetric
-// output is stored from the untransposed layout.  The bf16 update adds a lo
-// after its k-loop from the tile's lo rows loaded into the idle ring, then
-// stages its output through LDS and stores whole tile rows.  Buffers are zero-padded to
+// Epilogues.  bf16 outputs of the Gram, the polynomial and the update are
+// staged column-major in LDS straight from the accumulator layout (one 8-byte
+// write per 4 values) and stored as whole tile rows through transpose reads;
+// symmetric outputs are also stored mirrored, through plain reads of the same
+// staging.  The bf16 update adds a lo after its k-loop from the tile's lo rows
+// loaded into the idle ring.  The fp32 epilogues, the last update's W' and the
+// c = 0 polynomial work from registers: a 4 x 4 transpose inside each lane
+// quad (DPP) turns a lane's 4 rows x 1 column of a 32 x 32 block into 1 row x
+// 4 columns, and for bf16 a swap between lanes c and c ^ 4 then gives each lane
+// 8 columns (16 bytes).  Buffers are zero-padded to
 // the block tile, so there are no edge masks, and k-loops run over the real
 // extent rounded up to a k-step.
 //
@@ -147,9 +150,6 @@ struct Engine {
     static constexpr int GROUPS = SUB * SM;            // MFMA groups per k-step
     static_assert(BM == BN, "P and Q slabs have one size");
     static_assert(2 * HL <= GROUPS, "one load per MFMA group at most");
-    // The rotated k-loop (below) for k-contiguous Q; the k-major update keeps one
-    // barrier per step at its top, where its per-step hook needs the registers.
-    static constexpr bool ROTATE = !QK;
     // loads of P(kt + 2) issued before the barrier that opens step kt + 1 (the last slice's)
     static constexpr int PB = ((SUB - 1) * SM < 2 * HL ? (SUB - 1) * SM : 2 * HL) - HL;
     static_assert(PB >= 0 && PB <= HL, "the loads of Q(kt + 1) precede the last slice");
@@ -185,10 +185,9 @@ struct Engine {
     // A barrier opens step kt once each wave's loads of P(kt) and Q(kt) are done, so
     // only P(kt + 1) stays in flight across it; after it no wave reads the slots of
     // step kt - 1 again, and step kt refills them with Q(kt + 1) and P(kt + 2).
-    // Rotated (ROTATE), that barrier sits before the last k-slice of step kt - 1 (after
-    // the prologue for step 0), whose MFMAs then cover the first fragment reads of
-    // step kt; each wave also waits for its LDS reads before it.  Otherwise it sits at
-    // the top of step kt.
+    // The loop is rotated: that barrier sits before the last k-slice of step kt - 1
+    // (after the prologue for step 0), whose MFMAs then cover the first fragment reads
+    // of step kt; each wave also waits for its LDS reads before it.
     template <typename Init, typename Hook>
     static __device__ __attribute__((always_inline)) void run(const char* __restrict__ P, size_t ldp, const char* __restrict__ Q,
                                       size_t ldq, int ksteps, u32x4* lds, f32x16_t (&acc)[SM][SN], Init init,
@@ -258,18 +257,16 @@ struct Engine {
         };
 
         u32x4 fa[2][SM], fb[2][SN];
-        if constexpr (ROTATE) {
-            // step 0's slabs (P(1) may still be in flight), then its first fragments
-            if (ksteps > 1)
-                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(HL) : "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            asm volatile("s_barrier" ::: "memory");
+        // step 0's slabs (P(1) may still be in flight), then its first fragments
+        if (ksteps > 1)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(HL) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_barrier" ::: "memory");
 #pragma unroll
-            for (int i = 0; i < SM; ++i) fa[0][i] = lds[swz(arow + i * 32, half)];
+        for (int i = 0; i < SM; ++i) fa[0][i] = lds[swz(arow + i * 32, half)];
 #pragma unroll
-            for (int j = 0; j < SN; ++j) fb[0][j] = read_b(lds + SLAB, j, 0);
-        }
+        for (int j = 0; j < SN; ++j) fb[0][j] = read_b(lds + SLAB, j, 0);
 
         int sp = 0;   // slot of P(kt); Q(kt) sits in the next one
         for (int kt = 0; kt < ksteps; ++kt) {
@@ -279,28 +276,12 @@ struct Engine {
             const int np = sp >= 3 ? sp - 3 : sp + 2;   // slot of P(kt + 1)
             const u32x4* L = lds + sp * SLAB;
             const u32x4* LQ = lds + sq * SLAB;
-            if constexpr (!ROTATE) {
-                // this wave's loads of step kt's slabs are done (P(kt + 1) may still be
-                // in flight); the barrier publishes every wave's and ends all reads of
-                // the slots of step kt - 1
-                if (kt + 1 < ksteps)
-                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(HL) : "memory");
-                else
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                asm volatile("s_barrier" ::: "memory");
-            }
             hook(kt, (const lds_byte_t*)LQ, acc);
-            if constexpr (!ROTATE) {
-#pragma unroll
-                for (int i = 0; i < SM; ++i) fa[0][i] = L[swz(arow + i * 32, half)];
-#pragma unroll
-                for (int j = 0; j < SN; ++j) fb[0][j] = read_b(LQ, j, 0);
-            }
             const bool more1 = kt + 1 < ksteps, more2 = kt + 2 < ksteps;
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < SUB; ++s) {
-                if (ROTATE && s == SUB - 1 && more1) {
+                if (s == SUB - 1 && more1) {
                     // Open step kt + 1 before this step's last slice, whose MFMAs then
                     // cover the first fragment reads of the next step.  Every read of
                     // step kt's slabs (fragments and hook) has completed; this wave's
@@ -322,7 +303,7 @@ struct Engine {
                     if (s + 1 < SUB) {
                         fa[(s + 1) & 1][i] = L[swz(arow + i * 32, cn)];
                         if (i < SN) fb[(s + 1) & 1][i] = read_b(LQ, i, s + 1);
-                    } else if (ROTATE && more1) {
+                    } else if (more1) {
                         fa[0][i] = lds[np * SLAB + swz(arow + i * 32, half)];
                         if (i < SN) fb[0][i] = read_b(lds + s3 * SLAB, i, 0);
                     }
@@ -380,6 +361,7 @@ enum Phase { PH_GRAM = 0, PH_POLY = 1, PH_UPDATE = 2, PH_POLY_LDS = 3, PH_UPDATE
 struct NoHook {
     template <typename A> __device__ __forceinline__ void operator()(int, const lds_byte_t*, A&) const {}
 };
+
 
 struct ZeroInit {
     template <typename A> __device__ __forceinline__ void operator()(A& acc) const {
@@ -717,7 +699,9 @@ struct HiAddend {
 
 // a lo for the bf16 update, after the k-loop: the tile's lo rows arrive as
 // BM / KS k-major slabs in the idle ring (coalesced 512-byte rows) and are
-// added with the same transpose reads as a hi.
+// added with the same transpose reads as a hi.  (Issuing three of the slabs at
+// the barrier that opens the last k-step, into the slots freed there, timed the
+// same as loading all four here.)
 template <typename E>
 __device__ __forceinline__ void add_lo_tile(f32x16_t (&acc)[E::SM][E::SN], const uint16_t* xlo, size_t np, int row0,
                                             int col0, float a, u32x4* lds) {
@@ -806,86 +790,237 @@ __device__ __attribute__((always_inline)) void update_epilogue_f32(f32x16_t (&ac
             }
 }
 
-// bf16 update epilogue staged through LDS.  Stores whose lanes each hold 16 bytes
-// of a different row (the register layout) reach about a third of the per-CU
-// store rate of row-contiguous ones, so the tile goes through LDS: hi' is written
-// there in the register layout, read back as whole 512-byte tile rows (two per
-// wave instruction) and stored (non-temporal: the next reader is the next
-// step, after the whole launch); then the same for lo', kept in registers
-// meanwhile.  Staged row r of the tile sits at r * 512 bytes with its 16-byte
-// chunk c at position c ^ (r & 31).
-__device__ __forceinline__ int stage_off(int r, int chunk) { return r * 512 + ((chunk ^ (r & 31)) << 4); }
+// ----------------------------------------------------------------------------
+// Column-major staging of a 256 x 256 bf16 output tile in LDS (128 KB), used by
+// the bf16 update and symmetric-output epilogues.  Column c occupies the 512
+// bytes at c * 512; its 256 rows form 64 eight-byte units of 4 rows, unit u
+// stored at position u ^ csw(c).  In the accumulator layout a lane holds 4
+// consecutive rows of one column of each 32 x 32 block, i.e. exactly one unit:
+// the tile goes to LDS with one 8-byte write per 4 values and no register
+// shuffles (the quad transposes and lane swaps a row-major layout needs cost
+// more VALU cycles than the rest of the epilogue).  Read back
+//   * row-major, for direct stores: ds_read_b64_tr_b16 over units of 16
+//     columns gives each lane 4 consecutive columns of one row; two reads make
+//     the 16 bytes of one store, and a wave instruction stores 4 rows x 128
+//     columns (whole 128-byte lines);
+//   * column-major, for the mirrored store of a symmetric output: one 16-byte
+//     read is 8 consecutive rows of column c, i.e. 8 consecutive columns of the
+//     mirrored row c (the two units trade places when csw(c) is odd).
+// The swizzle makes the writes and the transpose reads free of LDS bank
+// conflicts and the mirror reads run at two cycles per half-wave (its minimum);
+// a CPU model of every lane address checked this and that each element is
+// written and read exactly once.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ int csw(int c) { return (c & 31) ^ (((c >> 5) & 1) << 2); }
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
 
 template <typename E>
-__device__ __forceinline__ void stage_copy_out(const lds_byte_t* L, uint16_t* dst, int row0, int col0, size_t np) {
-    constexpr int CHUNKS = E::BM * E::BN / 8;   // 16-byte chunks of the tile
-#pragma unroll 4
-    for (int q = threadIdx.x; q < CHUNKS; q += GEMM_THREADS) {
-        const int r = q >> 5, c = q & 31;
-        const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(L + stage_off(r, c));
-        __builtin_nontemporal_store(v, G(reinterpret_cast<u32x4*>(dst + static_cast<size_t>(row0 + r) * np + col0 + 8 * c)));
+struct CStage {
+    static_assert(E::BM == 256 && E::BN == 256 && E::WM == 128 && E::WN == 64, "staging geometry");
+    static_assert(E::BM * 512 <= E::LDS_CHUNKS * 16, "a staged tile fits the LDS");
+    int wbase[E::SN];   // byte address of this lane's unit for i = g = 0, per column block j
+    __device__ CStage() {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / WAVES_N, wn = wave % WAVES_N, h = lane >> 5;
+#pragma unroll
+        for (int j = 0; j < E::SN; ++j) {
+            const int c = wn * E::WN + 32 * j + (lane & 31);
+            wbase[j] = c * 512 + 256 * wm + 8 * (h ^ csw(c));
+        }
+    }
+    // rows 32 i + 8 g + 4 h + (0..3) of block (i, j): unit 32 wm + 8 i + 2 g + h; the
+    // block part of the unit index has no bits in common with wbase's, so XOR adds it
+    __device__ __forceinline__ void put(lds_byte_t* L, int i, int j, int g, unsigned w0, unsigned w1) const {
+        *(lds_u32x2_t*)(L + (wbase[j] ^ (64 * i + 16 * g))) = u32x2_t{w0, w1};
+    }
+};
+
+// 8 bf16 (packed, in column order) at p: one 16-byte store, or per element where `mask` has bits clear.
+template <bool NT>
+__device__ __forceinline__ void st_packed8(uint16_t* p, const u32x4& v, unsigned mask) {
+    if (mask == 0xFFu) {
+        if (NT) __builtin_nontemporal_store(v, G(reinterpret_cast<u32x4*>(p)));
+        else G(reinterpret_cast<u32x4*>(p))[0] = v;
+    } else if (mask) {
+        const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (mask & (1u << e)) G(p)[e] = static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)));
     }
 }
 
+// Direct copy-out of a staged tile: tile row r, columns cc .. cc + 7 per lane and
+// instruction.  DIAG stores only the elements with r <= c (the upper triangle of a
+// diagonal tile of a symmetric output).
+template <typename E, bool DIAG, bool NT>
+__device__ __forceinline__ void cstage_store_rows(const lds_byte_t* L, uint16_t* dst, int row0, int col0, size_t ld) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = lane >> 4, k = lane & 15;
+    // lane k of a 16-lane group addresses column ccA = 32 grp + 8 (k & 3) + (k >> 2) (read A)
+    // and ccA + 4 (read B) at the row quad being stored; the transpose hands lane l the
+    // row 4 u + (l & 3), columns 32 grp + 8 ((l & 15) >> 2) + (0..3) and (4..7)
+    const int ccA = 32 * grp + 8 * (k & 3) + (k >> 2);
+    // wave w stores the row quads 8 w .. 8 w + 7; 8 u = 64 w + 8 du shares no bits with
+    // the swizzled unit offset's upper part, and +128 columns is +65536 bytes
+    const int pA = (ccA * 512 + 8 * csw(ccA)) ^ (64 * wave);
+    const int pB = ((ccA + 4) * 512 + 8 * csw(ccA + 4)) ^ (64 * wave);
+    const int r = 32 * wave + (lane & 3);
+    const int cs = 32 * grp + 8 * (k >> 2);
+    // the store address advances by 4 rows per row quad (kept incremental: precomputing
+    // all 16 addresses of an unrolled loop costs registers the caller needs)
+    uint16_t* out = dst + static_cast<size_t>(row0 + r) * ld + col0 + cs;
+    const size_t quad = 4 * ld;
+#pragma unroll 2
+    for (int du = 0; du < 8; ++du) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(L + ((pA ^ (8 * du)) + 65536 * half)));
+            const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(L + ((pB ^ (8 * du)) + 65536 * half)));
+            const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
+            unsigned mask = 0xFFu;
+            if (DIAG) {
+                const int rr = r + 4 * du, cc = cs + 128 * half;
+                mask = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) mask |= (rr <= cc + e) ? (1u << e) : 0u;
+            }
+            st_packed8<NT>(out + 128 * half, u32x4{a2.x, a2.y, b2.x, b2.y}, mask);
+        }
+        out += quad;
+    }
+}
+
+// Mirrored copy-out of a staged symmetric-output tile: column c of the tile is row
+// col0 + c of the output, from column row0.  Lanes 0-31 take column c, lanes 32-63
+// column c + 1, each 8 consecutive rows.  DIAG stores only rows r < c (the strictly
+// upper triangle, mirrored).
+template <typename E, bool DIAG>
+__device__ __forceinline__ void cstage_store_mirror(const lds_byte_t* L, uint16_t* dst, int row0, int col0, size_t ld) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m = lane & 31, hh = lane >> 5;
+    // column c = 32 w + 2 t + hh: csw(c) = (2 t + hh) ^ (4 (w & 1)), odd exactly when hh = 1;
+    // the 16-byte slot of units 2m, 2m + 1 is 2m ^ (csw(c) & ~1)
+    const int base = (32 * wave + hh) * 512 + ((16 * m) ^ (32 * (wave & 1)));
+#pragma unroll 4
+    for (int t = 0; t < 16; ++t) {
+        const int c = 32 * wave + 2 * t + hh;
+        const u32x4 v = *(const lds_u32x4_t*)(L + ((base ^ (16 * t)) + 1024 * t));
+        const u32x4 w = hh ? u32x4{v.z, v.w, v.x, v.y} : v;   // rows 8m .. 8m + 7 in order
+        unsigned mask = 0xFFu;
+        if (DIAG) {
+            mask = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mask |= (8 * m + e < c) ? (1u << e) : 0u;
+        }
+        st_packed8<false>(dst + static_cast<size_t>(col0 + c) * ld + row0 + 8 * m, w, mask);
+    }
+}
+
+// bf16 symmetric output (Gram, polynomial with the staged addend): value = scale * acc,
+// staged once, stored directly and mirrored.
 template <typename E>
-__device__ __attribute__((always_inline)) void update_epilogue_staged(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
-                                                                      uint16_t* hi_out, uint16_t* lo_out, size_t np,
-                                                                      float u, u32x4* lds) {
-    static_assert(E::BN * 2 == 512 && E::BM * 512 <= E::LDS_CHUNKS * 16, "a staged tile row is 512 bytes");
-    const Coords<E> q(row0, col0);
-    const bool odd = odd_quad();
+__device__ __attribute__((always_inline)) void sym_epilogue_cstage(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
+                                                                   bool diag, uint16_t* dst, size_t ld, float scale,
+                                                                   u32x4* lds) {
+    const CStage<E> st;
     lds_byte_t* L = (lds_byte_t*)lds;
-    u32x4 lo[E::SM][E::SN][2];
     lds_barrier();   // every wave is done reading the operand slabs
 #pragma unroll
     for (int i = 0; i < E::SM; ++i)
 #pragma unroll
         for (int j = 0; j < E::SN; ++j)
 #pragma unroll
-            for (int gg = 0; gg < 2; ++gg) {
-                float v0[4], v1[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    v0[p] = acc[i][j][8 * gg + p];
-                    v1[p] = acc[i][j][8 * gg + 4 + p];
-                }
-                quad_transpose(v0);
-                quad_transpose(v1);
-                float x[8];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float keep = odd ? v1[p] : v0[p];
-                    const float recv = __uint_as_float(swap_xor4(__float_as_uint(odd ? v0[p] : v1[p])));
-                    x[p] = odd ? recv : keep;
-                    x[4 + p] = odd ? keep : recv;
-                }
-                unsigned h[4], l[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float o0 = u * x[2 * p], o1 = u * x[2 * p + 1];
-                    h[p] = pack_bf16x2(o0, o1);
-                    l[p] = pack_bf16x2(o0 - __uint_as_float(h[p] << 16), o1 - __uint_as_float(h[p] & 0xffff0000u));
-                }
-                const int r = q.tr_row - row0 + 32 * i + 8 * (2 * gg + odd);
-                const int c = (q.tr_col - col0 + 32 * j - (odd ? 4 : 0)) >> 3;
-                *(__attribute__((address_space(3))) u32x4*)(L + stage_off(r, c)) = u32x4{h[0], h[1], h[2], h[3]};
-                lo[i][j][gg] = u32x4{l[0], l[1], l[2], l[3]};
+            for (int g = 0; g < 4; ++g) {
+                const f32x16_t& a = acc[i][j];
+                st.put(L, i, j, g, pack_bf16x2(scale * a[4 * g], scale * a[4 * g + 1]),
+                       pack_bf16x2(scale * a[4 * g + 2], scale * a[4 * g + 3]));
             }
     lds_barrier();
-    stage_copy_out<E>(L, hi_out, row0, col0, np);
-    lds_barrier();
+    if (diag) {
+        cstage_store_rows<E, true, false>(L, dst, row0, col0, ld);
+        cstage_store_mirror<E, true>(L, dst, row0, col0, ld);
+    } else {
+        cstage_store_rows<E, false, false>(L, dst, row0, col0, ld);
+        cstage_store_mirror<E, false>(L, dst, row0, col0, ld);
+    }
+}
+
+// bf16 update epilogue: X' = u acc as hi' = bf16(X') and lo' = bf16(X' - hi'), in two
+// passes over the tile's row halves.  In pass p the waves owning rows 128 p ..
+// 128 p + 127 stage both hi' and lo' of those rows (64 KB each: column c of a half
+// at c * 256, unit u at u ^ csw(c), lo' 64 KB after hi'), straight from their
+// accumulators; then every wave stores the two halves as whole tile rows
+// (non-temporal: the next reader is the next launch).  No value waits in
+// registers for a later pass beyond the other half's accumulators.
+template <typename E>
+__device__ __forceinline__ void hstage_store_rows(const lds_byte_t* L, int region, uint16_t* dst, int row0, int col0,
+                                                  size_t ld) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = lane >> 4, k = lane & 15;
+    // as cstage_store_rows, over a half whose columns are 256 bytes: wave w stores the
+    // row quads u = 4 w .. 4 w + 3 (8 u = 32 w + 8 du, disjoint bits), +128 columns is
+    // +32768 bytes
+    const int ccA = 32 * grp + 8 * (k & 3) + (k >> 2);
+    const int pA = (region + ccA * 256 + 8 * csw(ccA)) ^ (32 * wave);
+    const int pB = (region + (ccA + 4) * 256 + 8 * csw(ccA + 4)) ^ (32 * wave);
+    uint16_t* out = dst + static_cast<size_t>(row0 + 16 * wave + (lane & 3)) * ld + col0 + 32 * grp + 8 * (k >> 2);
+    const size_t quad = 4 * ld;
 #pragma unroll
-    for (int i = 0; i < E::SM; ++i)
+    for (int du = 0; du < 4; ++du) {
 #pragma unroll
-        for (int j = 0; j < E::SN; ++j)
+        for (int half = 0; half < 2; ++half) {
+            const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(L + ((pA ^ (8 * du)) + 32768 * half)));
+            const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(L + ((pB ^ (8 * du)) + 32768 * half)));
+            const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
+            st_packed8<true>(out + 128 * half, u32x4{a2.x, a2.y, b2.x, b2.y}, 0xFFu);
+        }
+        out += quad;
+    }
+}
+
+template <typename E, bool SCALE>
+__device__ __attribute__((always_inline)) void update_epilogue_cstage(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
+                                                                      uint16_t* hi_out, uint16_t* lo_out, size_t np,
+                                                                      float u, u32x4* lds) {
+    static_assert(E::BM == 256 && E::BN == 256 && E::WM == 128 && E::WN == 64 && WAVES_M == 2, "staging geometry");
+    constexpr int LO = 65536;   // byte offset of the lo' half-tile stage
+    static_assert(2 * LO <= E::LDS_CHUNKS * 16, "both half stages fit the LDS");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N, h = lane >> 5;
+    lds_byte_t* L = (lds_byte_t*)lds;
+    int wbase[E::SN];   // this lane's unit for i = g = 0 in the half, per column block j
 #pragma unroll
-            for (int gg = 0; gg < 2; ++gg) {
-                const int r = q.tr_row - row0 + 32 * i + 8 * (2 * gg + odd);
-                const int c = (q.tr_col - col0 + 32 * j - (odd ? 4 : 0)) >> 3;
-                *(__attribute__((address_space(3))) u32x4*)(L + stage_off(r, c)) = lo[i][j][gg];
-            }
-    lds_barrier();
-    stage_copy_out<E>(L, lo_out, row0, col0, np);
+    for (int j = 0; j < E::SN; ++j) {
+        const int c = wn * E::WN + 32 * j + (lane & 31);
+        wbase[j] = c * 256 + 8 * (h ^ csw(c));
+    }
+#pragma unroll
+    for (int pass = 0; pass < WAVES_M; ++pass) {
+        lds_barrier();   // operand slabs (pass 0) or the previous half's stage (pass 1) are read
+        if (wm == pass) {
+#pragma unroll
+            for (int i = 0; i < E::SM; ++i)
+#pragma unroll
+                for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float v[4];
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) v[p] = SCALE ? u * acc[i][j][4 * g + p] : acc[i][j][4 * g + p];
+                        const unsigned h0 = pack_bf16x2(v[0], v[1]), h1 = pack_bf16x2(v[2], v[3]);
+                        const unsigned l0 = pack_bf16x2(v[0] - __uint_as_float(h0 << 16), v[1] - __uint_as_float(h0 & 0xffff0000u));
+                        const unsigned l1 = pack_bf16x2(v[2] - __uint_as_float(h1 << 16), v[3] - __uint_as_float(h1 & 0xffff0000u));
+                        // rows 32 i + 8 g + 4 h of the half: unit 8 i + 2 g + h
+                        const int at = wbase[j] ^ (64 * i + 16 * g);
+                        *(lds_u32x2_t*)(L + at) = u32x2_t{h0, h1};
+                        *(lds_u32x2_t*)(L + LO + at) = u32x2_t{l0, l1};
+                    }
+        }
+        lds_barrier();
+        hstage_store_rows<E>(L, 0, hi_out, row0 + 128 * pass, col0, np);
+        hstage_store_rows<E>(L, LO, lo_out, row0 + 128 * pass, col0, np);
+    }
 }
 
 // Last update of muon_step: W' = decay W - coef X' goes straight from the
@@ -1048,7 +1183,10 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         E::run(X + row0 * ld, ld, X + col0 * ld, ld, ks_n, lds, acc, ZeroInit{}, NoHook{});
         // first step: X0 = s * M' is folded in as A0 = s^2 M' M'^T
         const float scale = args.first ? G(d.scal)[0] * G(d.scal)[0] : 1.0f;
-        sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.amat, mp, scale, nullptr, 0.0f, 0.0f);
+        if constexpr (sizeof(T) == 2)
+            sym_epilogue_cstage<E>(acc, row0, col0, ti == tj, static_cast<uint16_t*>(d.amat), mp, scale, lds);
+        else
+            sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.amat, mp, scale, nullptr, 0.0f, 0.0f);
     } else if (PHASE == PH_POLY) {
         const char* A = static_cast<const char*>(d.amat);
         const size_t ld = static_cast<size_t>(mp) * sizeof(T);
@@ -1059,7 +1197,10 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         const size_t ld = static_cast<size_t>(mp) * sizeof(T);
         E::run(A + row0 * ld, ld, A + col0 * ld, ld, ks_m, lds, acc, ZeroInit{},
                PolyAddend<E, T>{row0 / E::KS, args.b / args.c});
-        sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.bmat, mp, args.c, nullptr, 0.0f, 0.0f);
+        if constexpr (sizeof(T) == 2)
+            sym_epilogue_cstage<E>(acc, row0, col0, ti == tj, static_cast<uint16_t*>(d.bmat), mp, args.c, lds);
+        else
+            sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.bmat, mp, args.c, nullptr, 0.0f, 0.0f);
     } else {
         const char* B = static_cast<const char*>(d.bmat);
         const char* X = static_cast<const char*>(args.first ? d.hi0 : d.xop[ping]);
@@ -1076,8 +1217,12 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         const float u = args.first ? G(d.scal)[0] : 1.0f;
         if constexpr (PHASE == PH_UPDATE_APPLY)
             apply_epilogue<E, T>(acc, row0, col0, d, u);
-        else if constexpr (sizeof(T) == 2)
-            update_epilogue_staged<E>(acc, row0, col0, static_cast<uint16_t*>(d.xop[ping ^ 1]), d.xlo, np, u, lds);
+        else if constexpr (sizeof(T) == 2) {
+            if (u != 1.0f)
+                update_epilogue_cstage<E, true>(acc, row0, col0, static_cast<uint16_t*>(d.xop[ping ^ 1]), d.xlo, np, u, lds);
+            else
+                update_epilogue_cstage<E, false>(acc, row0, col0, static_cast<uint16_t*>(d.xop[ping ^ 1]), d.xlo, np, u, lds);
+        }
         else
             update_epilogue_f32<E>(acc, row0, col0, d.x32[ping ^ 1], np, u);
     }

@@ -188,10 +188,30 @@ struct Engine {
     // The loop is rotated: that barrier sits before the last k-slice of step kt - 1
     // (after the prologue for step 0), whose MFMAs then cover the first fragment reads
     // of step kt; each wave also waits for its LDS reads before it.
+    //
+    // p_half: only the first BM / 2 rows of P are real (the last tile row of a matrix
+    // whose padded size adds at most BM / 2 rows).  The waves owning rows BM / 2 ..
+    // BM - 1 (wm = 1, which also load exactly those P rows) then issue no P loads, read
+    // no fragments and run no MFMAs: their accumulators keep init's value (zero for
+    // every caller that passes p_half), so the padding stays exactly zero.  They still
+    // load their share of Q and take part in every barrier, and wait for all their
+    // loads wherever the other waves keep P loads in flight.
     template <typename Init, typename Hook>
     static __device__ __attribute__((always_inline)) void run(const char* __restrict__ P, size_t ldp, const char* __restrict__ Q,
                                       size_t ldq, int ksteps, u32x4* lds, f32x16_t (&acc)[SM][SN], Init init,
-                                      Hook hook) {
+                                      Hook hook, bool p_half = false) {
+        static_assert(HL * 64 / CHUNKS_PER_ROW == BM / NWAVES && 2 * WAVES_N == NWAVES,
+                      "wave w loads P rows w BM / 8 ..: the waves with wm = 1 load exactly rows BM / 2 .. BM - 1");
+        if (p_half && (threadIdx.x >> 6) / WAVES_N == 1)
+            run_impl<true>(P, ldp, Q, ldq, ksteps, lds, acc, init, hook);
+        else
+            run_impl<false>(P, ldp, Q, ldq, ksteps, lds, acc, init, hook);
+    }
+
+    template <bool IDLE, typename Init, typename Hook>
+    static __device__ __attribute__((always_inline)) void run_impl(const char* __restrict__ P, size_t ldp,
+                                      const char* __restrict__ Q, size_t ldq, int ksteps, u32x4* lds,
+                                      f32x16_t (&acc)[SM][SN], Init init, Hook hook) {
         const int tid = threadIdx.x;
         const int lane = tid & 63, wave = tid >> 6;
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -215,11 +235,13 @@ struct Engine {
             const char* s = q ? srcq[j] + static_cast<size_t>(kt) * qstep : srcp[j] + static_cast<size_t>(kt) * pstep;
             __builtin_amdgcn_global_load_lds((const void*)s, d, 16, 0, 0);
         };
+        if constexpr (!IDLE) {
 #pragma unroll
-        for (int j = 0; j < HL; ++j) issue(0, false, 0, j);
+            for (int j = 0; j < HL; ++j) issue(0, false, 0, j);
+        }
 #pragma unroll
         for (int j = 0; j < HL; ++j) issue(0, true, 1, j);
-        if (ksteps > 1) {
+        if (!IDLE && ksteps > 1) {
 #pragma unroll
             for (int j = 0; j < HL; ++j) issue(1, false, 2, j);
         }
@@ -258,15 +280,17 @@ struct Engine {
 
         u32x4 fa[2][SM], fb[2][SN];
         // step 0's slabs (P(1) may still be in flight), then its first fragments
-        if (ksteps > 1)
+        if (!IDLE && ksteps > 1)
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(HL) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_barrier" ::: "memory");
+        if constexpr (!IDLE) {
 #pragma unroll
-        for (int i = 0; i < SM; ++i) fa[0][i] = lds[swz(arow + i * 32, half)];
+            for (int i = 0; i < SM; ++i) fa[0][i] = lds[swz(arow + i * 32, half)];
 #pragma unroll
-        for (int j = 0; j < SN; ++j) fb[0][j] = read_b(lds + SLAB, j, 0);
+            for (int j = 0; j < SN; ++j) fb[0][j] = read_b(lds + SLAB, j, 0);
+        }
 
         int sp = 0;   // slot of P(kt); Q(kt) sits in the next one
         for (int kt = 0; kt < ksteps; ++kt) {
@@ -288,7 +312,7 @@ struct Engine {
                     // loads of Q(kt + 1) and P(kt + 1) are done, only P(kt + 2) may be
                     // in flight.  After the barrier the slots of step kt are free.
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                    if (more2)
+                    if (!IDLE && more2)
                         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PB) : "memory");
                     else
                         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -298,18 +322,20 @@ struct Engine {
                 const int cn = 2 * (s + 1) + half;
 #pragma unroll
                 for (int i = 0; i < SM; ++i) {
+                    if constexpr (!IDLE) {
 #pragma unroll
-                    for (int j = 0; j < SN; ++j) mfma_chunk(acc[i][j], fa[s & 1][i], fb[s & 1][j], T{});
-                    if (s + 1 < SUB) {
-                        fa[(s + 1) & 1][i] = L[swz(arow + i * 32, cn)];
-                        if (i < SN) fb[(s + 1) & 1][i] = read_b(LQ, i, s + 1);
-                    } else if (more1) {
-                        fa[0][i] = lds[np * SLAB + swz(arow + i * 32, half)];
-                        if (i < SN) fb[0][i] = read_b(lds + s3 * SLAB, i, 0);
+                        for (int j = 0; j < SN; ++j) mfma_chunk(acc[i][j], fa[s & 1][i], fb[s & 1][j], T{});
+                        if (s + 1 < SUB) {
+                            fa[(s + 1) & 1][i] = L[swz(arow + i * 32, cn)];
+                            if (i < SN) fb[(s + 1) & 1][i] = read_b(LQ, i, s + 1);
+                        } else if (more1) {
+                            fa[0][i] = lds[np * SLAB + swz(arow + i * 32, half)];
+                            if (i < SN) fb[0][i] = read_b(lds + s3 * SLAB, i, 0);
+                        }
                     }
                     const int g = s * SM + i;
                     if (g < HL && more1) issue(kt + 1, true, s3, g);
-                    if (g >= HL && g < 2 * HL && more2) issue(kt + 2, false, s4, g - HL);
+                    if (!IDLE && g >= HL && g < 2 * HL && more2) issue(kt + 2, false, s4, g - HL);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -1170,6 +1196,17 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
     } else {
         sym_decode(local, mp / E::BM, ti, tj);
     }
+    // When the last tile row holds at most BM / 2 real rows (bf16), its tiles run with
+    // half of the waves idle (Engine::run, p_half).  A symmetric output stores every
+    // tile both directly and mirrored, so its last tile column is computed as the
+    // mirrored tile (tj, ti), whose padding then also falls in the P half.
+    const int tlast = mp / E::BM - 1;
+    const bool half_last = sizeof(T) == 2 && d.m - tlast * E::BM <= E::BM / 2;
+    if (!UPD && half_last && tj == tlast && ti != tj) {
+        tj = ti;
+        ti = tlast;
+    }
+    const bool p_half = half_last && ti == tlast;
     const int row0 = ti * E::BM, col0 = tj * E::BN;
 
     // k runs over the real extent rounded up to a k-step, not the tile padding: the
@@ -1180,7 +1217,7 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         // the first step reads hi0 (the workspace copy, or the caller's buffer holding the same bits)
         const char* X = static_cast<const char*>(args.first ? d.hi0 : d.xop[ping]);
         const size_t ld = static_cast<size_t>(np) * sizeof(T);
-        E::run(X + row0 * ld, ld, X + col0 * ld, ld, ks_n, lds, acc, ZeroInit{}, NoHook{});
+        E::run(X + row0 * ld, ld, X + col0 * ld, ld, ks_n, lds, acc, ZeroInit{}, NoHook{}, p_half);
         // first step: X0 = s * M' is folded in as A0 = s^2 M' M'^T
         const float scale = args.first ? G(d.scal)[0] * G(d.scal)[0] : 1.0f;
         if constexpr (sizeof(T) == 2)
@@ -1190,13 +1227,13 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
     } else if (PHASE == PH_POLY) {
         const char* A = static_cast<const char*>(d.amat);
         const size_t ld = static_cast<size_t>(mp) * sizeof(T);
-        E::run(A + row0 * ld, ld, A + col0 * ld, ld, ks_m, lds, acc, ZeroInit{}, NoHook{});
+        E::run(A + row0 * ld, ld, A + col0 * ld, ld, ks_m, lds, acc, ZeroInit{}, NoHook{}, p_half);
         sym_epilogue<E, T, true>(acc, row0, col0, ti == tj, d.bmat, mp, 1.0f, d.amat, args.b, args.c);
     } else if (PHASE == PH_POLY_LDS) {
         const char* A = static_cast<const char*>(d.amat);
         const size_t ld = static_cast<size_t>(mp) * sizeof(T);
         E::run(A + row0 * ld, ld, A + col0 * ld, ld, ks_m, lds, acc, ZeroInit{},
-               PolyAddend<E, T>{row0 / E::KS, args.b / args.c});
+               PolyAddend<E, T>{row0 / E::KS, args.b / args.c}, p_half);
         if constexpr (sizeof(T) == 2)
             sym_epilogue_cstage<E>(acc, row0, col0, ti == tj, static_cast<uint16_t*>(d.bmat), mp, args.c, lds);
         else
@@ -1207,7 +1244,7 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         const size_t ldb = static_cast<size_t>(mp) * sizeof(T), ldx = static_cast<size_t>(np) * sizeof(T);
         if constexpr (sizeof(T) == 2) {
             E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, ks_m, lds, acc, ZeroInit{},
-                   HiAddend<E>{row0 / E::KS, args.a});
+                   HiAddend<E>{row0 / E::KS, args.a}, p_half);
             add_lo_tile<E>(acc, d.xlo, static_cast<size_t>(np), row0, col0, args.a, lds);
         } else {
             const UpdateInit<E, T> init{d.x32[ping], static_cast<size_t>(np), row0, col0, args.a};

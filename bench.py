@@ -40,10 +40,10 @@ PROFILE_COMMANDS = [
     "cd /tmp && export TMPDIR=/tmp",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o transformer "
     "-- python3 $R/bench.py --steps 5 --warmup 2 --only --no-cpu-baseline",
-    "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"ns_gemm_kernel<unsigned short, 2>\" --output-format csv "
-    "-d $R/gpurun_out/prof/fetch -o upd -- python3 $R/bench.py --steps 2 --warmup 1 --only --no-cpu-baseline",
-    "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"ns_gemm_kernel<unsigned short, 2>\" --output-format csv "
-    "-d $R/gpurun_out/prof/write -o upd -- python3 $R/bench.py --steps 2 --warmup 1 --only --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE --kernel-include-regex muon:: --output-format csv "
+    "-d $R/gpurun_out/prof/fetch -o fetch -- python3 $R/bench.py --steps 1 --warmup 1 --only --no-cpu-baseline",
+    "rocprofv3 --pmc WRITE_SIZE --kernel-include-regex muon:: --output-format csv "
+    "-d $R/gpurun_out/prof/write -o write -- python3 $R/bench.py --steps 1 --warmup 1 --only --no-cpu-baseline",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/cfetch -o copy "
     "-- python3 $R/bench.py --calibrate-copy",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/cwrite -o copy "

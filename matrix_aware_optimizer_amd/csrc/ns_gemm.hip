@@ -939,12 +939,13 @@ __device__ __forceinline__ void cstage_store_mirror(const lds_byte_t* L, uint16_
 #pragma unroll
             for (int e = 0; e < 8; ++e) mask |= (8 * m + e < c) ? (1u << e) : 0u;
         }
-        st_packed8<false>(dst + static_cast<size_t>(col0 + c) * ld + row0 + 8 * m, w, mask);
+        st_packed8<true>(dst + static_cast<size_t>(col0 + c) * ld + row0 + 8 * m, w, mask);
     }
 }
 
 // bf16 symmetric output (Gram, polynomial with the staged addend): value = scale * acc,
-// staged once, stored directly and mirrored.
+// staged once, stored directly and mirrored (non-temporal: the next reader is the
+// next launch, and a batch's outputs do not stay in the caches until then).
 template <typename E>
 __device__ __attribute__((always_inline)) void sym_epilogue_cstage(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
                                                                    bool diag, uint16_t* dst, size_t ld, float scale,
@@ -964,10 +965,10 @@ __device__ __attribute__((always_inline)) void sym_epilogue_cstage(f32x16_t (&ac
             }
     lds_barrier();
     if (diag) {
-        cstage_store_rows<E, true, false>(L, dst, row0, col0, ld);
+        cstage_store_rows<E, true, true>(L, dst, row0, col0, ld);
         cstage_store_mirror<E, true>(L, dst, row0, col0, ld);
     } else {
-        cstage_store_rows<E, false, false>(L, dst, row0, col0, ld);
+        cstage_store_rows<E, false, true>(L, dst, row0, col0, ld);
         cstage_store_mirror<E, false>(L, dst, row0, col0, ld);
     }
 }

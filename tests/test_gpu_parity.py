@@ -104,6 +104,34 @@ def test_ns_grouped_ragged(gpu_lib, dtype, sched_name):
             _check_band(got[i], ref, RAGGED[i])
 
 
+# A seeded sweep of shapes around the tile edges (256 for bf16, 128 for fp32), thin
+# and single-row or single-column matrices, in one grouped call.
+def _sweep_shapes(seed, count):
+    rng = np.random.default_rng(seed)
+    edges = [1, 2, 31, 127, 128, 129, 255, 256, 257, 383, 511, 512, 513, 640, 767, 769, 1024]
+    shapes = []
+    for _ in range(count):
+        r = int(rng.choice(edges)) if rng.random() < 0.6 else int(rng.integers(1, 1100))
+        c = int(rng.choice(edges)) if rng.random() < 0.6 else int(rng.integers(1, 1100))
+        shapes.append((r, c))
+    return shapes
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ns_shape_sweep(gpu_lib, dtype):
+    shapes = _sweep_shapes(2024 if dtype == "bf16" else 2025, 24)
+    wl = wk.custom_workload(shapes, dtype=dtype, wid=230)
+    mats = [wk.host_matrix(wl, i, need=("G",))["G"] for i in range(len(shapes))]
+    _say("ns shape sweep", dtype, shapes)
+    got = _ns_gpu(gpu_lib, mats, dtype, KJ5)
+    for i, m in enumerate(mats):
+        ref = orc.muon_ns(m, KJ5)
+        err = rel_frob(got[i], ref)
+        assert err <= TOL[dtype], (shapes[i], err)
+        if dtype == "bf16" and min(m.shape) > 1:
+            _check_band(got[i], ref, shapes[i])
+
+
 def test_lowrank_ill_conditioned_bf16(gpu_lib):
     # rank-32 + 1e-3 noise, condition number far above 1e4
     wl = wk.custom_workload([(1024, 1024), (768, 1536)], dtype="bf16", grad="lowrank", rank=32,
@@ -329,6 +357,17 @@ def test_step_grouped_ragged(gpu_lib, dtype, rule):
     host = [wk.host_matrix(wl, i) for i in range(len(shapes))]
     _say("step grouped", dtype, rule)
     _check_step(gpu_lib, wl, range(len(shapes)), host, label=f"ragged grouped step, {rule} scale")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_step_shape_sweep(gpu_lib, dtype):
+    # the sweep of NS shapes through the whole step: K1's row groups with and without
+    # 16-byte accesses (cols % 8), the tall transposes, and the fused apply at the edges
+    shapes = _sweep_shapes(2026 if dtype == "bf16" else 2027, 24)
+    wl = wk.custom_workload(shapes, dtype=dtype, wid=231, lr=0.02, weight_decay=0.1, scale_rule="kellerjordan")
+    host = [wk.host_matrix(wl, i) for i in range(len(shapes))]
+    _say("step shape sweep", dtype, shapes)
+    _check_step(gpu_lib, wl, range(len(shapes)), host, label="shape sweep, Keller Jordan scale")
 
 
 def test_step_nesterov(gpu_lib):

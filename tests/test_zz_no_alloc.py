@@ -78,3 +78,41 @@ def test_noalloc_rejects_a_list_beyond_its_scratch(gpu_lib):
     # nothing was enqueued: the state is untouched
     assert all(int(torch.count_nonzero(m)) == 0 for m in M)
     assert all(int(torch.count_nonzero(w)) == 0 for w in W)
+
+
+def test_noalloc_step_replays_from_a_captured_graph(gpu_lib):
+    # The callers this entry is for capture it in a graph.  One call is captured after an
+    # eager warm-up (which sets up the library's per-GPU array); the graph is replayed three
+    # times, each time after eager work that resets the state to the same inputs, and every
+    # replay must give the eager call's bits.
+    wl = wk.custom_workload([(512, 768), (300, 517), (1024, 256)], dtype="bf16", wid=303,
+                            lr=0.02, weight_decay=0.1, scale_rule="moonlight")
+    hp = wl.hp
+    kw = dict(lr=hp["lr"], beta=hp["beta"], weight_decay=hp["weight_decay"], schedule=hp["schedule"],
+              scale_rule=hp["scale_rule"], eps=hp["eps"])
+    host, up = _inputs(wl)
+    G, W0, M0 = up("G"), up("W"), up("M")
+    We, Me = [w.clone() for w in W0], [m.clone() for m in M0]
+    mao.muon_step_noalloc(We, G, Me, **kw)
+    torch.cuda.synchronize()
+    Wg, Mg = [w.clone() for w in W0], [m.clone() for m in M0]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mao.muon_step_noalloc([w.clone() for w in W0], G, [m.clone() for m in M0], **kw)   # warm-up
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        mao.muon_step_noalloc(Wg, G, Mg, **kw)
+    for replay in range(3):
+        for w, w0 in zip(Wg, W0):
+            w.copy_(w0)
+        for m, m0 in zip(Mg, M0):
+            m.copy_(m0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i in range(wl.n):
+            assert torch.equal(Wg[i], We[i]), (replay, wl.shapes[i], "W'")
+            assert torch.equal(Mg[i], Me[i]), (replay, wl.shapes[i], "M'")

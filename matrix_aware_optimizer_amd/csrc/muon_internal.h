@@ -18,6 +18,27 @@ constexpr int GEMM_TILE_BF16 = 256;
 constexpr int GEMM_TILE_F32 = 128;
 constexpr int GEMM_THREADS = 512;   // 8 waves: two per SIMD
 
+// The bf16 iterate's lo part is kept in the update kernel's accumulator layout, so
+// that the update reads it straight into its accumulators and writes it straight from
+// them, one contiguous kilobyte per wave instruction.  The padded matrix is cut into
+// 256 x 256 tiles in row-major tile order, 64 Ki elements each.  Within a tile, 16-byte
+// chunk v * 512 + t belongs to thread t = 64 w + l of the update's workgroup (wave
+// w = 4 wm + wn, lane l) and holds its accumulator registers 8 h .. 8 h + 7 of 32 x 32
+// block (i, j), v = 4 i + 2 j + h.  Register q of that block is tile row
+// 128 wm + 32 i + 8 (q / 4) + 4 (l / 32) + q % 4 and tile column 64 wn + 32 j + l % 32
+// (the 32 x 32 MFMA output layout).
+static_assert(GEMM_TILE_BF16 == 256, "lo_offset is written for 256 x 256 tiles");
+__host__ __device__ inline size_t lo_offset(int row, int col, int np) {
+    const int r = row & 255, c = col & 255;
+    const int wm = r >> 7, wn = c >> 6, i = (r >> 5) & 3, j = (c >> 5) & 1, rr = r & 31;
+    const int q = 4 * (rr >> 3) + (rr & 3);            // accumulator register
+    const int l = (c & 31) + 32 * ((rr >> 2) & 1);      // lane
+    const int v = 4 * i + 2 * j + (q >> 3);
+    const int t = 64 * (4 * wm + wn) + l;
+    const size_t tile = static_cast<size_t>(row >> 8) * (np >> 8) + (col >> 8);
+    return tile * 65536 + (static_cast<size_t>(v) * 512 + t) * 8 + (q & 7);
+}
+
 enum Dtype : int32_t { DT_F32 = 0, DT_BF16 = 1 };
 
 // One active matrix.  "User frame" is the caller's rows x cols layout;
@@ -39,8 +60,9 @@ struct MatDesc {
     // k & 1 and writes index (k & 1) ^ 1.
     //   fp32: the iterate is x32[k & 1], which is also the MFMA operand.
     //   bf16: the iterate is the pair hi + lo with hi = bf16(X) = xop[k & 1]
-    //         (the MFMA operand) and lo = bf16(X - hi) = xlo (about 16
-    //         significant bits in all); x32 is unused.
+    //         (the MFMA operand, row-major) and lo = bf16(X - hi) = xlo (about
+    //         16 significant bits in all), stored in the update's accumulator
+    //         layout (lo_offset); x32 is unused.
     float* x32[2];
     void* xop[2];       // operand copies, ping-pong; equal to x32 for fp32
     // Operand read by the first step (Gram and update): xop[0], or, when
@@ -53,7 +75,7 @@ struct MatDesc {
     const void* hi0;
     int32_t hi_alias;
     int32_t pad_alias;
-    uint16_t* xlo;      // bf16 only, updated in place
+    uint16_t* xlo;      // bf16 only, updated in place, element (r, c) at lo_offset(r, c, np)
     void* amat;         // mp x mp, A = X X^T (symmetric, stored in full)
     void* bmat;         // mp x mp, B = b A + c A A (symmetric, stored in full)
     // Normalization scalars, NS_SCAL floats per matrix:

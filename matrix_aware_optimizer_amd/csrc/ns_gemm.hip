@@ -404,6 +404,32 @@ struct ZeroInit {
     }
 };
 
+// The bf16 update starts from a lo: lo is stored in this workgroup's accumulator
+// layout (lo_offset), so thread t's 16 chunks of the tile, chunk (i, j, h) at
+// ((4 i + 2 j + h) * 512 + t) * 16 bytes, are its registers 8 h .. 8 h + 7 of
+// block (i, j); each wave instruction reads 1 KB contiguous.
+template <typename E>
+struct LoInit {
+    const uint16_t* lo;   // the tile's 64 Ki elements
+    float a;
+    template <typename A> __device__ __forceinline__ void operator()(A& acc) const {
+        static_assert(E::SM == 4 && E::SN == 2, "lo_offset's block numbering");
+        const u32x4* p = reinterpret_cast<const u32x4*>(lo) + threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < E::SM; ++i)
+#pragma unroll
+            for (int j = 0; j < E::SN; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const u32x4 v = G(p)[((E::SN * i + j) * 2 + h) * GEMM_THREADS];
+                    const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        acc[i][j][8 * h + e] = a * __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+                }
+    }
+};
+
 // ----------------------------------------------------------------------------
 // Epilogue helpers.  Accumulator register r of 32 x 32 block (i, j) holds, in
 // lane l, element (8 (r >> 2) + 4 (l >> 5) + (r & 3), l & 31) of the block:
@@ -654,11 +680,11 @@ __device__ __forceinline__ void sym_epilogue(f32x16_t (&acc)[E::SM][E::SN], int 
 //         accumulators while the first operand slabs load (UpdateInit), and
 //         X' goes to x32[ping ^ 1].
 //   bf16: the iterate is the pair hi + lo (hi = xop[ping], the operand copy,
-//         lo = xlo).  a hi is added from LDS during the k-steps that stage the
-//         tile's own rows of X as operand k-rows (HiAddend); a lo after the
-//         k-loop, from the tile's lo rows loaded into the idle ring as k-major
-//         slabs (add_lo_tile).  X' is stored as hi' = bf16(X') to xop[ping ^ 1]
-//         and lo' = bf16(X' - hi') to xlo, in place.
+//         lo = xlo in the accumulator layout).  a lo is the accumulators'
+//         initial value (LoInit); a hi is added from LDS during the k-steps that
+//         stage the tile's own rows of X as operand k-rows (HiAddend).  X' is
+//         stored as hi' = bf16(X') to xop[ping ^ 1] and lo' = bf16(X' - hi') to
+//         xlo, in place (update_epilogue_native).
 template <typename E, typename T>
 struct UpdateInit {   // fp32 iterate
     const void* src;    // x32[ping]
@@ -726,27 +752,6 @@ struct HiAddend {
         }
     }
 };
-
-// a lo for the bf16 update, after the k-loop: the tile's lo rows arrive as
-// BM / KS k-major slabs in the idle ring (coalesced 512-byte rows) and are
-// added with the same transpose reads as a hi.  (Issuing three of the slabs at
-// the barrier that opens the last k-step, into the slots freed there, timed the
-// same as loading all four here.)
-template <typename E>
-__device__ __forceinline__ void add_lo_tile(f32x16_t (&acc)[E::SM][E::SN], const uint16_t* xlo, size_t np, int row0,
-                                            int col0, float a, u32x4* lds) {
-    constexpr int NSLAB = E::BM / E::KS;
-    static_assert(NSLAB * E::SLAB <= E::LDS_CHUNKS, "the lo tile fits the ring");
-    const size_t ld = np * sizeof(uint16_t);
-    const char* base = reinterpret_cast<const char*>(xlo + static_cast<size_t>(row0) * np + col0);
-    lds_barrier();   // every wave is done reading the operand slabs
-#pragma unroll
-    for (int c = 0; c < NSLAB; ++c) E::load_kmajor_slab(base + static_cast<size_t>(c) * E::KS * ld, ld, lds, c);
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    const HiAddend<E> add{row0 / E::KS, a};
-#pragma unroll
-    for (int c = 0; c < NSLAB; ++c) add(row0 / E::KS + c, (const lds_byte_t*)(lds + c * E::SLAB), acc);
-}
 
 // Polynomial B = b A + c A A with c != 0, accumulated as c (A A + (b / c) A): the
 // Q slab of k-step kt holds A[col0 + r][kt KS + (0..KS-1)], which by symmetry is
@@ -977,81 +982,43 @@ __device__ __attribute__((always_inline)) void sym_epilogue_cstage(f32x16_t (&ac
     }
 }
 
-// bf16 update epilogue: X' = u acc as hi' = bf16(X') and lo' = bf16(X' - hi'), in two
-// passes over the tile's row halves.  In pass p the waves owning rows 128 p ..
-// 128 p + 127 stage both hi' and lo' of those rows (64 KB each: column c of a half
-// at c * 256, unit u at u ^ csw(c), lo' 64 KB after hi'), straight from their
-// accumulators; then every wave stores the two halves as whole tile rows
-// (non-temporal: the next reader is the next launch).  No value waits in
-// registers for a later pass beyond the other half's accumulators.
-template <typename E>
-__device__ __forceinline__ void hstage_store_rows(const lds_byte_t* L, int region, uint16_t* dst, int row0, int col0,
-                                                  size_t ld) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int grp = lane >> 4, k = lane & 15;
-    // as cstage_store_rows, over a half whose columns are 256 bytes: wave w stores the
-    // row quads u = 4 w .. 4 w + 3 (8 u = 32 w + 8 du, disjoint bits), +128 columns is
-    // +32768 bytes
-    const int ccA = 32 * grp + 8 * (k & 3) + (k >> 2);
-    const int pA = (region + ccA * 256 + 8 * csw(ccA)) ^ (32 * wave);
-    const int pB = (region + (ccA + 4) * 256 + 8 * csw(ccA + 4)) ^ (32 * wave);
-    uint16_t* out = dst + static_cast<size_t>(row0 + 16 * wave + (lane & 3)) * ld + col0 + 32 * grp + 8 * (k >> 2);
-    const size_t quad = 4 * ld;
-#pragma unroll
-    for (int du = 0; du < 4; ++du) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(L + ((pA ^ (8 * du)) + 32768 * half)));
-            const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(L + ((pB ^ (8 * du)) + 32768 * half)));
-            const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
-            st_packed8<true>(out + 128 * half, u32x4{a2.x, a2.y, b2.x, b2.y}, 0xFFu);
-        }
-        out += quad;
-    }
-}
-
+// bf16 update epilogue: X' = u acc as hi' = bf16(X') and lo' = bf16(X' - hi').  hi' is
+// staged column-major in LDS (CStage) by every wave and stored as whole tile rows; lo'
+// goes straight from the accumulators to its tile in the accumulator layout (lo_offset),
+// 1 KB contiguous per wave instruction.  Both non-temporal: the next reader is the next
+// launch.
 template <typename E, bool SCALE>
-__device__ __attribute__((always_inline)) void update_epilogue_cstage(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
-                                                                      uint16_t* hi_out, uint16_t* lo_out, size_t np,
-                                                                      float u, u32x4* lds) {
-    static_assert(E::BM == 256 && E::BN == 256 && E::WM == 128 && E::WN == 64 && WAVES_M == 2, "staging geometry");
-    constexpr int LO = 65536;   // byte offset of the lo' half-tile stage
-    static_assert(2 * LO <= E::LDS_CHUNKS * 16, "both half stages fit the LDS");
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N, h = lane >> 5;
+__device__ __attribute__((always_inline)) void update_epilogue_native(f32x16_t (&acc)[E::SM][E::SN], int row0,
+                                                                      int col0, uint16_t* hi_out, uint16_t* lo_tile,
+                                                                      size_t np, float u, u32x4* lds) {
+    static_assert(E::SM == 4 && E::SN == 2, "lo_offset's block numbering");
+    const CStage<E> st;
     lds_byte_t* L = (lds_byte_t*)lds;
-    int wbase[E::SN];   // this lane's unit for i = g = 0 in the half, per column block j
+    u32x4* lp = reinterpret_cast<u32x4*>(lo_tile) + threadIdx.x;
+    lds_barrier();   // every wave is done reading the operand slabs
 #pragma unroll
-    for (int j = 0; j < E::SN; ++j) {
-        const int c = wn * E::WN + 32 * j + (lane & 31);
-        wbase[j] = c * 256 + 8 * (h ^ csw(c));
-    }
+    for (int i = 0; i < E::SM; ++i)
 #pragma unroll
-    for (int pass = 0; pass < WAVES_M; ++pass) {
-        lds_barrier();   // operand slabs (pass 0) or the previous half's stage (pass 1) are read
-        if (wm == pass) {
+        for (int j = 0; j < E::SN; ++j)
 #pragma unroll
-            for (int i = 0; i < E::SM; ++i)
+            for (int h = 0; h < 2; ++h) {
+                unsigned lw[4];
 #pragma unroll
-                for (int j = 0; j < E::SN; ++j)
+                for (int gg = 0; gg < 2; ++gg) {
+                    const int g = 2 * h + gg;
+                    float v[4];
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        float v[4];
-#pragma unroll
-                        for (int p = 0; p < 4; ++p) v[p] = SCALE ? u * acc[i][j][4 * g + p] : acc[i][j][4 * g + p];
-                        const unsigned h0 = pack_bf16x2(v[0], v[1]), h1 = pack_bf16x2(v[2], v[3]);
-                        const unsigned l0 = pack_bf16x2(v[0] - __uint_as_float(h0 << 16), v[1] - __uint_as_float(h0 & 0xffff0000u));
-                        const unsigned l1 = pack_bf16x2(v[2] - __uint_as_float(h1 << 16), v[3] - __uint_as_float(h1 & 0xffff0000u));
-                        // rows 32 i + 8 g + 4 h of the half: unit 8 i + 2 g + h
-                        const int at = wbase[j] ^ (64 * i + 16 * g);
-                        *(lds_u32x2_t*)(L + at) = u32x2_t{h0, h1};
-                        *(lds_u32x2_t*)(L + LO + at) = u32x2_t{l0, l1};
-                    }
-        }
-        lds_barrier();
-        hstage_store_rows<E>(L, 0, hi_out, row0 + 128 * pass, col0, np);
-        hstage_store_rows<E>(L, LO, lo_out, row0 + 128 * pass, col0, np);
-    }
+                    for (int p = 0; p < 4; ++p) v[p] = SCALE ? u * acc[i][j][4 * g + p] : acc[i][j][4 * g + p];
+                    const unsigned h0 = pack_bf16x2(v[0], v[1]), h1 = pack_bf16x2(v[2], v[3]);
+                    lw[2 * gg] = pack_bf16x2(v[0] - __uint_as_float(h0 << 16), v[1] - __uint_as_float(h0 & 0xffff0000u));
+                    lw[2 * gg + 1] = pack_bf16x2(v[2] - __uint_as_float(h1 << 16), v[3] - __uint_as_float(h1 & 0xffff0000u));
+                    st.put(L, i, j, g, h0, h1);
+                }
+                __builtin_nontemporal_store(u32x4{lw[0], lw[1], lw[2], lw[3]},
+                                            G(lp + ((E::SN * i + j) * 2 + h) * GEMM_THREADS));
+            }
+    lds_barrier();
+    cstage_store_rows<E, false, true>(L, hi_out, row0, col0, np);
 }
 
 // Last update of muon_step: W' = decay W - coef X' goes straight from the
@@ -1247,10 +1214,11 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
         const char* B = static_cast<const char*>(d.bmat);
         const char* X = static_cast<const char*>(args.first ? d.hi0 : d.xop[ping]);
         const size_t ldb = static_cast<size_t>(mp) * sizeof(T), ldx = static_cast<size_t>(np) * sizeof(T);
+        // bf16: the tile's lo, in the accumulator layout (lo_offset)
+        uint16_t* lo_tile = d.xlo + static_cast<size_t>(ti * (np / E::BN) + tj) * (E::BM * E::BN);
         if constexpr (sizeof(T) == 2) {
-            E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, ks_m, lds, acc, ZeroInit{},
+            E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, ks_m, lds, acc, LoInit<E>{lo_tile, args.a},
                    HiAddend<E>{row0 / E::KS, args.a}, p_half);
-            add_lo_tile<E>(acc, d.xlo, static_cast<size_t>(np), row0, col0, args.a, lds);
         } else {
             const UpdateInit<E, T> init{d.x32[ping], static_cast<size_t>(np), row0, col0, args.a};
             E::run(B + row0 * ldb, ldb, X + col0 * sizeof(T), ldx, ks_m, lds, acc, init, NoHook{});
@@ -1261,9 +1229,9 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
             apply_epilogue<E, T>(acc, row0, col0, d, u);
         else if constexpr (sizeof(T) == 2) {
             if (u != 1.0f)
-                update_epilogue_cstage<E, true>(acc, row0, col0, static_cast<uint16_t*>(d.xop[ping ^ 1]), d.xlo, np, u, lds);
+                update_epilogue_native<E, true>(acc, row0, col0, static_cast<uint16_t*>(d.xop[ping ^ 1]), lo_tile, np, u, lds);
             else
-                update_epilogue_cstage<E, false>(acc, row0, col0, static_cast<uint16_t*>(d.xop[ping ^ 1]), d.xlo, np, u, lds);
+                update_epilogue_native<E, false>(acc, row0, col0, static_cast<uint16_t*>(d.xop[ping ^ 1]), lo_tile, np, u, lds);
         }
         else
             update_epilogue_f32<E>(acc, row0, col0, d.x32[ping ^ 1], np, u);

@@ -136,26 +136,17 @@ __device__ __forceinline__ void momentum_group(const MatDesc& d, float beta, int
     }
 }
 
-// lo of one EW tile, staged in the order of lo_offset: the 64 x 64 tile covers 2 x 2
-// of the 32 x 32 blocks of one wave of the update's workgroup, i.e. 8 chunk rows v of
-// 64 lanes: 16-byte chunk k = q * 64 + lane for piece q = v - 4 i_a (i_a: its first
-// block row), element = accumulator register & 7.  Chunk k sits at LDS chunk
-// lo_stage_slot(k): the XOR spreads one wave's 2-byte writes (k differing in bits 3-7)
-// over 16 banks instead of 4.
-__device__ __forceinline__ int lo_stage_slot(int k) { return k ^ ((k >> 4) & 15); }
-__device__ __forceinline__ int lo_stage_index(int r, int c) {
-    const int rr = r & 31;
-    const int q = 4 * (rr >> 3) + (rr & 3);               // accumulator register
-    const int lane = (c & 31) + 32 * ((rr >> 2) & 1);
-    const int piece = 4 * (r >> 5) + 2 * (c >> 5) + (q >> 3);
-    return lo_stage_slot(piece * 64 + lane) * 8 + (q & 7);
-}
-
 template <typename T, bool NS_ONLY>
-__global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) {
-    __shared__ float tile[EW_TILE][EW_TILE + 1];
+__global__ __launch_bounds__(EW_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void momentum_norm_kernel(EwArgs args) {
+    // the turned tile and the lo stage share one LDS area (a barrier separates their uses):
+    // at 16.7 KB a block, eight blocks of the grid's eight per CU are resident together
+    __shared__ union __attribute__((aligned(16))) {
+        float tile[EW_TILE][EW_TILE + 1];
+        uint16_t lo[LO_STAGE_CHUNKS * 8];
+    } stage;
     __shared__ double red[4];
-    __shared__ __attribute__((aligned(16))) uint16_t lo_stage[EW_TILE * EW_TILE];
+    auto& tile = stage.tile;
+    uint16_t* const lo_stage = stage.lo;
     const int t0 = blockIdx.x * args.tiles_per_block;
     const int t1 = min(args.total, t0 + args.tiles_per_block);
     if (t0 >= t1) return;
@@ -188,6 +179,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
             for (int p = 0; p < EW_PASSES; ++p)
 #pragma unroll
                 for (int e = 0; e < EW_GROUP; ++e) u[p][e] = tile[ew_row(p)][jl + e];
+            if (sizeof(T) == 2) lds_barrier();   // every read of the turned tile precedes the lo stage
         }
 
         // ---- NS-frame rows: X32 (and the bf16 operand copy).  The squares are
@@ -213,9 +205,7 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
                 // with hi_alias the caller's buffer already holds hi (the stored M', or the input)
                 if (!d.hi_alias)
                     G(reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(d.xop[0]) + idx))[0] = u32x4_t{h[0], h[1], h[2], h[3]};
-#pragma unroll
-                for (int e = 0; e < EW_GROUP; ++e)
-                    lo_stage[lo_stage_index(ew_row(p), jl + e)] = static_cast<uint16_t>(l[e >> 1] >> (16 * (e & 1)));
+                lo_stage8(lo_stage, ew_row(p), jl, l);
             } else {
                 store8<float>(d.x32[0], idx, u[p]);
             }
@@ -224,14 +214,10 @@ __global__ __launch_bounds__(EW_THREADS) void momentum_norm_kernel(EwArgs args) 
             // lo in the update's accumulator layout: the staged tile is 8 whole 1 KB chunk
             // rows (v = 4 i_a + piece, lanes of wave 4 wm + wn), two 16-byte chunks a thread
             lds_barrier();
-            const int r0 = i0 & 255, c0 = j0 & 255;
-            const size_t tile_base = (static_cast<size_t>(i0 >> 8) * (d.np >> 8) + (j0 >> 8)) * 65536;
-            const int w = 4 * (r0 >> 7) + (c0 >> 6), ia = (r0 >> 5) & 3;
 #pragma unroll
             for (int k = static_cast<int>(threadIdx.x); k < EW_TILE * EW_TILE / 8; k += EW_THREADS) {
-                const int piece = k >> 6, lane = k & 63;
                 const u32x4_t v = reinterpret_cast<const u32x4_t*>(lo_stage)[lo_stage_slot(k)];
-                G(reinterpret_cast<u32x4_t*>(d.xlo + tile_base + static_cast<size_t>((4 * ia + piece) * 512 + w * 64 + lane) * 8))[0] = v;
+                G(reinterpret_cast<u32x4_t*>(d.xlo + lo_chunk_dst(i0, j0, d.np, k)))[0] = v;
             }
         }
         const double total = block_sum_256(sq, red);   // also orders LDS reuse

@@ -6,7 +6,10 @@ w = 4 wm + wn, lane l) holds register q of 32 x 32 block (i, j) for tile row
 128 wm + 32 i + 8 (q / 4) + 4 (l / 32) + q % 4 and column 64 wn + 32 j + l % 32 (the
 MFMA 32 x 32 output layout), in 16-byte chunk v = 4 i + 2 j + q / 8 of the tile.  The
 test compiles a small host program against the header and checks that lo_offset is a
-bijection onto the padded matrix and agrees with that per-thread description.
+bijection onto the padded matrix and agrees with that per-thread description.  It also
+runs the momentum kernel's LDS staging of lo (lo_stage8, lo_stage_slot, lo_chunk_dst) on
+the host over every 64 x 64 elementwise tile and checks that each element reaches its
+lo_offset.
 """
 from __future__ import annotations
 
@@ -49,7 +52,44 @@ int main() {
                             if (muon::lo_offset(row, col, np) != want) ++bad;
                         }
     std::printf("mismatches %ld\n", bad);
-    return bad != 0;
+    if (bad) return 1;
+
+    // The momentum kernel's staging: every 64 x 64 elementwise tile of the matrix, its
+    // 512 row groups of 8 staged with lo_stage8 (values name their element), then chunk k
+    // copied from LDS chunk lo_stage_slot(k) to lo_chunk_dst.  Each element must land at
+    // lo_offset, and no two staged chunks may share an LDS chunk.
+    long bad_stage = 0;
+    std::vector<uint16_t> stage(muon::LO_STAGE_CHUNKS * 8);
+    for (int i0 = 0; i0 < mp; i0 += 64)
+        for (int j0 = 0; j0 < np; j0 += 64) {
+            for (auto& x : stage) x = 0;
+            for (int r = 0; r < 64; ++r)
+                for (int c0 = 0; c0 < 64; c0 += 8) {
+                    unsigned l[4];
+                    for (int k = 0; k < 4; ++k)
+                        l[k] = (unsigned)(1 + r * 64 + c0 + 2 * k) | ((unsigned)(1 + r * 64 + c0 + 2 * k + 1) << 16);
+                    muon::lo_stage8(stage.data(), r, c0, l);
+                }
+            std::vector<int> slot_seen(muon::LO_STAGE_CHUNKS, 0);
+            for (int k = 0; k < 512; ++k) ++slot_seen[muon::lo_stage_slot(k)];
+            int used = 0;
+            for (int x : slot_seen) {
+                if (x > 1) ++bad_stage;
+                used += x;
+            }
+            if (used != 512) ++bad_stage;
+            for (int k = 0; k < 512; ++k) {
+                const size_t dst = muon::lo_chunk_dst(i0, j0, np, k);
+                for (int e = 0; e < 8; ++e) {
+                    const int v = stage[muon::lo_stage_slot(k) * 8 + e];
+                    if (v == 0) { ++bad_stage; continue; }
+                    const int r = (v - 1) / 64, c = (v - 1) % 64;
+                    if (muon::lo_offset(i0 + r, j0 + c, np) != dst + e) ++bad_stage;
+                }
+            }
+        }
+    std::printf("stage mismatches %ld\n", bad_stage);
+    return bad_stage != 0;
 }
 """
 
@@ -66,3 +106,4 @@ def test_lo_offset_is_the_update_accumulator_layout(tmp_path):
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0, run.stdout + run.stderr
     assert "mismatches 0" in run.stdout
+    assert "stage mismatches 0" in run.stdout

@@ -13,6 +13,7 @@
 // for Nesterov); the iteration starts from U / (||U||_F + eps); after it,
 // W' = (1 - lr*wd) W - lr*s*X.
 #include "muon_internal.h"
+#include "lo_stage.h"
 
 namespace muon {
 

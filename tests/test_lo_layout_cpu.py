@@ -1,4 +1,4 @@
-"""The bf16 iterate's lo layout (lo_offset in csrc/muon_internal.h), checked on the CPU.
+"""The bf16 iterate's lo layout (lo_offset in csrc/muon_internal.h, staging in csrc/lo_stage.h), checked on the CPU.
 
 lo_offset places element (row, col) of the padded NS-frame matrix at the position the
 update kernel's thread reads it from and writes it to: thread t = 64 w + l (wave
@@ -24,6 +24,7 @@ CSRC = os.path.join(HERE, "..", "matrix_aware_optimizer_amd", "csrc")
 
 PROGRAM = r"""
 #include "muon_internal.h"
+#include "lo_stage.h"
 #include <cstdio>
 #include <vector>
 int main() {

@@ -38,8 +38,10 @@
 // staged column-major in LDS straight from the accumulator layout (one 8-byte
 // write per 4 values) and stored as whole tile rows through transpose reads;
 // symmetric outputs are also stored mirrored, through plain reads of the same
-// staging.  The bf16 update adds a lo after its k-loop from the tile's lo rows
-// loaded into the idle ring.  The fp32 epilogues, the last update's W' and the
+// staging.  The bf16 iterate's lo part is kept in the update's accumulator
+// layout: the update reads a lo straight into its accumulators before the
+// k-loop and writes lo' straight from them (hi' goes through the staging).
+// The fp32 epilogues, the last update's W' and the
 // c = 0 polynomial work from registers: a 4 x 4 transpose inside each lane
 // quad (DPP) turns a lane's 4 rows x 1 column of a 32 x 32 block into 1 row x
 // 4 columns, and for bf16 a swap between lanes c and c ^ 4 then gives each lane
@@ -51,7 +53,8 @@
 // concatenation of all matrices' tiles (per-matrix prefix sums, largest
 // matrices first), one workgroup per tile.  The hardware deals workgroups
 // round-robin over the 8 XCDs; block ids are remapped so that each XCD works
-// on runs of 32 consecutive tiles, whose operand blocks then share its L2.
+// on runs of consecutive tiles (32 for the update, 16 for the symmetric
+// products), whose operand blocks then share its L2.
 #include <cmath>
 
 #include "muon_internal.h"

@@ -1079,6 +1079,32 @@ __device__ __attribute__((always_inline)) void apply_epilogue(f32x16_t (&acc)[E:
     const bool tall = d.tall != 0, vec = d.uvec != 0;
     const int rows = d.rows, cols = d.cols;
     char* const w = static_cast<char*>(d.w);
+    // user-frame origin of 8-element group k of row block i
+    auto origin = [&](int i, int k, int& r, int& c) {
+        const int j = k >> 1, gg = k & 1;
+        if (tall) {
+            r = q.raw_col + 32 * j;
+            c = mbase + 32 * i + 8 * (2 * gg + hh);
+        } else {
+            r = q.tr_row + 32 * i + 8 * (2 * gg + odd);
+            c = q.tr_col + 32 * j - (odd ? 4 : 0);
+        }
+    };
+    // bf16 weights with 16-byte groups: every group's load is issued before the first
+    // store (64 VGPRs of packed weights; the k-loop's fragment registers are free here)
+    constexpr bool PACKED = sizeof(T) == 2;
+    u32x4 wraw[PACKED ? E::SM : 1][E::SN * 2];
+    if (PACKED && vec) {
+#pragma unroll
+        for (int i = 0; i < E::SM; ++i)
+#pragma unroll
+            for (int k = 0; k < E::SN * 2; ++k) {
+                int r, c;
+                origin(i, k, r, c);
+                if (r < rows && c < cols)
+                    wraw[PACKED ? i : 0][k] = G(reinterpret_cast<const u32x4*>(w + (static_cast<size_t>(r) * cols + c) * sizeof(T)))[0];
+            }
+    }
 #pragma unroll
     for (int i = 0; i < E::SM; ++i) {
         // user-frame origin of each 8-element group of this row block
@@ -1102,7 +1128,17 @@ __device__ __attribute__((always_inline)) void apply_epilogue(f32x16_t (&acc)[E:
             const bool in = ur[k] < rows && uc[k] < cols;
             const size_t idx = static_cast<size_t>(ur[k]) * cols + uc[k];
             if (vec) {
-                if (in) IO::load8(w + idx * sizeof(T), wv[k]);
+                if (PACKED) {
+                    const u32x4 qw = wraw[PACKED ? i : 0][k];
+                    const unsigned wu[4] = {qw.x, qw.y, qw.z, qw.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        wv[k][2 * e] = __uint_as_float(wu[e] << 16);
+                        wv[k][2 * e + 1] = __uint_as_float(wu[e] & 0xffff0000u);
+                    }
+                } else if (in) {
+                    IO::load8(w + idx * sizeof(T), wv[k]);
+                }
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)

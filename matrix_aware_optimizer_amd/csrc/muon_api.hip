@@ -107,7 +107,8 @@ struct Item {            // one active matrix, before sorting
 struct Plan {
     std::vector<MatDesc> descs;
     std::vector<int32_t> ew_prefix, sym_prefix, upd_prefix;
-    size_t off_descs = 0, off_prefix = 0, off_scal = 0, off_partials = 0, header_bytes = 0, total_bytes = 0;
+    std::vector<TileRun> sym_runs, upd_runs;
+    size_t off_descs = 0, off_prefix = 0, off_runs = 0, off_scal = 0, off_partials = 0, header_bytes = 0, total_bytes = 0;
     int64_t total_ew = 0, total_sym = 0, total_upd = 0;
 };
 
@@ -156,7 +157,9 @@ muon_status build_plan(std::vector<Item>& items, const muon_hparams* hp, bool ns
     pl.off_descs = off;
     off = align_up(off + sizeof(MatDesc) * nmat, ALIGN);
     pl.off_prefix = off;
-    off = align_up(off + sizeof(int32_t) * 3 * (nmat + 1), ALIGN);
+    off = align_up(off + sizeof(int32_t) * (nmat + 1), ALIGN);
+    pl.off_runs = off;                           // sym runs, then upd runs: at most nmat each
+    off = align_up(off + sizeof(TileRun) * 2 * nmat, ALIGN);
     pl.header_bytes = off;                       // uploaded from the host
     pl.off_scal = off;
     off = align_up(off + sizeof(float) * NS_SCAL * nmat, ALIGN);
@@ -217,6 +220,16 @@ muon_status build_plan(std::vector<Item>& items, const muon_hparams* hp, bool ns
     pl.total_ew = ew;
     pl.total_sym = sym;
     pl.total_upd = upd;
+    // consecutive matrices with equal tile counts form one run
+    auto make_runs = [&](const std::vector<int32_t>& prefix, std::vector<TileRun>& runs) {
+        runs.clear();
+        for (int k = 0; k < nmat; ++k) {
+            const int32_t tiles = prefix[k + 1] - prefix[k];
+            if (runs.empty() || runs.back().tiles != tiles) runs.push_back(TileRun{prefix[k], k, tiles});
+        }
+    };
+    make_runs(pl.sym_prefix, pl.sym_runs);
+    make_runs(pl.upd_prefix, pl.upd_runs);
     pl.off_partials = off;
     off = align_up(off + sizeof(double) * ew, ALIGN);
 
@@ -482,19 +495,20 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
     rebase(pl, base);
     const int nmat = static_cast<int>(pl.descs.size());
 
-    // header: descriptors + prefix sums
+    // header: descriptors, the elementwise prefix sums and the GEMM phases' tile runs
     std::vector<char> header(pl.header_bytes, 0);
     std::memcpy(header.data() + pl.off_descs, pl.descs.data(), sizeof(MatDesc) * nmat);
-    int32_t* pre = reinterpret_cast<int32_t*>(header.data() + pl.off_prefix);
-    std::memcpy(pre, pl.ew_prefix.data(), sizeof(int32_t) * (nmat + 1));
-    std::memcpy(pre + (nmat + 1), pl.sym_prefix.data(), sizeof(int32_t) * (nmat + 1));
-    std::memcpy(pre + 2 * (nmat + 1), pl.upd_prefix.data(), sizeof(int32_t) * (nmat + 1));
+    std::memcpy(header.data() + pl.off_prefix, pl.ew_prefix.data(), sizeof(int32_t) * (nmat + 1));
+    TileRun* runs = reinterpret_cast<TileRun*>(header.data() + pl.off_runs);
+    std::memcpy(runs, pl.sym_runs.data(), sizeof(TileRun) * pl.sym_runs.size());
+    std::memcpy(runs + nmat, pl.upd_runs.data(), sizeof(TileRun) * pl.upd_runs.size());
     st = header_by_args ? upload_by_args(base, header.data(), pl.header_bytes, stream)
                         : upload(dev, base, header.data(), pl.header_bytes, stream);
     if (st != MUON_OK) return st;
 
     const MatDesc* d_descs = reinterpret_cast<const MatDesc*>(base + pl.off_descs);
     const int32_t* d_pre = reinterpret_cast<const int32_t*>(base + pl.off_prefix);
+    const TileRun* d_runs = reinterpret_cast<const TileRun*>(base + pl.off_runs);
     double* d_partials = reinterpret_cast<double*>(base + pl.off_partials);
 
     EwArgs ew{};
@@ -523,7 +537,12 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
 
     NsArgs na{};
     na.descs = d_descs;
-    na.nmat = nmat;
+    // a phase's runs: by value when they fit in the arguments, the uploaded table otherwise
+    auto set_runs = [](NsArgs& a, const TileRun* table, const std::vector<TileRun>& runs) {
+        a.runs = table;
+        a.nruns = static_cast<int32_t>(runs.size());
+        for (int i = 0; i < NS_ARG_RUNS; ++i) a.run[i] = i < a.nruns ? runs[i] : TileRun{0, 0, 1};
+    };
     for (int k = 0; k < hp->ns_steps; ++k) {
         na.a = hp->schedule[k].a;
         na.b = hp->schedule[k].b;
@@ -532,13 +551,13 @@ muon_status run(std::vector<Item>& items, const muon_hparams* hp, bool ns_only, 
         // muon_step's last update writes W' itself (no apply launch)
         na.apply = (!ns_only && k == hp->ns_steps - 1) ? 1 : 0;
         na.ping = k & 1;
-        na.prefix = d_pre + (nmat + 1);
+        set_runs(na, d_runs, pl.sym_runs);
         na.total = static_cast<int32_t>(pl.total_sym);
         st = timed_launch(2, stream, "Gram kernel", [&] { return launch_gram(dtype, na, stream); });
         if (st != MUON_OK) return st;
         st = timed_launch(3, stream, "polynomial kernel", [&] { return launch_poly(dtype, na, stream); });
         if (st != MUON_OK) return st;
-        na.prefix = d_pre + 2 * (nmat + 1);
+        set_runs(na, d_runs + nmat, pl.upd_runs);
         na.total = static_cast<int32_t>(pl.total_upd);
         st = timed_launch(na.apply ? 8 : 4, stream, "update kernel", [&] { return launch_update(dtype, na, stream); });
         if (st != MUON_OK) return st;

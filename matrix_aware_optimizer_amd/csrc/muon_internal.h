@@ -111,11 +111,20 @@ struct EwArgs {
     int32_t fin;             // index of the last step's iterate (ns_steps & 1)
 };
 
+// A GEMM phase's tile space as runs of consecutive matrices with equal tile counts (the
+// plan sorts the matrices by size, so equal shapes are adjacent): run r covers tiles
+// tile0 .. of matrices mat0 .., `tiles` tiles each.
+struct TileRun {
+    int32_t tile0, mat0, tiles;
+};
+
+constexpr int NS_ARG_RUNS = 4;   // runs passed by value; longer lists use the table
 struct NsArgs {
     const MatDesc* descs;
-    const int32_t* prefix;   // nmat + 1 exclusive prefix sums for this phase
-    int32_t nmat;
+    const TileRun* runs;     // this phase's runs, ordered by tile0 (tile0 of run 0 is 0)
+    int32_t nruns;
     int32_t total;
+    TileRun run[NS_ARG_RUNS];   // runs[0 .. nruns) when nruns <= NS_ARG_RUNS
     float a, b, c;           // this step's coefficients
     int32_t first;           // first step: fold the normalization scale in
     int32_t apply;           // last step of muon_step: write W' = decay W - coef X' instead of X'
@@ -218,13 +227,39 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Index of the matrix that owns global tile t: the largest i with
 // prefix[i] <= t (prefix has nmat + 1 entries, prefix[0] = 0).
-__device__ inline int find_matrix(const int32_t* prefix, int nmat, int t) {
+__host__ __device__ inline int find_matrix(const int32_t* prefix, int nmat, int t) {
     int lo = 0, hi = nmat - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
         if (prefix[mid] <= t) lo = mid; else hi = mid - 1;
     }
     return lo;
+}
+
+// Matrix of GEMM tile t and the tile's index within it: a search over the runs
+// (one to three for a model's layer or expert set) and one division, in place of a
+// chain of dependent loads over every matrix's prefix sum.
+__host__ __device__ inline int run_matrix(const TileRun* runs, int nruns, int t, int& local) {
+    int lo = 0, hi = nruns - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (runs[mid].tile0 <= t) lo = mid; else hi = mid - 1;
+    }
+    const TileRun r = runs[lo];
+    const int q = (t - r.tile0) / r.tiles;
+    local = t - r.tile0 - q * r.tiles;
+    return r.mat0 + q;
+}
+// The same from the runs passed by value (nruns <= NS_ARG_RUNS): no memory access, so
+// the tile's descriptor is the first load that waits.
+__host__ __device__ inline int run_matrix_args(const TileRun (&run)[NS_ARG_RUNS], int nruns, int t, int& local) {
+    TileRun r = run[0];
+#pragma unroll
+    for (int i = 1; i < NS_ARG_RUNS; ++i)
+        if (i < nruns && run[i].tile0 <= t) r = run[i];
+    const int q = (t - r.tile0) / r.tiles;
+    local = t - r.tile0 - q * r.tiles;
+    return r.mat0 + q;
 }
 
 // Pointers reached through the descriptor table are generic; viewing them in

@@ -1195,9 +1195,10 @@ template <typename T, int PHASE>
 __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, int t, u32x4* lds) {
     constexpr bool UPD = PHASE == PH_UPDATE || PHASE == PH_UPDATE_APPLY;
     using E = Engine<T, UPD>;
-    const int mi = find_matrix(args.prefix, args.nmat, t);
+    int local;
+    const int mi = args.nruns <= NS_ARG_RUNS ? run_matrix_args(args.run, args.nruns, t, local)
+                                             : run_matrix(args.runs, args.nruns, t, local);
     const MatDesc& d = args.descs[mi];
-    const int local = t - args.prefix[mi];
     const int mp = d.mp, np = d.np;
     const int ping = args.ping;
 

@@ -108,3 +108,4 @@ def test_lo_offset_is_the_update_accumulator_layout(tmp_path):
     assert run.returncode == 0, run.stdout + run.stderr
     assert "mismatches 0" in run.stdout
     assert "stage mismatches 0" in run.stdout
+

@@ -142,6 +142,47 @@ __device__ inline void sym_decode(int q, int T, int& ti, int& tj) {
     tj = i + q;
 }
 
+// Diagonal tiles of a symmetric product (bf16 256 x 256, 8 x 8 blocks of 32 x 32).
+// Only the blocks (R, C) with R <= C are stored, and P = Q, so block (C, R) is the
+// transpose of block (R, C): a wave may form the lower block (R, C) of its own slot
+// and stage it transposed in place of (C, R).  Each strictly upper block is formed
+// once, in its own slot or in its twin's, so that the 36 blocks fall 9 to each SIMD
+// when a SIMD runs the two waves with the same wn (which own the columns 2 wn,
+// 2 wn + 1, and so the twins of the rows 2 wn, 2 wn + 1), and 10 at most when it runs
+// waves 2 s and 2 s + 1.
+//   R == C, or R < C in one column pair:      native;
+//   R < C in different pairs:                 native for even C, else the twin forms it;
+//   R > C in different pairs, R odd:          swapped (formed here, staged as (C, R));
+//   otherwise:                                skipped.
+// Two bits per slot (i, j) at 2 (2 i + j): 0 skip, 1 native, 2 swapped; wave-uniform.
+constexpr unsigned DG_SKIP = 0u, DG_NATIVE = 1u, DG_SWAP = 2u;
+__host__ __device__ constexpr unsigned diag_modes_of(int wave) {
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    unsigned m = 0;
+    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 2; ++j) {
+            const int R = 4 * wm + i, C = 2 * wn + j;
+            const bool pair = (R >> 1) == (C >> 1);
+            unsigned md = DG_SKIP;
+            if (R == C || (R < C && (pair || !(C & 1)))) md = DG_NATIVE;
+            else if (R > C && !pair && (R & 1)) md = DG_SWAP;
+            m |= md << (2 * (2 * i + j));
+        }
+    return m;
+}
+__host__ __device__ constexpr unsigned dg_mode(unsigned modes, int i, int j) { return (modes >> (2 * (2 * i + j))) & 3u; }
+// fragment row i (A) or column block j (B) feeds some slot that is not skipped
+__host__ __device__ constexpr bool dg_needs_a(unsigned modes, int i) {
+    return dg_mode(modes, i, 0) != DG_SKIP || dg_mode(modes, i, 1) != DG_SKIP;
+}
+__host__ __device__ constexpr bool dg_needs_b(unsigned modes, int j) {
+    return dg_mode(modes, 0, j) != DG_SKIP || dg_mode(modes, 1, j) != DG_SKIP || dg_mode(modes, 2, j) != DG_SKIP ||
+           dg_mode(modes, 3, j) != DG_SKIP;
+}
+__device__ __forceinline__ unsigned diag_modes() {
+    return diag_modes_of(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)));
+}
+
 // QK: Q is k-major (row k holds BN consecutive columns), else k-contiguous.
 template <typename T, bool QK>
 struct Engine {
@@ -210,12 +251,34 @@ struct Engine {
         static_assert(HL * 64 / CHUNKS_PER_ROW == BM / NWAVES && 2 * WAVES_N == NWAVES,
                       "wave w loads P rows w BM / 8 ..: the waves with wm = 1 load exactly rows BM / 2 .. BM - 1");
         if (p_half && (threadIdx.x >> 6) / WAVES_N == 1)
-            run_impl<true>(P, ldp, Q, ldq, ksteps, lds, acc, init, hook);
+            run_impl<true, false>(P, ldp, Q, ldq, ksteps, lds, acc, init, hook);
         else
-            run_impl<false>(P, ldp, Q, ldq, ksteps, lds, acc, init, hook);
+            run_impl<false, false>(P, ldp, Q, ldq, ksteps, lds, acc, init, hook);
     }
 
-    template <bool IDLE, typename Init, typename Hook>
+    // A diagonal tile of a symmetric product (P = Q, k-contiguous): only the P slabs
+    // are loaded, the B fragments and the hook read them too, and the slots that
+    // diag_modes() skips run no MFMAs (their accumulators keep init's value).
+    template <typename Init, typename Hook>
+    static __device__ __attribute__((always_inline)) void run_diag(const char* __restrict__ P, size_t ldp, int ksteps,
+                                                                   u32x4* lds, f32x16_t (&acc)[SM][SN], Init init,
+                                                                   Hook hook) {
+        static_assert(!QK && SM == 4 && SN == 2 && BM == 256 && NWAVES == 8, "diag_modes' block geometry");
+        // one copy of the loop per wave, so that the skipped MFMAs and fragment reads
+        // drop out at compile time (a branch per MFMA costs the loop its LDS-read overlap)
+        switch (__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6))) {
+            case 0: run_impl<false, true, diag_modes_of(0)>(P, ldp, P, ldp, ksteps, lds, acc, init, hook); break;
+            case 1: run_impl<false, true, diag_modes_of(1)>(P, ldp, P, ldp, ksteps, lds, acc, init, hook); break;
+            case 2: run_impl<false, true, diag_modes_of(2)>(P, ldp, P, ldp, ksteps, lds, acc, init, hook); break;
+            case 3: run_impl<false, true, diag_modes_of(3)>(P, ldp, P, ldp, ksteps, lds, acc, init, hook); break;
+            case 4: run_impl<false, true, diag_modes_of(4)>(P, ldp, P, ldp, ksteps, lds, acc, init, hook); break;
+            case 5: run_impl<false, true, diag_modes_of(5)>(P, ldp, P, ldp, ksteps, lds, acc, init, hook); break;
+            case 6: run_impl<false, true, diag_modes_of(6)>(P, ldp, P, ldp, ksteps, lds, acc, init, hook); break;
+            default: run_impl<false, true, diag_modes_of(7)>(P, ldp, P, ldp, ksteps, lds, acc, init, hook); break;
+        }
+    }
+
+    template <bool IDLE, bool DIAGM, unsigned MODES = 0u, typename Init, typename Hook>
     static __device__ __attribute__((always_inline)) void run_impl(const char* __restrict__ P, size_t ldp,
                                       const char* __restrict__ Q, size_t ldq, int ksteps, u32x4* lds,
                                       f32x16_t (&acc)[SM][SN], Init init, Hook hook) {
@@ -246,8 +309,10 @@ struct Engine {
 #pragma unroll
             for (int j = 0; j < HL; ++j) issue(0, false, 0, j);
         }
+        if constexpr (!DIAGM) {
 #pragma unroll
-        for (int j = 0; j < HL; ++j) issue(0, true, 1, j);
+            for (int j = 0; j < HL; ++j) issue(0, true, 1, j);
+        }
         if (!IDLE && ksteps > 1) {
 #pragma unroll
             for (int j = 0; j < HL; ++j) issue(1, false, 2, j);
@@ -292,11 +357,17 @@ struct Engine {
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_barrier" ::: "memory");
+        // a diagonal tile reads its B fragments from the P slab (same rows, same bytes),
+        // and only the fragments that its slots use (the conditions fold at compile time)
+        auto need_a = [](int i) { return !DIAGM || dg_needs_a(MODES, i); };
+        auto need_b = [](int j) { return !DIAGM || dg_needs_b(MODES, j); };
         if constexpr (!IDLE) {
 #pragma unroll
-            for (int i = 0; i < SM; ++i) fa[0][i] = lds[swz(arow + i * 32, half)];
+            for (int i = 0; i < SM; ++i)
+                if (need_a(i)) fa[0][i] = lds[swz(arow + i * 32, half)];
 #pragma unroll
-            for (int j = 0; j < SN; ++j) fb[0][j] = read_b(lds + SLAB, j, 0);
+            for (int j = 0; j < SN; ++j)
+                if (need_b(j)) fb[0][j] = read_b(DIAGM ? lds : lds + SLAB, j, 0);
         }
 
         int sp = 0;   // slot of P(kt); Q(kt) sits in the next one
@@ -306,7 +377,7 @@ struct Engine {
             const int s4 = sp >= 1 ? sp - 1 : sp + 4;   // slot of P(kt + 2)
             const int np = sp >= 3 ? sp - 3 : sp + 2;   // slot of P(kt + 1)
             const u32x4* L = lds + sp * SLAB;
-            const u32x4* LQ = lds + sq * SLAB;
+            const u32x4* LQ = DIAGM ? L : lds + sq * SLAB;
             hook(kt, (const lds_byte_t*)LQ, acc);
             const bool more1 = kt + 1 < ksteps, more2 = kt + 2 < ksteps;
             __builtin_amdgcn_sched_barrier(0);
@@ -331,17 +402,20 @@ struct Engine {
                 for (int i = 0; i < SM; ++i) {
                     if constexpr (!IDLE) {
 #pragma unroll
-                        for (int j = 0; j < SN; ++j) mfma_chunk(acc[i][j], fa[s & 1][i], fb[s & 1][j], T{});
+                        for (int j = 0; j < SN; ++j) {
+                            if (!DIAGM || dg_mode(MODES, i, j) != DG_SKIP)
+                                mfma_chunk(acc[i][j], fa[s & 1][i], fb[s & 1][j], T{});
+                        }
                         if (s + 1 < SUB) {
-                            fa[(s + 1) & 1][i] = L[swz(arow + i * 32, cn)];
-                            if (i < SN) fb[(s + 1) & 1][i] = read_b(LQ, i, s + 1);
+                            if (need_a(i)) fa[(s + 1) & 1][i] = L[swz(arow + i * 32, cn)];
+                            if (i < SN && need_b(i)) fb[(s + 1) & 1][i] = read_b(LQ, i, s + 1);
                         } else if (more1) {
-                            fa[0][i] = lds[np * SLAB + swz(arow + i * 32, half)];
-                            if (i < SN) fb[0][i] = read_b(lds + s3 * SLAB, i, 0);
+                            if (need_a(i)) fa[0][i] = lds[np * SLAB + swz(arow + i * 32, half)];
+                            if (i < SN && need_b(i)) fb[0][i] = read_b(lds + (DIAGM ? np : s3) * SLAB, i, 0);
                         }
                     }
                     const int g = s * SM + i;
-                    if (g < HL && more1) issue(kt + 1, true, s3, g);
+                    if (!DIAGM && g < HL && more1) issue(kt + 1, true, s3, g);
                     if (!IDLE && g >= HL && g < 2 * HL && more2) issue(kt + 2, false, s4, g - HL);
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -872,6 +946,19 @@ struct CStage {
     __device__ __forceinline__ void put(lds_byte_t* L, int i, int j, int g, unsigned w0, unsigned w1) const {
         *(lds_u32x2_t*)(L + (wbase[j] ^ (64 * i + 16 * g))) = u32x2_t{w0, w1};
     }
+    // Slot (i, j) holds block (R, C) = (4 wm + i, 2 wn + j) of a diagonal tile; stage its
+    // transpose as block (C, R) (diag_modes, swapped).  After a quad transpose lane
+    // 4 q + t (of its half h) holds rows 4 q .. 4 q + 3 of column 8 g + 4 h + t of the
+    // transpose: unit u = 8 C + q of tile column c = 32 R + 8 g + 4 h + t, at byte
+    // c 512 + 8 (u ^ csw(c)).  v: the 4 values of group g in accumulator order.
+    __device__ __forceinline__ void put_transposed(lds_byte_t* L, int i, int j, int g, float (&v)[4]) const {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+        quad_transpose(v);
+        const int c = 32 * (E::SM * wm + i) + 8 * g + 4 * (lane >> 5) + (lane & 3);
+        const int u = 8 * (E::SN * wn + j) + ((lane & 31) >> 2);
+        *(lds_u32x2_t*)(L + (c * 512 + 8 * (u ^ csw(c)))) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
 };
 
 // 8 bf16 (packed, in column order) at p: one 16-byte store, or per element where `mask` has bits clear.
@@ -958,23 +1045,34 @@ __device__ __forceinline__ void cstage_store_mirror(const lds_byte_t* L, uint16_
 // bf16 symmetric output (Gram, polynomial with the staged addend): value = scale * acc,
 // staged once, stored directly and mirrored (non-temporal: the next reader is the
 // next launch, and a batch's outputs do not stay in the caches until then).
-template <typename E>
+// DGM: the tile was formed by Engine::run_diag, its slots hold what diag_modes says;
+// only the upper blocks are staged (the stores below read no lower block).
+template <typename E, bool DGM = false>
 __device__ __attribute__((always_inline)) void sym_epilogue_cstage(f32x16_t (&acc)[E::SM][E::SN], int row0, int col0,
                                                                    bool diag, uint16_t* dst, size_t ld, float scale,
                                                                    u32x4* lds) {
     const CStage<E> st;
     lds_byte_t* L = (lds_byte_t*)lds;
+    const unsigned modes = DGM ? diag_modes() : 0u;
     lds_barrier();   // every wave is done reading the operand slabs
 #pragma unroll
     for (int i = 0; i < E::SM; ++i)
 #pragma unroll
-        for (int j = 0; j < E::SN; ++j)
+        for (int j = 0; j < E::SN; ++j) {
+            const unsigned md = DGM ? dg_mode(modes, i, j) : DG_NATIVE;
+            if (md == DG_SKIP) continue;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const f32x16_t& a = acc[i][j];
-                st.put(L, i, j, g, pack_bf16x2(scale * a[4 * g], scale * a[4 * g + 1]),
-                       pack_bf16x2(scale * a[4 * g + 2], scale * a[4 * g + 3]));
+                if (md == DG_NATIVE) {
+                    st.put(L, i, j, g, pack_bf16x2(scale * a[4 * g], scale * a[4 * g + 1]),
+                           pack_bf16x2(scale * a[4 * g + 2], scale * a[4 * g + 3]));
+                } else {
+                    float v[4] = {scale * a[4 * g], scale * a[4 * g + 1], scale * a[4 * g + 2], scale * a[4 * g + 3]};
+                    st.put_transposed(L, i, j, g, v);
+                }
             }
+        }
     lds_barrier();
     if (diag) {
         cstage_store_rows<E, true, true>(L, dst, row0, col0, ld);
@@ -1225,31 +1323,47 @@ __device__ __attribute__((always_inline)) void process_tile(const NsArgs& args, 
     // padding of X, A and B is zero, so the skipped k-steps would add nothing
     const int ks_m = (d.m + E::KS - 1) / E::KS, ks_n = (d.n + E::KS - 1) / E::KS;
     f32x16_t acc[E::SM][E::SN];
-    if (PHASE == PH_GRAM) {
+    if constexpr (PHASE == PH_GRAM) {
         // the first step reads hi0 (the workspace copy, or the caller's buffer holding the same bits)
         const char* X = static_cast<const char*>(args.first ? d.hi0 : d.xop[ping]);
         const size_t ld = static_cast<size_t>(np) * sizeof(T);
-        E::run(X + row0 * ld, ld, X + col0 * ld, ld, ks_n, lds, acc, ZeroInit{}, NoHook{}, p_half);
         // first step: X0 = s * M' is folded in as A0 = s^2 M' M'^T
         const float scale = args.first ? G(d.scal)[0] * G(d.scal)[0] : 1.0f;
-        if constexpr (sizeof(T) == 2)
-            sym_epilogue_cstage<E>(acc, row0, col0, ti == tj, static_cast<uint16_t*>(d.amat), mp, scale, lds);
-        else
+        if constexpr (sizeof(T) == 2) {
+            if (ti == tj && !p_half) {
+                E::run_diag(X + row0 * ld, ld, ks_n, lds, acc, ZeroInit{}, NoHook{});
+                sym_epilogue_cstage<E, true>(acc, row0, col0, true, static_cast<uint16_t*>(d.amat), mp, scale, lds);
+            } else {
+                E::run(X + row0 * ld, ld, X + col0 * ld, ld, ks_n, lds, acc, ZeroInit{}, NoHook{}, p_half);
+                sym_epilogue_cstage<E>(acc, row0, col0, ti == tj, static_cast<uint16_t*>(d.amat), mp, scale, lds);
+            }
+        } else {
+            E::run(X + row0 * ld, ld, X + col0 * ld, ld, ks_n, lds, acc, ZeroInit{}, NoHook{}, p_half);
             sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.amat, mp, scale, nullptr, 0.0f, 0.0f);
-    } else if (PHASE == PH_POLY) {
+        }
+    } else if constexpr (PHASE == PH_POLY) {
         const char* A = static_cast<const char*>(d.amat);
         const size_t ld = static_cast<size_t>(mp) * sizeof(T);
         E::run(A + row0 * ld, ld, A + col0 * ld, ld, ks_m, lds, acc, ZeroInit{}, NoHook{}, p_half);
         sym_epilogue<E, T, true>(acc, row0, col0, ti == tj, d.bmat, mp, 1.0f, d.amat, args.b, args.c);
-    } else if (PHASE == PH_POLY_LDS) {
+    } else if constexpr (PHASE == PH_POLY_LDS) {
         const char* A = static_cast<const char*>(d.amat);
         const size_t ld = static_cast<size_t>(mp) * sizeof(T);
-        E::run(A + row0 * ld, ld, A + col0 * ld, ld, ks_m, lds, acc, ZeroInit{},
-               PolyAddend<E, T>{row0 / E::KS, args.b / args.c}, p_half);
-        if constexpr (sizeof(T) == 2)
-            sym_epilogue_cstage<E>(acc, row0, col0, ti == tj, static_cast<uint16_t*>(d.bmat), mp, args.c, lds);
-        else
+        if constexpr (sizeof(T) == 2) {
+            if (ti == tj && !p_half) {
+                E::run_diag(A + row0 * ld, ld, ks_m, lds, acc, ZeroInit{},
+                            PolyAddend<E, T>{row0 / E::KS, args.b / args.c});
+                sym_epilogue_cstage<E, true>(acc, row0, col0, true, static_cast<uint16_t*>(d.bmat), mp, args.c, lds);
+            } else {
+                E::run(A + row0 * ld, ld, A + col0 * ld, ld, ks_m, lds, acc, ZeroInit{},
+                       PolyAddend<E, T>{row0 / E::KS, args.b / args.c}, p_half);
+                sym_epilogue_cstage<E>(acc, row0, col0, ti == tj, static_cast<uint16_t*>(d.bmat), mp, args.c, lds);
+            }
+        } else {
+            E::run(A + row0 * ld, ld, A + col0 * ld, ld, ks_m, lds, acc, ZeroInit{},
+                   PolyAddend<E, T>{row0 / E::KS, args.b / args.c}, p_half);
             sym_epilogue<E, T, false>(acc, row0, col0, ti == tj, d.bmat, mp, args.c, nullptr, 0.0f, 0.0f);
+        }
     } else {
         const char* B = static_cast<const char*>(d.bmat);
         const char* X = static_cast<const char*>(args.first ? d.hi0 : d.xop[ping]);

@@ -92,6 +92,11 @@ typedef __attribute__((address_space(3))) char lds_byte_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) float lds_float_t;
 
+// The wave's index in the workgroup as a wave-uniform (scalar) value, so that LDS
+// destinations of the direct-to-LDS loads (M0) and per-wave branch conditions are
+// formed with scalar instructions instead of one v_readfirstlane per use.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)); }
+
 // One 16-byte chunk per lane of both operands, accumulated into a 32 x 32 block.
 __device__ inline void mfma_chunk(f32x16_t& acc, const u32x4& a, const u32x4& b, uint16_t) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -180,7 +185,7 @@ __host__ __device__ constexpr bool dg_needs_b(unsigned modes, int j) {
            dg_mode(modes, 3, j) != DG_SKIP;
 }
 __device__ __forceinline__ unsigned diag_modes() {
-    return diag_modes_of(__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)));
+    return diag_modes_of(wave_id());
 }
 
 // QK: Q is k-major (row k holds BN consecutive columns), else k-contiguous.
@@ -216,7 +221,7 @@ struct Engine {
     }
     // Issue this wave's share of the DMA of one k-major slab into LDS slot `slot`.
     static __device__ __forceinline__ void load_kmajor_slab(const char* Q, size_t ldq, u32x4* lds, int slot) {
-        const int wave = threadIdx.x >> 6;
+        const int wave = wave_id();
 #pragma unroll
         for (int j = 0; j < HL; ++j)
             __builtin_amdgcn_global_load_lds((const void*)kmajor_src(Q, ldq, j),
@@ -250,7 +255,7 @@ struct Engine {
                                       Hook hook, bool p_half = false) {
         static_assert(HL * 64 / CHUNKS_PER_ROW == BM / NWAVES && 2 * WAVES_N == NWAVES,
                       "wave w loads P rows w BM / 8 ..: the waves with wm = 1 load exactly rows BM / 2 .. BM - 1");
-        if (p_half && (threadIdx.x >> 6) / WAVES_N == 1)
+        if (p_half && wave_id() / WAVES_N == 1)
             run_impl<true, false>(P, ldp, Q, ldq, ksteps, lds, acc, init, hook);
         else
             run_impl<false, false>(P, ldp, Q, ldq, ksteps, lds, acc, init, hook);
@@ -266,7 +271,7 @@ struct Engine {
         static_assert(!QK && SM == 4 && SN == 2 && BM == 256 && NWAVES == 8, "diag_modes' block geometry");
         // one copy of the loop per wave, so that the skipped MFMAs and fragment reads
         // drop out at compile time (a branch per MFMA costs the loop its LDS-read overlap)
-        switch (__builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6))) {
+        switch (wave_id()) {
             case 0: run_impl<false, true, diag_modes_of(0)>(P, ldp, P, ldp, ksteps, lds, acc, init, hook); break;
             case 1: run_impl<false, true, diag_modes_of(1)>(P, ldp, P, ldp, ksteps, lds, acc, init, hook); break;
             case 2: run_impl<false, true, diag_modes_of(2)>(P, ldp, P, ldp, ksteps, lds, acc, init, hook); break;
@@ -283,7 +288,7 @@ struct Engine {
                                       const char* __restrict__ Q, size_t ldq, int ksteps, u32x4* lds,
                                       f32x16_t (&acc)[SM][SN], Init init, Hook hook) {
         const int tid = threadIdx.x;
-        const int lane = tid & 63, wave = tid >> 6;
+        const int lane = tid & 63, wave = wave_id();
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
 
         // Load j of this wave fills slab chunks [(wave*HL + j)*64, +64) in lane order;
@@ -550,7 +555,7 @@ struct Coords {
     int raw_row, raw_col;   // untransposed: rows raw_row + 32 i + 8 g + (0..3), column raw_col + 32 j
     int tr_row, tr_col;     // transposed:   row tr_row + 32 i + 8 g, columns tr_col + 32 j + (0..3)
     __device__ Coords(int row0, int col0) {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int lane = threadIdx.x & 63, wave = wave_id();
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
         const int c = lane & 31, h = lane >> 5;
         raw_row = row0 + wm * E::WM + 4 * h;
@@ -795,7 +800,7 @@ struct HiAddend {
     // group g16 addresses rows 8 g + 4 (g16 >> 1) + (0..3) and 16 columns.
     template <typename A> __device__ __forceinline__ void operator()(int kt, const lds_byte_t* Lq, A& acc) const {
         const int rel = kt - kt0;
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int lane = threadIdx.x & 63, wave = wave_id();
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
         if (rel < 0 || rel >= E::BM / E::KS || (rel * E::KS) / E::WM != wm) return;
         const int ifirst = (rel * E::KS - wm * E::WM) / 32;
@@ -842,7 +847,7 @@ struct PolyAddend {
     float f;    // b / c
     template <typename A> __device__ __forceinline__ void operator()(int kt, const lds_byte_t* Lq, A& acc) const {
         const int rel = kt - kt0;
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int lane = threadIdx.x & 63, wave = wave_id();
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
         if (rel < 0 || rel >= E::BM / E::KS || (rel * E::KS) / E::WM != wm) return;
         const int ifirst = (rel * E::KS - wm * E::WM) / 32;
@@ -933,7 +938,7 @@ struct CStage {
     static_assert(E::BM * 512 <= E::LDS_CHUNKS * 16, "a staged tile fits the LDS");
     int wbase[E::SN];   // byte address of this lane's unit for i = g = 0, per column block j
     __device__ CStage() {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int lane = threadIdx.x & 63, wave = wave_id();
         const int wm = wave / WAVES_N, wn = wave % WAVES_N, h = lane >> 5;
 #pragma unroll
         for (int j = 0; j < E::SN; ++j) {
@@ -952,7 +957,7 @@ struct CStage {
     // transpose: unit u = 8 C + q of tile column c = 32 R + 8 g + 4 h + t, at byte
     // c 512 + 8 (u ^ csw(c)).  v: the 4 values of group g in accumulator order.
     __device__ __forceinline__ void put_transposed(lds_byte_t* L, int i, int j, int g, float (&v)[4]) const {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int lane = threadIdx.x & 63, wave = wave_id();
         const int wm = wave / WAVES_N, wn = wave % WAVES_N;
         quad_transpose(v);
         const int c = 32 * (E::SM * wm + i) + 8 * g + 4 * (lane >> 5) + (lane & 3);
@@ -980,7 +985,7 @@ __device__ __forceinline__ void st_packed8(uint16_t* p, const u32x4& v, unsigned
 // diagonal tile of a symmetric output).
 template <typename E, bool DIAG, bool NT>
 __device__ __forceinline__ void cstage_store_rows(const lds_byte_t* L, uint16_t* dst, int row0, int col0, size_t ld) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int grp = lane >> 4, k = lane & 15;
     // lane k of a 16-lane group addresses column ccA = 32 grp + 8 (k & 3) + (k >> 2) (read A)
     // and ccA + 4 (read B) at the row quad being stored; the transpose hands lane l the
@@ -1022,7 +1027,7 @@ __device__ __forceinline__ void cstage_store_rows(const lds_byte_t* L, uint16_t*
 // upper triangle, mirrored).
 template <typename E, bool DIAG>
 __device__ __forceinline__ void cstage_store_mirror(const lds_byte_t* L, uint16_t* dst, int row0, int col0, size_t ld) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_id();
     const int m = lane & 31, hh = lane >> 5;
     // column c = 32 w + 2 t + hh: csw(c) = (2 t + hh) ^ (4 (w & 1)), odd exactly when hh = 1;
     // the 16-byte slot of units 2m, 2m + 1 is 2m ^ (csw(c) & ~1)

@@ -356,6 +356,20 @@ struct Engine {
         };
 
         u32x4 fa[2][SM], fb[2][SN];
+        // fp32 products sum in two levels: each run of SUM_BLOCK k-steps (1024 values of k)
+        // into part, which is then added to acc.  A single running fp32 sum over k carries a
+        // rounding error that grows like sqrt(k) (about 1e-4 relative at k = 2^20); two
+        // levels bring it to about sqrt(1024) + sqrt(k / 1024).  The fp32 tile's
+        // accumulators are 32 registers, so the second set is cheap; bf16 keeps one level.
+        constexpr bool TWO_LEVEL = sizeof(T) == 4;
+        constexpr int SUM_BLOCK = 32;
+        f32x16_t part[TWO_LEVEL ? SM : 1][TWO_LEVEL ? SN : 1];
+        if constexpr (TWO_LEVEL) {
+#pragma unroll
+            for (int i = 0; i < SM; ++i)
+#pragma unroll
+                for (int j = 0; j < SN; ++j) part[i][j] = f32x16_t{};
+        }
         // step 0's slabs (P(1) may still be in flight), then its first fragments
         if (!IDLE && ksteps > 1)
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(HL) : "memory");
@@ -409,7 +423,8 @@ struct Engine {
 #pragma unroll
                         for (int j = 0; j < SN; ++j) {
                             if (!DIAGM || dg_mode(MODES, i, j) != DG_SKIP)
-                                mfma_chunk(acc[i][j], fa[s & 1][i], fb[s & 1][j], T{});
+                                mfma_chunk(TWO_LEVEL ? part[TWO_LEVEL ? i : 0][TWO_LEVEL ? j : 0] : acc[i][j],
+                                           fa[s & 1][i], fb[s & 1][j], T{});
                         }
                         if (s + 1 < SUB) {
                             if (need_a(i)) fa[(s + 1) & 1][i] = L[swz(arow + i * 32, cn)];
@@ -423,6 +438,17 @@ struct Engine {
                     if (!DIAGM && g < HL && more1) issue(kt + 1, true, s3, g);
                     if (!IDLE && g >= HL && g < 2 * HL && more2) issue(kt + 2, false, s4, g - HL);
                     __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if constexpr (TWO_LEVEL) {
+                if (kt % SUM_BLOCK == SUM_BLOCK - 1 || kt + 1 == ksteps) {
+#pragma unroll
+                    for (int i = 0; i < SM; ++i)
+#pragma unroll
+                        for (int j = 0; j < SN; ++j) {
+                            acc[i][j] += part[i][j];
+                            part[i][j] = f32x16_t{};
+                        }
                 }
             }
             sp = np;

@@ -75,6 +75,7 @@ def test_workspace_bytes_is_host_only_and_grows_with_work():
 @pytest.mark.parametrize("case", [
     "null_hp", "bad_dtype", "bad_rule", "steps_high", "steps_neg", "nan_lr", "inf_coeff",
     "neg_eps", "bad_flags", "zero_rows", "null_weight", "overlap", "misaligned", "null_schedule",
+    "cols_above_max", "rows_above_max",
 ])
 def test_invalid_arguments_are_rejected_before_any_gpu_work(case):
     lib = mao.load()
@@ -107,12 +108,26 @@ def test_invalid_arguments_are_rejected_before_any_gpu_work(case):
         specs = [(FAKE + 1, FAKE + (1 << 30), FAKE + (2 << 30), 64, 96)]
     elif case == "null_schedule":
         hp.schedule = ctypes.POINTER(mao.MuonNsCoeffs)()
+    elif case == "cols_above_max":   # MUON_MAX_DIM = 2^20 is the largest accepted extent
+        specs = [(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), 1, (1 << 20) + 1)]
+    elif case == "rows_above_max":
+        specs = [(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), (1 << 20) + 1, 1)]
     arr = _mats(specs)
     hpp = None if case == "null_hp" else ctypes.byref(hp)
     st = lib.muon_step(arr, 1, hpp, ctypes.c_void_p(FAKE + (8 << 30)), 1 << 40, None)
     assert st == mao.MUON_ERR_INVALID_ARG, (case, st, mao.muon_last_error_message())
     assert mao.muon_last_error_message() != ""
     assert lib.muon_workspace_bytes(arr, 1, hpp) == 0
+
+
+def test_maximum_dimension_is_accepted():
+    """An extent of exactly MUON_MAX_DIM (2^20), wide or tall, passes validation and
+    gets a workspace size (host-only call)."""
+    lib = mao.load()
+    hp, keep = _hp(dtype=mao.MUON_BF16)
+    for rows, cols in ((1, 1 << 20), (1 << 20, 1), (40, 1 << 20)):
+        arr = _mats([(FAKE, FAKE + (1 << 30), FAKE + (2 << 30), rows, cols)])
+        assert lib.muon_workspace_bytes(arr, 1, ctypes.byref(hp)) > 0, (rows, cols, mao.muon_last_error_message())
 
 
 def test_workspace_errors():

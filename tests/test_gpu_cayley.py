@@ -37,8 +37,8 @@ def _run(mao, hosts, lr, beta, skip=()):
     return [w.cpu().numpy() for w in W], [m.cpu().numpy() for m in M]
 
 
-def _check(h, w, m, lr, beta):
-    ref = orc.cayley_step(h["W"], h["G"], h["M"], lr=lr, beta=beta)
+def _check(h, w, m, lr, beta, retraction=orc.cayley_retraction):
+    ref = orc.cayley_step(h["W"], h["G"], h["M"], lr=lr, beta=beta, retraction=retraction)
     assert _rel(w, ref["W"]) <= 1e-5, _rel(w, ref["W"])
     assert _rel(w.astype(np.float64) - h["W"], ref["W"] - h["W"]) <= 1e-3
     assert _rel(m, ref["M"]) <= 1e-5
@@ -97,6 +97,19 @@ def test_cayley_full_width_blocks(gpu_lib):
     Ws, Ms = _run(gpu_lib, hosts, 0.05, 0.9)
     for h, w, m in zip(hosts, Ws, Ms):
         _check(h, w, m, 0.05, 0.9)
+
+
+def test_cayley_maximum_dimension(gpu_lib):
+    # MUON_MAX_DIM (2^20) rows, and 2^20 columns through the transposed frame: the K x K
+    # products over N = 2^20 (row-block partials).  The oracle takes its 2K x 2K form here
+    # (pinned equal to the n x n solve); an n x n system of that size cannot be formed.
+    big = 1 << 20
+    shapes = [(big, 8), (16, big)]
+    hosts = [wk.cayley_host_matrix(r, c, seed=60 + i) for i, (r, c) in enumerate(shapes)]
+    _say("maximum dimension", shapes)
+    Ws, Ms = _run(gpu_lib, hosts, 0.05, 0.9)
+    for h, w, m in zip(hosts, Ws, Ms):
+        _check(h, w, m, 0.05, 0.9, retraction=orc.cayley_retraction_lowrank)
 
 
 def test_cayley_benchmark_set(gpu_lib):

@@ -298,7 +298,8 @@ def _oracle_step(h, dtype, hp, zero_w=False, lr=None):
 
 
 def _check_step(mao, wl, indices, host, label=None):
-    """Full step on all of `host` (one grouped call); oracle checks on `indices`."""
+    """Full step on all of `host` (one grouped call); oracle checks on `indices`.
+    Returns the first pass's W' and M' (real weights) for every matrix."""
     dtype, hp = wl.dtype, wl.hp
     # pass 1: real weights -> M' and W'
     Wg, Mg = _step_gpu(mao, host, dtype, hp)
@@ -344,6 +345,7 @@ def _check_step(mao, wl, indices, host, label=None):
             assert exact.any()
             record_parity(**rec, w_bound_ratio=float(np.max(dev_ / (ulp + slack))),
                           w_ulp_max_where_o_negligible=int(du[exact].max()))
+    return Wg, Mg
 
 
 def test_step_fp32_single_matrix_workload(gpu_lib):
@@ -374,6 +376,28 @@ def test_step_maximum_dimension(gpu_lib, dtype):
     host = [wk.host_matrix(wl, i) for i in range(len(shapes))]
     _say("step at the maximum dimension", dtype, shapes)
     _check_step(gpu_lib, wl, range(len(shapes)), host, label="maximum dimension 2^20")
+
+
+def test_step_maximum_matrix_count(gpu_lib):
+    """MUON_MAX_MATRICES (65536) matrices in one grouped call: the descriptor table, the tile
+    prefix sums and the run lookup at their largest.  Every matrix's stored momentum within
+    1 ulp of its rounding and every W' finite; 16 sampled matrices against the oracle in full.
+    fp32, whose 1e-5 bar is tight at any size: small Gaussian matrices in bf16 carry an O
+    error of 2-3 % under any bf16-operand plan (tests/diag_bf16_emulation.py), at the 3e-2 bar."""
+    n = 1 << 16
+    base = [(1, 1), (3, 7), (16, 24), (40, 9), (64, 64), (100, 31), (5, 256), (256, 2)]
+    shapes = [base[i % len(base)] for i in range(n)]
+    wl = wk.custom_workload(shapes, dtype="f32", wid=233, lr=0.02, weight_decay=0.1, scale_rule="kellerjordan")
+    _say("step with the maximum matrix count", n)
+    host = [wk.host_matrix(wl, i) for i in range(n)]
+    sample = sorted({0, 1, 2, 3, 4, 5, 6, 7, n // 2, n // 2 + 3, n - 6, n - 5, n - 4, n - 3, n - 2, n - 1})
+    Wg, Mg = _check_step(gpu_lib, wl, sample, host, label="65536 matrices in one call (sampled)")
+    beta = orc.as_f32(wl.hp["beta"])   # beta crosses the C boundary as a float, as in the oracle's step
+    for i in range(n):
+        h = host[i]
+        want = orc.rne(orc.momentum_update(h["M"], h["G"], beta), "f32")
+        assert ulp_distance(Mg[i], want, "f32").max() <= 1, (i, "M'")
+        assert np.all(np.isfinite(Wg[i])), (i, "W'")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -422,9 +422,12 @@ struct Engine {
                     if constexpr (!IDLE) {
 #pragma unroll
                         for (int j = 0; j < SN; ++j) {
-                            if (!DIAGM || dg_mode(MODES, i, j) != DG_SKIP)
-                                mfma_chunk(TWO_LEVEL ? part[TWO_LEVEL ? i : 0][TWO_LEVEL ? j : 0] : acc[i][j],
-                                           fa[s & 1][i], fb[s & 1][j], T{});
+                            if (!DIAGM || dg_mode(MODES, i, j) != DG_SKIP) {
+                                if constexpr (TWO_LEVEL)
+                                    mfma_chunk(part[i][j], fa[s & 1][i], fb[s & 1][j], T{});
+                                else
+                                    mfma_chunk(acc[i][j], fa[s & 1][i], fb[s & 1][j], T{});
+                            }
                         }
                         if (s + 1 < SUB) {
                             if (need_a(i)) fa[(s + 1) & 1][i] = L[swz(arow + i * 32, cn)];
